@@ -1,0 +1,195 @@
+"""CPU oracle of the paged-KV decode step (ctypes binding of ``pkv_oracle.c``).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package. The product package ``paged_kv_cache_315_amd`` never
+imports it, and the two share no code: the only thing both sides see is the seeded input
+generator module ``paged_kv_cache_315_amd.workloads``, which holds none of the method's
+arithmetic.
+
+Every function here is argument marshalling around the C oracle; what each C function computes
+and which page passage it follows is stated in ``pkv_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "pkv_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
+
+F16 = 1
+BF16 = 2
+DTYPES = {"f16": F16, "fp16": F16, "bf16": BF16}
+
+OK = 0
+ERR_ARG = 1
+ERR_RANGE = 2
+
+
+def build(out_path: str = LIB_PATH, defines: tuple[str, ...] = ()) -> str:
+    """Compile the oracle with gcc: no FMA contraction, no fast-math, plain -O2."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra"]
+    cmd += [f"-D{d}" for d in defines]
+    cmd += [SOURCE, "-o", out_path + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+_lib = None
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int
+    i64 = ctypes.c_int64
+    f32 = ctypes.c_float
+    lib.pkvo_f32_to_f16.argtypes = [f32]
+    lib.pkvo_f32_to_f16.restype = ctypes.c_uint16
+    lib.pkvo_f32_to_bf16.argtypes = [f32]
+    lib.pkvo_f32_to_bf16.restype = ctypes.c_uint16
+    lib.pkvo_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.pkvo_f16_to_f32.restype = f32
+    lib.pkvo_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.pkvo_bf16_to_f32.restype = f32
+    lib.pkvo_encode_array.argtypes = [P, P, i64, i32]
+    lib.pkvo_encode_array.restype = None
+    lib.pkvo_decode_array.argtypes = [P, P, i64, i32]
+    lib.pkvo_decode_array.restype = None
+    lib.pkvo_rmsnorm_head.argtypes = [P, P, f32, i32, P]
+    lib.pkvo_rmsnorm_head.restype = None
+    lib.pkvo_rope_head.argtypes = [P, i32, i32, f32, P]
+    lib.pkvo_rope_head.restype = None
+    lib.pkvo_kv_append.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, f32, f32,
+                                   i32, i32, i32, i32, i32, i64, i32]
+    lib.pkvo_kv_append.restype = i32
+    lib.pkvo_paged_attn_decode.argtypes = [P, P, P, P, i32, P, f32, P,
+                                           i32, i32, i32, i32, i32, i64, i32, P]
+    lib.pkvo_paged_attn_decode.restype = i32
+    return lib
+
+
+def load(path: str = LIB_PATH, rebuild: bool = False):
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    if path == LIB_PATH and _lib is not None and not rebuild:
+        return _lib
+    if rebuild or not os.path.exists(path) or (
+            path == LIB_PATH and os.path.getmtime(path) < os.path.getmtime(SOURCE)):
+        build(path)
+    lib = _bind(ctypes.CDLL(path))
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _dtype_code(dtype) -> int:
+    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def encode(x: np.ndarray, dtype, lib=None) -> np.ndarray:
+    """float32 array -> uint16 codes (fp16 or bf16 rule)."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.pkvo_encode_array(_ptr(x), _ptr(out), x.size, _dtype_code(dtype))
+    return out
+
+
+def decode(c: np.ndarray, dtype, lib=None) -> np.ndarray:
+    """uint16 codes -> float32 (exact)."""
+    lib = lib or load()
+    c = np.ascontiguousarray(c, dtype=np.uint16)
+    out = np.empty(c.shape, dtype=np.float32)
+    lib.pkvo_decode_array(_ptr(c), _ptr(out), c.size, _dtype_code(dtype))
+    return out
+
+
+def rmsnorm_head(x: np.ndarray, w: np.ndarray, eps: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    y = np.empty_like(x)
+    lib.pkvo_rmsnorm_head(_ptr(x), _ptr(w), float(eps), x.size, _ptr(y))
+    return y
+
+
+def rope_head(x: np.ndarray, pos: int, theta: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    lib.pkvo_rope_head(_ptr(x), x.size, int(pos), float(theta), _ptr(y))
+    return y
+
+
+def kv_append(q_in, k_in, v_in, k_pool, v_pool, tables, positions, q_norm_w, k_norm_w,
+              eps, theta, dtype, lib=None):
+    """Append one token per sequence. Updates k_pool / v_pool (uint16, [NB, bs, Hkv, D]) IN
+    PLACE and returns q_out [B, Hq, D] float32."""
+    lib = lib or load()
+    q_in = np.ascontiguousarray(q_in, dtype=np.float32)
+    k_in = np.ascontiguousarray(k_in, dtype=np.float32)
+    v_in = np.ascontiguousarray(v_in, dtype=np.float32)
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    assert k_pool.dtype == np.uint16 and v_pool.dtype == np.uint16
+    assert k_pool.flags["C_CONTIGUOUS"] and v_pool.flags["C_CONTIGUOUS"]
+    B, Hq, D = q_in.shape
+    Hkv = k_in.shape[1]
+    NB, bs = k_pool.shape[0], k_pool.shape[1]
+    qn = None if q_norm_w is None else np.ascontiguousarray(q_norm_w, dtype=np.float32)
+    kn = None if k_norm_w is None else np.ascontiguousarray(k_norm_w, dtype=np.float32)
+    q_out = np.empty_like(q_in)
+    st = lib.pkvo_kv_append(_ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(q_out), _ptr(k_pool),
+                            _ptr(v_pool), _ptr(tables), tables.shape[1], _ptr(positions),
+                            _ptr(qn), _ptr(kn), float(eps), float(theta), B, Hq, Hkv, D, bs,
+                            NB, _dtype_code(dtype))
+    if st != OK:
+        raise ValueError(f"oracle kv_append failed with status {st}")
+    return q_out
+
+
+def paged_attn_decode(q, k_pool, v_pool, tables, context_lens, scale, dtype, Hkv=None,
+                      row_mask=None, lib=None):
+    """Decode attention for one query token per sequence; returns out [B, Hq, D] float32.
+    Rows not selected by ``row_mask`` are left as NaN."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    NB, bs = k_pool.shape[0], k_pool.shape[1]
+    Hkv = k_pool.shape[2] if Hkv is None else Hkv
+    mask = None if row_mask is None else np.ascontiguousarray(row_mask, dtype=np.uint8)
+    out = np.full_like(q, np.nan)
+    st = lib.pkvo_paged_attn_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(tables),
+                                    tables.shape[1], _ptr(context_lens), float(scale), _ptr(out),
+                                    B, Hq, Hkv, D, bs, NB, _dtype_code(dtype), _ptr(mask))
+    if st != OK:
+        raise ValueError(f"oracle paged_attn_decode failed with status {st}")
+    return out
+
+
+def decode_step(wl, lib=None):
+    """Oracle of one whole step on a workload dict (see paged_kv_cache_315_amd.workloads):
+    append into copies of the pools, then attend. Returns (q_out, out, k_pool, v_pool)."""
+    k_pool = wl["k_pool"].copy()
+    v_pool = wl["v_pool"].copy()
+    q_out = kv_append(wl["q"], wl["k_new"], wl["v_new"], k_pool, v_pool, wl["tables"],
+                      wl["positions"], wl["q_norm_w"], wl["k_norm_w"], wl["eps"], wl["theta"],
+                      wl["dtype"], lib=lib)
+    out = paged_attn_decode(q_out, k_pool, v_pool, wl["tables"], wl["context_lens"],
+                            wl["scale"], wl["dtype"], lib=lib)
+    return q_out, out, k_pool, v_pool

@@ -1,0 +1,393 @@
+/*
+ * pkv_oracle.c — plain, slow, single-threaded CPU oracle of the paged-KV decode step.
+ *
+ * TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
+ * leg load this library. The product path (paged_kv_cache_315_amd/) never links, imports
+ * or calls it, and this file shares no code, header, table or constant with the HIP path.
+ *
+ * Arithmetic: IEEE double, evaluated in program order. Build with
+ *   gcc -O2 -ffp-contract=off -fno-fast-math
+ * so that no product and sum are fused and nothing is reassociated.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MK-DEC]  makarna/pkg/model/arch/hybrid_decoder.go
+ *             - runHybridAttentionBlock: QK-norm before RoPE, scale = 1/sqrt(HeadDim),
+ *               startPos = cache.SeqLen(), kvLen = startPos + seqLen.
+ *             - runHybridAttentionBlockBatch: one new token per sequence, kvLen = startPos + 1,
+ *               queryPos = startPos, per-sequence block lists.
+ *   [MK-KV]   makarna/pkg/kvcache/paged_cache.go
+ *             - float32ToFloat16Bits / float32ToBFloat16Bits: the stored-bit rules.
+ *             - GetBlockForPosition / GetBlockOffset: block = list[pos / BlockSize], slot = pos % BlockSize.
+ *             - Append: a token's kvDim row is written at blockOffset * kvDim inside its block
+ *               (token-major block rows), K and V kept in separate tensors per block.
+ *             - viewsLockedAt: only the first kvLen tokens of the block list are valid.
+ *   [GL-FWD]  soft3/glia/run/arch/decoder/forward.rs
+ *             - forward_layer, QK-norm step: RMS normalisation per head vector with q_norm/k_norm.
+ *             - forward_layer, RoPE step: full head_dim rotary for LlamaStyle layers.
+ *             - forward_layer, CPU attention path: kv_h = h / (num_heads / kv_heads),
+ *               scores = (q.k) * scale, max, exp(s - max), normalise, out += p * v.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in the design notes):
+ *   R-ROPE   rotate-half pairing (i, i + D/2), angle pos * theta^(-2i/D), all in double,
+ *            one rounding of each rotated element to float.
+ *   R-NORM   y = x / sqrt(mean(x^2) + eps) * w per head vector, double internals.
+ *   R-BF16NAN  NaN inputs to the bf16 rule keep the sign and the 7 leading payload bits,
+ *            forced non-zero (the fp16 rule's NaN treatment carried to bf16 width).
+ *
+ * Parity status of each function is stated in its comment ("pinned by" / "parity unpinned").
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define PKVO_OK 0
+#define PKVO_ERR_ARG 1
+#define PKVO_ERR_RANGE 2
+
+#define PKVO_F16 1
+#define PKVO_BF16 2
+
+/* Planted mistakes for the tests that prove the pins bite (0 = the oracle as specified).
+ * Each mutant is a plausible slip: a dropped term, a wrong sign or index, an off-by-one. */
+#ifndef PKVO_MUTANT
+#define PKVO_MUTANT 0
+#endif
+#define MUT(n) (PKVO_MUTANT == (n))
+
+/* ------------------------------------------------------------------------------------------
+ * Conversions float -> 16-bit codes.
+ *
+ * [MK-KV] float32ToFloat16Bits and float32ToBFloat16Bits fix the stored bits. For every
+ * non-NaN input both rules give the IEEE-754 round-to-nearest, ties-to-even result (with
+ * overflow to infinity at max + half an ulp), so the oracle writes that definition out
+ * directly on the VALUE: count how many quanta of the target format's spacing the magnitude
+ * holds, round that count with rint() (ties to even under the default rounding mode), and
+ * assemble the code. Only the NaN branch is a bit rule and is taken from the page as stated.
+ *
+ * Pinned by: the exhaustive nearest/ties-to-even property over all 2^32 inputs, x86 F16C /
+ * AVX512-BF16 hardware conversion on normal inputs, numpy's float16 cast, and hand-derived
+ * values from the page's rules (tests/golden/convert_values.txt).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Round the magnitude a >= 0 (finite) to a binary format with `prec` significand bits
+ * (implicit bit included) and minimum normal exponent emin, maximum exponent emax.
+ * Returns the code without sign: exponent field (biased by 1 - emin) << (prec-1) | fraction,
+ * or the infinity code when the rounded value exceeds the largest finite one. */
+static uint32_t round_magnitude(double a, int prec, int emin, int emax)
+{
+    const uint32_t frac_bits = (uint32_t)(prec - 1);
+    const uint32_t inf_code = (uint32_t)(emax - emin + 2) << frac_bits;
+    const double one_binade = ldexp(1.0, prec - 1); /* quanta count at the bottom of a binade */
+    if (a == 0.0)
+        return 0;
+    int e2;
+    (void)frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;      /* a in [2^E, 2^(E+1)) */
+    if (E < emin)
+        E = emin;        /* subnormal range: the quantum stays at 2^(emin - prec + 1) */
+    /* number of quanta of size 2^(E - prec + 1); exact (a has at most 24 significant bits) */
+    double q = MUT(7) ? round(ldexp(a, prec - 1 - E)) : rint(ldexp(a, prec - 1 - E));
+    if (q >= 2.0 * one_binade) { /* rounding carried into the next binade */
+        q = q / 2.0;
+        E += 1;
+    }
+    if (E > emax)
+        return inf_code;
+    if (q < one_binade) /* subnormal (or zero): exponent field 0, fraction = quanta count */
+        return (uint32_t)q;
+    return ((uint32_t)(E - emin + 1) << frac_bits) | ((uint32_t)q - (uint32_t)one_binade);
+}
+
+/* [MK-KV] float32ToFloat16Bits. */
+uint16_t pkvo_f32_to_f16(float x)
+{
+    uint32_t bits;
+    memcpy(&bits, &x, 4);
+    const uint16_t sign = (bits & 0x80000000u) ? 0x8000u : 0u;
+    if (isnan(x)) {
+        /* page rule: keep the sign, all-ones exponent, and the 10 leading payload bits,
+         * forced to be non-zero so the code stays a NaN (no quieting). */
+        uint16_t payload = (uint16_t)((bits & 0x007FFFFFu) >> 13);
+        if (payload == 0)
+            payload = 1;
+        return (uint16_t)(sign | 0x7C00u | payload);
+    }
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | round_magnitude(fabs((double)x), 11, -14, 15));
+}
+
+/* [MK-KV] float32ToBFloat16Bits for non-NaN inputs; R-BF16NAN for NaN inputs (the page's
+ * rule, applied to a NaN, can round the payload into an infinity or wrap it to zero). */
+uint16_t pkvo_f32_to_bf16(float x)
+{
+    uint32_t bits;
+    memcpy(&bits, &x, 4);
+    const uint16_t sign = (bits & 0x80000000u) ? 0x8000u : 0u;
+    if (isnan(x)) {
+        uint16_t payload = (uint16_t)((bits & 0x007FFFFFu) >> 16);
+        if (payload == 0)
+            payload = 1;
+        return (uint16_t)(sign | 0x7F80u | payload);
+    }
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7F80u);
+    return (uint16_t)(sign | round_magnitude(fabs((double)x), 8, -126, 127));
+}
+
+/* Exact decode of a 16-bit code to float: value = significand * 2^exponent, built with
+ * ldexp (every fp16 and bf16 value is a float). Pinned by numpy float16 -> float32 and by
+ * bf16 bits << 16 reinterpretation in the tests. */
+static float decode_code(uint16_t c, int prec, int emin, int emax)
+{
+    const int frac_bits = prec - 1;
+    const int exp_bits = 15 - frac_bits;
+    const uint32_t frac = c & ((1u << frac_bits) - 1u);
+    const uint32_t ef = (c >> frac_bits) & ((1u << exp_bits) - 1u);
+    const int neg = (c & 0x8000u) != 0;
+    double v;
+    if (ef == (1u << exp_bits) - 1u)
+        v = frac ? NAN : INFINITY;
+    else if (ef == 0)
+        v = ldexp((double)frac, emin - frac_bits);
+    else
+        v = ldexp((double)((1u << frac_bits) | frac), (int)ef - 1 + emin - frac_bits);
+    (void)emax;
+    return (float)(neg ? -v : v);
+}
+
+float pkvo_f16_to_f32(uint16_t c) { return decode_code(c, 11, -14, 15); }
+float pkvo_bf16_to_f32(uint16_t c) { return decode_code(c, 8, -126, 127); }
+
+static uint16_t encode(float x, int dtype)
+{
+    return dtype == PKVO_F16 ? pkvo_f32_to_f16(x) : pkvo_f32_to_bf16(x);
+}
+
+static float decode(uint16_t c, int dtype)
+{
+    return dtype == PKVO_F16 ? pkvo_f16_to_f32(c) : pkvo_bf16_to_f32(c);
+}
+
+/* Convert n floats to codes (array form for the tests). */
+void pkvo_encode_array(const float* x, uint16_t* out, int64_t n, int dtype)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = encode(x[i], dtype);
+}
+
+void pkvo_decode_array(const uint16_t* c, float* out, int64_t n, int dtype)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = decode(c[i], dtype);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Per-head QK RMS normalisation, reading R-NORM.
+ * [MK-DEC] runHybridAttentionBlock applies QNorm / KNorm (RMSNorm with a weight and eps) to
+ * the projected Q and K before RoPE; [GL-FWD] forward_layer reshapes Q to [num_heads, head_dim]
+ * and K to [kv_heads, head_dim] and normalises each row with the q_norm / k_norm weight, and its
+ * per-head V norm shows the form x / sqrt(mean(x^2) + eps).
+ * Pinned by: constant-vector closed form, mean(y^2) identity with unit weight, scale invariance,
+ * an independent numpy formula (tests/test_oracle_norm_rope.py).
+ * ------------------------------------------------------------------------------------------ */
+void pkvo_rmsnorm_head(const float* x, const float* w, float eps, int D, float* y)
+{
+    double ss = 0.0;
+    for (int j = 0; j < D; ++j)
+        ss += (double)x[j] * (double)x[j];
+    const double r = 1.0 / sqrt(ss / (double)D + (MUT(3) ? 0.0 : (double)eps));
+    for (int j = 0; j < D; ++j)
+        y[j] = (float)(((double)x[j] * r) * (double)w[j]);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * RoPE on one head vector, reading R-ROPE.
+ * [MK-DEC] runHybridAttentionBlock rotates Q and K with HybridRoPE(positions, HeadDim, RopeTheta)
+ * after the QK-norm (and only fuses it when HeadDim is even and at most 256); [GL-FWD]
+ * forward_layer uses Op::Rope with rope_dim = head_dim for LlamaStyle layers.
+ * Pinned by: position 0 is the identity bit for bit, norm preservation, the relative-position
+ * property, an independent complex-exponential formulation in numpy.
+ * ------------------------------------------------------------------------------------------ */
+void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
+{
+    const int half = D / 2;
+    for (int i = 0; i < half; ++i) {
+        const double inv_freq = pow((double)theta, -((MUT(2) ? 1.0 : 2.0) * (double)i) / (double)D);
+        const double angle = (double)(pos + (MUT(8) ? 1 : 0)) * inv_freq;
+        const double c = cos(angle);
+        const double s = sin(angle);
+        const double x0 = (double)x[i];
+        const double x1 = (double)x[i + half];
+        y[i] = (float)(MUT(1) ? x0 * c + x1 * s : x0 * c - x1 * s);
+        y[i + half] = (float)(x1 * c + x0 * s);
+    }
+}
+
+/* Pool element offset of (block, slot, kv head, dim) in a [num_blocks, bs, Hkv, D] pool
+ * ([MK-KV] Append: row of token at blockOffset * kvDim, kvDim = Hkv * D, head-minor). */
+static int64_t pool_offset(int64_t blk, int slot, int g, int d, int bs, int Hkv, int D)
+{
+    return ((blk * bs + slot) * Hkv + g) * (int64_t)D + d;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * KV append for a batch of one new token per sequence.
+ * [MK-DEC] runHybridAttentionBlockBatch: for each sequence the new K/V row is appended at
+ * startPos = SeqLen() (the number of tokens already cached) and RoPE uses that position.
+ * [MK-KV] Append: the block is list[pos / BlockSize], the slot pos % BlockSize, and the value is
+ * converted f32 -> fp16 (CastF32ToF16 on the GPU path, float32ToFloat16Bits on the CPU path).
+ *
+ * Inputs (host): q_in [B,Hq,D], k_in / v_in [B,Hkv,D] f32; pools [num_blocks,bs,Hkv,D] codes;
+ * tables [B,max_blocks]; positions [B]; q_norm_w / k_norm_w [D] (both NULL: no QK-norm).
+ * Outputs: q_out [B,Hq,D] f32 (normed, rotated), the new rows of k_pool / v_pool.
+ * Returns PKVO_ERR_RANGE (and writes nothing more) if a position or block id is out of range.
+ * ------------------------------------------------------------------------------------------ */
+int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                   uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                   const int32_t* positions, const float* q_norm_w, const float* k_norm_w,
+                   float eps, float theta, int B, int Hq, int Hkv, int D, int bs,
+                   int64_t num_blocks, int dtype)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (D & 1) || bs <= 0 || Hq % Hkv)
+        return PKVO_ERR_ARG;
+    if ((q_norm_w == NULL) != (k_norm_w == NULL))
+        return PKVO_ERR_ARG;
+    float* tmp = (float*)malloc(sizeof(float) * (size_t)D);
+    float* rot = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!tmp || !rot) {
+        free(tmp);
+        free(rot);
+        return PKVO_ERR_ARG;
+    }
+    int status = PKVO_OK;
+    for (int b = 0; b < B && status == PKVO_OK; ++b) {
+        const int pos = positions[b];
+        if (pos < 0 || pos / bs >= max_blocks) {
+            status = PKVO_ERR_RANGE;
+            break;
+        }
+        const int64_t blk = tables[(int64_t)b * max_blocks + pos / bs];
+        const int slot = pos % bs;
+        if (blk < 0 || blk >= num_blocks) {
+            status = PKVO_ERR_RANGE;
+            break;
+        }
+        /* Q: optional norm, then RoPE; the float result is the output (not stored in the pool). */
+        for (int h = 0; h < Hq; ++h) {
+            const float* x = q_in + ((int64_t)b * Hq + h) * D;
+            const float* src = x;
+            if (q_norm_w) {
+                pkvo_rmsnorm_head(x, q_norm_w, eps, D, tmp);
+                src = tmp;
+            }
+            pkvo_rope_head(src, D, pos, theta, q_out + ((int64_t)b * Hq + h) * D);
+        }
+        /* K: optional norm, RoPE, convert, store. V: convert, store. */
+        for (int g = 0; g < Hkv; ++g) {
+            const float* x = k_in + ((int64_t)b * Hkv + g) * D;
+            const float* src = x;
+            if (k_norm_w) {
+                pkvo_rmsnorm_head(x, k_norm_w, eps, D, tmp);
+                src = tmp;
+            }
+            pkvo_rope_head(src, D, pos, theta, rot);
+            const float* v = v_in + ((int64_t)b * Hkv + g) * D;
+            for (int d = 0; d < D; ++d) {
+                const int64_t o = pool_offset(blk, slot, g, d, bs, Hkv, D);
+                k_pool[o] = encode(rot[d], dtype);
+                v_pool[o] = encode(v[d], dtype);
+            }
+        }
+    }
+    free(tmp);
+    free(rot);
+    return status;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Paged-attention decode for one query token per sequence.
+ * [MK-DEC] runHybridAttentionBlockBatch passes q [B, Hq*D], per-sequence block lists, kvLens and
+ * scale = 1/sqrt(HeadDim); [MK-KV] viewsLockedAt clips the last block to kvLen tokens;
+ * [GL-FWD] forward_layer's CPU attention path fixes the arithmetic: the query head h reads KV head
+ * h / (Hq/Hkv); s_t = (q . k_t) * scale; m = max s_t; e_t = exp(s_t - m); out = sum e_t v_t / sum e_t.
+ * Steps as written here: gather the sequence's K and V into contiguous float arrays
+ * [L, Hkv, D] (exact decode of the codes), then dense attention in double for every query head.
+ * The max ignores NaN scores (as a float max fold does); a NaN score still makes sum e_t NaN.
+ *
+ * row_mask (may be NULL): compute only the sequences b with row_mask[b] != 0.
+ * Pinned by: brute force against an independent numpy formulation, closed forms (L = 1,
+ * K = 0, V[t] = t), block-permutation invariance, GQA = MHA with duplicated heads.
+ * ------------------------------------------------------------------------------------------ */
+int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                           const int32_t* tables, int max_blocks, const int32_t* context_lens,
+                           float scale, float* out, int B, int Hq, int Hkv, int D, int bs,
+                           int64_t num_blocks, int dtype, const uint8_t* row_mask)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv)
+        return PKVO_ERR_ARG;
+    const int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b) {
+        if (row_mask && !row_mask[b])
+            continue;
+        const int L = context_lens[b] - (MUT(9) && context_lens[b] > 1 ? 1 : 0);
+        if (L < 1 || (L + bs - 1) / bs > max_blocks)
+            return PKVO_ERR_RANGE;
+        float* kc = (float*)malloc(sizeof(float) * (size_t)L * Hkv * D);
+        float* vc = (float*)malloc(sizeof(float) * (size_t)L * Hkv * D);
+        double* e = (double*)malloc(sizeof(double) * (size_t)L);
+        if (!kc || !vc || !e) {
+            free(kc);
+            free(vc);
+            free(e);
+            return PKVO_ERR_ARG;
+        }
+        int status = PKVO_OK;
+        /* gather: token t lives in block tables[b][t / bs] at slot t % bs */
+        for (int t = 0; t < L && status == PKVO_OK; ++t) {
+            const int64_t blk = tables[(int64_t)b * max_blocks + t / bs];
+            if (blk < 0 || blk >= num_blocks) {
+                status = PKVO_ERR_RANGE;
+                break;
+            }
+            for (int g = 0; g < Hkv; ++g)
+                for (int d = 0; d < D; ++d) {
+                    const int64_t o = pool_offset(blk, (t + (MUT(5) ? 1 : 0)) % bs, g, d, bs, Hkv, D);
+                    kc[((int64_t)t * Hkv + g) * D + d] = decode(k_pool[o], dtype);
+                    vc[((int64_t)t * Hkv + g) * D + d] = decode(v_pool[o], dtype);
+                }
+        }
+        for (int h = 0; h < Hq && status == PKVO_OK; ++h) {
+            const int g = MUT(4) ? h % Hkv : h / G;
+            const float* qh = q + ((int64_t)b * Hq + h) * D;
+            double m = -INFINITY;
+            for (int t = 0; t < L; ++t) {
+                const float* kt = kc + ((int64_t)t * Hkv + g) * D;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += (double)qh[d] * (double)kt[d];
+                e[t] = (MUT(6) ? 1.0 : (double)scale) * dot;
+                if (e[t] > m) /* NaN never compares greater: ignored by the max */
+                    m = e[t];
+            }
+            double l = 0.0;
+            for (int t = 0; t < L; ++t) {
+                e[t] = exp(e[t] - m);
+                l += e[t];
+            }
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int t = 0; t < L; ++t)
+                    acc += e[t] * (double)vc[((int64_t)t * Hkv + g) * D + d];
+                out[((int64_t)b * Hq + h) * D + d] = (float)(acc / l);
+            }
+        }
+        free(kc);
+        free(vc);
+        free(e);
+        if (status != PKVO_OK)
+            return status;
+    }
+    return PKVO_OK;
+}
