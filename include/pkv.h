@@ -1,0 +1,178 @@
+/*
+ * pkv.h — C ABI of the paged-KV decode step on AMD Instinct MI355X (gfx950).
+ *
+ * One decoder layer's decode step over a paged KV cache is two calls on one HIP stream:
+ *
+ *   pkv_kv_append          new token of every sequence: optional per-head QK-RMSNorm, RoPE,
+ *                          f32 -> fp16/bf16 round-to-nearest-even, scatter of its K and V rows
+ *                          into the block pools;
+ *   pkv_paged_attn_decode  softmax(scale * q . K^T) . V over each sequence's block list, with
+ *                          grouped-query heads sharing one KV head, split over the token axis
+ *                          and merged.
+ *
+ * Sources (web pages, by title and section):
+ *   makarna/pkg/model/arch/hybrid_decoder.go — runHybridAttentionBlock (QK-norm before RoPE,
+ *     scale = 1/sqrt(HeadDim), fused-RoPE limits: even HeadDim <= 256) and
+ *     runHybridAttentionBlockBatch (one query row per sequence, per-sequence block lists,
+ *     kvLen = startPos + 1, queryPos = startPos, maxKvLen passed for grid sizing).
+ *   makarna/pkg/kvcache/paged_cache.go — float32ToFloat16Bits / float32ToBFloat16Bits (stored
+ *     bits), GetBlockForPosition / GetBlockOffset (block = list[pos / BlockSize],
+ *     slot = pos % BlockSize), Append (a token's row of kvDim = kv_heads * head_dim elements at
+ *     offset slot * kvDim inside its block; K and V in separate tensors), viewsLockedAt (only
+ *     the first kvLen tokens are valid).
+ *   soft3/glia/run/arch/decoder/forward.rs — forward_layer: per-head QK-norm, RoPE over the
+ *     full head_dim, CPU attention (kv head = h / (Hq / Hkv), max-subtracted softmax).
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked (device) are HIP device pointers owned by the caller; the library never
+ *     allocates, frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and the call returns as soon as it is enqueued.
+ *   - Pools: k_pool and v_pool are two arrays of 16-bit codes shaped
+ *     [num_blocks, block_size, num_kv_heads, head_dim], row-major: element (blk, slot, g, d)
+ *     is at ((blk * block_size + slot) * num_kv_heads + g) * head_dim + d. Offsets are 64-bit.
+ *   - block_tables: int32 [B, max_blocks_per_seq], row-major; row b lists the physical block
+ *     ids of sequence b in logical order. Entries past a sequence's length are never read.
+ *   - Device-array CONTENTS are preconditions, not checked on the hot path (checking needs a
+ *     synchronisation): block ids in [0, num_blocks), positions[b] in
+ *     [0, max_blocks_per_seq * block_size), context_lens[b] in [1, max_context_len], and no
+ *     two sequences appending into the same (block, slot). Kernels clamp every index into its
+ *     array, so a violated precondition gives wrong values, never an out-of-bounds access.
+ *     pkv_validate_tables checks the contents on host copies.
+ *   - Non-finite data is not an error: NaN and Inf propagate through the arithmetic.
+ *   - Every call returns a pkv_status; on failure nothing was enqueued and pkv_last_error()
+ *     returns a description (thread-local, valid until the thread's next failing call).
+ *   - The functions are stateless and thread-safe.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, theta <= 0 ... */
+    PKV_ERR_UNSUPPORTED = 2, /* shape the kernels are not built for (see each call) */
+    PKV_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than pkv_decode_workspace_bytes */
+    PKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum {
+    PKV_F16 = 1,  /* IEEE binary16 */
+    PKV_BF16 = 2  /* bfloat16 */
+} pkv_dtype;
+
+/*
+ * pkv_kv_append — write the new token of each of B sequences into the cache.
+ *
+ * For each sequence b, with p = positions[b] (the number of tokens already cached, which is
+ * both the write slot and the RoPE position; makarna's startPos = SeqLen()):
+ *   1. if q_norm_w and k_norm_w are given: every head vector x of q and of k becomes
+ *      x / sqrt(mean(x^2) + rms_eps) * w (w = q_norm_w for q heads, k_norm_w for k heads);
+ *   2. RoPE: for i < D/2 the pair (x[i], x[i + D/2]) is rotated by the angle
+ *      p * rope_theta^(-2i/D); the angle, cos, sin and the rotation are evaluated in double
+ *      and each result is rounded once to float;
+ *   3. q_out[b] = the rotated q (float);
+ *   4. the rotated k and the input v are converted to 16-bit codes (round to nearest, ties to
+ *      even, overflow to infinity; a NaN keeps its sign and leading payload bits, forced
+ *      non-zero) and stored at block block_tables[b][p / block_size], slot p % block_size,
+ *      for every KV head. No other pool element is written.
+ *
+ * q_in   (device) float [B, num_q_heads, head_dim]
+ * k_in   (device) float [B, num_kv_heads, head_dim]
+ * v_in   (device) float [B, num_kv_heads, head_dim]
+ * q_out  (device) float [B, num_q_heads, head_dim]; may equal q_in (updated in place)
+ * k_pool, v_pool (device) 16-bit codes, layout above; written at one row per sequence
+ * block_tables (device) int32 [B, max_blocks_per_seq]
+ * positions    (device) int32 [B]
+ * q_norm_w, k_norm_w (device) float [head_dim] each, or both NULL for no QK-norm
+ * rms_eps      used only with the norm weights
+ * rope_theta   RoPE base, > 0
+ * Errors: INVALID_ARG for a NULL required pointer, B < 0, a non-positive size, Hq % Hkv != 0,
+ *   rope_theta <= 0 or not finite, exactly one norm weight NULL, an unknown dtype;
+ *   UNSUPPORTED for an odd head_dim or head_dim > 256 (the limits of the fused RoPE path).
+ *   B == 0 is a no-op.
+ */
+pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                         void* k_pool, void* v_pool, const int32_t* block_tables,
+                         int max_blocks_per_seq, const int32_t* positions, const float* q_norm_w,
+                         const float* k_norm_w, float rms_eps, float rope_theta, int B,
+                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int64_t num_blocks, pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_paged_attn_decode — one query token per sequence against its paged K/V.
+ *
+ * For each sequence b with L = context_lens[b] tokens and each query head h (KV head
+ * g = h / (num_q_heads / num_kv_heads)):
+ *   s_t = scale * (q[b][h] . K[t][g]) for t < L, where token t of sequence b lives in block
+ *         block_tables[b][t / block_size] at slot t % block_size;
+ *   out[b][h] = sum_t exp(s_t - max s) V[t][g] / sum_t exp(s_t - max s).
+ * Arithmetic is float (fp16/bf16 codes decode exactly); the token axis is cut into partitions
+ * of split_tokens tokens, each partition keeps a running max / sum / weighted V (online
+ * softmax), and partitions are merged with their max-rescaled weights.
+ *
+ * q            (device) float [B, num_q_heads, head_dim] (q_out of pkv_kv_append)
+ * k_pool, v_pool (device) 16-bit codes, layout above; read only
+ * block_tables (device) int32 [B, max_blocks_per_seq]
+ * context_lens (device) int32 [B]; tokens attended (= positions + 1 after an append)
+ * max_context_len  host int >= every context_lens[b]; sizes the grid (tokens beyond it are
+ *                  not attended)
+ * scale        host float; the pages pass 1/sqrt(head_dim)
+ * out          (device) float [B, num_q_heads, head_dim]
+ * workspace    (device) scratch of at least pkv_decode_workspace_bytes(...) bytes, or NULL when
+ *              that size is 0; contents need no initialisation and are not meaningful after
+ * split_tokens tokens per partition, a positive multiple of 64, or 0 to let the library choose
+ *              from the shape (pkv_decode_split_tokens)
+ * Errors: INVALID_ARG as for pkv_kv_append, plus max_context_len < 0, split_tokens not 0 or a
+ *   positive multiple of 64; UNSUPPORTED for head_dim not in {32, 64, 128, 256} or a GQA group
+ *   num_q_heads / num_kv_heads above 8; WORKSPACE when the workspace is too small.
+ *   B == 0 or max_context_len == 0 is a no-op.
+ */
+pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 int split_tokens, int B, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, int64_t num_blocks,
+                                 pkv_dtype dtype, void* stream);
+
+/* Tokens per split-K partition that pkv_paged_attn_decode uses for split_tokens == 0. Host
+ * only; depends on the shape and on the current device's compute-unit count. Returns 0 on
+ * invalid arguments. */
+int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_dim,
+                            int max_context_len);
+
+/* Workspace bytes pkv_paged_attn_decode needs for these arguments (split_tokens as passed to
+ * it, 0 = the library's choice): B * num_q_heads * S * (head_dim + 2) * 4 with
+ * S = ceil(max_context_len / split_tokens) partitions, or 0 when S <= 1. Host only. */
+size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int max_context_len, int split_tokens);
+
+/* Debug check of the device-array preconditions on HOST copies of the arrays (any may be
+ * NULL to skip it): every block id a sequence uses is in [0, num_blocks); positions[b] in
+ * [0, max_blocks_per_seq * block_size); context_lens[b] in [1, max_context_len] and covered
+ * by the table row; no two sequences append into the same (block, slot). Returns PKV_OK or
+ * PKV_ERR_INVALID_ARG with the first violation in pkv_last_error(). */
+pkv_status pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* positions, const int32_t* context_lens, int B,
+                               int block_size, int64_t num_blocks, int max_context_len);
+
+/* Static name of a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Description of the calling thread's last failure ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -33,6 +33,9 @@
  *   R-NORM   y = x / sqrt(mean(x^2) + eps) * w per head vector, double internals.
  *   R-BF16NAN  NaN inputs to the bf16 rule keep the sign and the 7 leading payload bits,
  *            forced non-zero (the fp16 rule's NaN treatment carried to bf16 width).
+ *   R-NAN    a NaN that the norm / RoPE arithmetic produces is the canonical quiet NaN
+ *            0x7FC00000 (IEEE 754 leaves the sign and payload of such a NaN to the
+ *            implementation); a NaN that reaches the converter untouched (V) keeps its bits.
  *
  * Parity status of each function is stated in its comment ("pinned by" / "parity unpinned").
  */
@@ -207,9 +210,19 @@ void pkvo_rmsnorm_head(const float* x, const float* w, float eps, int D, float* 
  * [MK-DEC] runHybridAttentionBlock rotates Q and K with HybridRoPE(positions, HeadDim, RopeTheta)
  * after the QK-norm (and only fuses it when HeadDim is even and at most 256); [GL-FWD]
  * forward_layer uses Op::Rope with rope_dim = head_dim for LlamaStyle layers.
+ * Each rotated element that comes out NaN is stored as the canonical quiet NaN (R-NAN).
  * Pinned by: position 0 is the identity bit for bit, norm preservation, the relative-position
  * property, an independent complex-exponential formulation in numpy.
  * ------------------------------------------------------------------------------------------ */
+static float canonical_nan_if_nan(float v)
+{
+    if (isnan(v)) {
+        const uint32_t qnan = 0x7FC00000u;
+        memcpy(&v, &qnan, 4);
+    }
+    return v;
+}
+
 void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
 {
     const int half = D / 2;
@@ -220,8 +233,8 @@ void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
         const double s = sin(angle);
         const double x0 = (double)x[i];
         const double x1 = (double)x[i + half];
-        y[i] = (float)(MUT(1) ? x0 * c + x1 * s : x0 * c - x1 * s);
-        y[i + half] = (float)(x1 * c + x0 * s);
+        y[i] = canonical_nan_if_nan((float)(MUT(1) ? x0 * c + x1 * s : x0 * c - x1 * s));
+        y[i + half] = canonical_nan_if_nan((float)(x1 * c + x0 * s));
     }
 }
 

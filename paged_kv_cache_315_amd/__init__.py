@@ -1,0 +1,162 @@
+"""paged_kv_cache_315_amd — the paged-KV decode step on AMD Instinct MI355X (gfx950).
+
+Python face of the C ABI in include/pkv.h (libpkv.so, hand-written HIP kernels). torch is
+used only for device memory and streams: every function takes torch tensors that already live
+on the GPU, passes their pointers to libpkv and enqueues the kernels on the current stream.
+
+    kv_append(...)          new token per sequence: QK-norm (optional), RoPE, fp16/bf16
+                            round-to-nearest-even, scatter into the block pools
+    paged_attn_decode(...)  softmax(scale q.K^T).V over each sequence's block list (GQA)
+    decode_step(...)        both, as one decoder layer's attention step
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import PKV_BF16, PKV_F16, PkvError
+
+__all__ = ["kv_append", "paged_attn_decode", "decode_step", "decode_workspace_bytes",
+           "decode_split_tokens", "validate_tables", "version", "PkvError", "pool_dtype_code"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def version() -> str:
+    return _lib.load().pkv_version().decode()
+
+
+def pool_dtype_code(pool, dtype=None) -> int:
+    """PKV_F16 / PKV_BF16 from an explicit name or from the pool tensor's dtype."""
+    torch = _torch()
+    if dtype is not None:
+        return {"f16": PKV_F16, "fp16": PKV_F16, "bf16": PKV_BF16}[dtype]
+    if pool.dtype == torch.float16:
+        return PKV_F16
+    if pool.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise ValueError("pool dtype must be float16 or bfloat16, or pass dtype='f16'|'bf16'")
+
+
+def _dev_ptr(t, name, *, dtype=None, ndim=None, elem_size=None):
+    """Device pointer of a contiguous CUDA(HIP) tensor, after shape/dtype checks."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, theta: float,
+              q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None, dtype=None,
+              stream=None):
+    """Append one token per sequence; returns q_out ([B, Hq, D] float32, normed + rotated).
+
+    q_in [B,Hq,D], k_in / v_in [B,Hkv,D] float32; k_pool / v_pool [NB,bs,Hkv,D] 16-bit;
+    block_tables [B,max_blocks] int32; positions [B] int32 (write slot = RoPE position).
+    """
+    torch = _torch()
+    B, Hq, D = q_in.shape
+    Hkv = k_in.shape[1]
+    NB, bs = k_pool.shape[0], k_pool.shape[1]
+    if q_out is None:
+        q_out = torch.empty_like(q_in)
+    f32 = torch.float32
+    args = (
+        _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
+        _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2), _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
+        _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
+        _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
+        float(eps), float(theta), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
+        _stream(stream))
+    _lib.check(_lib.load().pkv_kv_append(*args), "pkv_kv_append")
+    return q_out
+
+
+def decode_split_tokens(B, Hq, Hkv, D, max_context_len) -> int:
+    return _lib.load().pkv_decode_split_tokens(B, Hq, Hkv, D, max_context_len)
+
+
+def decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens: int = 0) -> int:
+    return _lib.load().pkv_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens)
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                      scale: float, *, out=None, workspace=None, split_tokens: int = 0,
+                      dtype=None, stream=None):
+    """Decode attention for one query token per sequence; returns out [B, Hq, D] float32.
+
+    workspace: uint8 GPU tensor of >= decode_workspace_bytes(...) bytes, allocated here if None.
+    """
+    torch = _torch()
+    B, Hq, D = q.shape
+    NB, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    f32 = torch.float32
+    args = (
+        _dev_ptr(q, "q", dtype=f32, ndim=3), _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
+        _dev_ptr(context_lens, "context_lens", dtype=torch.int32, ndim=1), int(max_context_len),
+        float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3), ws_ptr, ws_bytes,
+        int(split_tokens), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype), _stream(stream))
+    _lib.check(_lib.load().pkv_paged_attn_decode(*args), "pkv_paged_attn_decode")
+    return out
+
+
+def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, context_lens,
+                max_context_len: int, *, theta: float, scale: float, q_norm_w=None,
+                k_norm_w=None, eps: float = 1e-6, q_out=None, out=None, workspace=None,
+                split_tokens: int = 0, dtype=None, stream=None):
+    """One layer's decode step: kv_append then paged_attn_decode on the same stream.
+    Returns (q_out, out)."""
+    q_out = kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, theta=theta,
+                      q_norm_w=q_norm_w, k_norm_w=k_norm_w, eps=eps, q_out=q_out, dtype=dtype,
+                      stream=stream)
+    out = paged_attn_decode(q_out, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                            scale, out=out, workspace=workspace, split_tokens=split_tokens,
+                            dtype=dtype, stream=stream)
+    return q_out, out
+
+
+def validate_tables(block_tables, positions, context_lens, block_size: int, num_blocks: int,
+                    max_context_len: int) -> None:
+    """Host-side precondition check (numpy int32 arrays or None); raises PkvError."""
+    import numpy as np
+
+    def ptr(a):
+        return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+    t, p, c = ptr(block_tables), ptr(positions), ptr(context_lens)
+    B = next(len(x) for x in (t, p, c) if x is not None)
+    st = _lib.load().pkv_validate_tables(
+        None if t is None else t.ctypes.data, t.shape[1] if t is not None else 1,
+        None if p is None else p.ctypes.data, None if c is None else c.ctypes.data, B,
+        block_size, num_blocks, max_context_len)
+    _lib.check(st, "pkv_validate_tables")

@@ -1,0 +1,74 @@
+"""ctypes binding of libpkv.so (the C ABI declared in include/pkv.h).
+
+Argument marshalling only: tensors become device pointers, shapes become ints, the current
+torch stream becomes the hipStream_t. Every step of the computation runs in the HIP kernels
+of libpkv; if the library is missing, loading raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_WORKSPACE = 3
+PKV_ERR_HIP = 4
+PKV_F16 = 1
+PKV_BF16 = 2
+
+# every function include/pkv.h declares, with (restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "pkv_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _F, _F,
+                           _I, _I, _I, _I, _I, _I64, _I, _P]),
+    "pkv_paged_attn_decode": (_I, [_P, _P, _P, _P, _I, _P, _I, _F, _P, _P, _SZ, _I,
+                                   _I, _I, _I, _I, _I, _I64, _I, _P]),
+    "pkv_decode_split_tokens": (_I, [_I, _I, _I, _I, _I]),
+    "pkv_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "pkv_validate_tables": (_I, [_P, _I, _P, _P, _I, _I, _I64, _I]),
+    "pkv_status_string": (ctypes.c_char_p, [_I]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libpkv.so; raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built: run `python -m paged_kv_cache_315_amd.build` "
+            "(the paged-KV kernels have no fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def check(status: int, what: str):
+    if status != PKV_OK:
+        lib = load()
+        msg = lib.pkv_last_error().decode()
+        raise PkvError(status, f"{what}: {lib.pkv_status_string(status).decode()}: {msg}")

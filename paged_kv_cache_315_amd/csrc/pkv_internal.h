@@ -1,0 +1,52 @@
+// Internal declarations shared by the HIP translation units of libpkv (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+    const float* q_in;
+    const float* k_in;
+    const float* v_in;
+    float* q_out;
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const int32_t* tables;
+    const int32_t* positions;
+    const float* q_norm_w;  // nullptr: no QK-norm
+    const float* k_norm_w;
+    int max_blocks;
+    float eps;
+    float theta;
+    int B, Hq, Hkv, D, bs;
+    int64_t num_blocks;
+    bool bf16;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    const float* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* tables;
+    const int32_t* context_lens;
+    float* out;
+    float* part_acc;  // [B, Hq, S, D]
+    float* part_ml;   // [B, Hq, S, 2]
+    int max_blocks;
+    int max_context_len;
+    float scale;
+    int split_tokens;
+    int S;            // partitions per sequence = ceil(max_context_len / split_tokens)
+    int B, Hq, Hkv, D, bs;
+    int64_t num_blocks;
+    bool bf16;
+};
+
+// Launches the partition kernel and, when S > 1, the merge kernel.
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pkv
