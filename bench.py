@@ -10,7 +10,7 @@ The pools exist in R identical copies and step i uses copy i % R, so the K/V str
 step is not still in the 256 MB last-level cache from the previous step.
 
 Prints ONE JSON line. `value` is the step's algorithmic bytes over the step time (GB/s);
-`roofline` is the paged-decode call alone (partition + merge kernels), timed with HIP events
+`roofline` is the paged-decode kernel alone, timed with HIP events
 on its stream; `cpu_baseline` is the single-threaded CPU oracle on one full step of the same
 workload.
 """
@@ -84,7 +84,7 @@ def main() -> int:
     B, Hq, Hkv, D = wl["B"], wl["Hq"], wl["Hkv"], wl["D"]
     split = args.split_tokens
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["max_context_len"], split)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(q)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -170,7 +170,7 @@ def main() -> int:
             "bytes_per_step": nbytes["step"], "kv_bytes": nbytes["kv"],
         },
         "roofline": {
-            "bound": "hbm", "kernel": "paged_attn_decode call (partition + merge kernels)",
+            "bound": "hbm", "kernel": "paged_decode_kernel",
             "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None,
             "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(decode_ms * 1e3, 3),

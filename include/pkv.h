@@ -112,9 +112,11 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *   s_t = scale * (q[b][h] . K[t][g]) for t < L, where token t of sequence b lives in block
  *         block_tables[b][t / block_size] at slot t % block_size;
  *   out[b][h] = sum_t exp(s_t - max s) V[t][g] / sum_t exp(s_t - max s).
- * Arithmetic is float (fp16/bf16 codes decode exactly); the token axis is cut into partitions
- * of split_tokens tokens, each partition keeps a running max / sum / weighted V (online
- * softmax), and partitions are merged with their max-rescaled weights.
+ * Arithmetic is float (fp16/bf16 codes decode exactly; q . k runs on the matrix cores with q
+ * split into a 16-bit high part and a 16-bit remainder, accurate to about 2^-16 relative);
+ * the token axis is cut into partitions of split_tokens tokens, each partition keeps a
+ * running max / sum / weighted V (online softmax), and the last partition of each
+ * (sequence, KV head) to finish merges them with their max-rescaled weights.
  *
  * q            (device) float [B, num_q_heads, head_dim] (q_out of pkv_kv_append)
  * k_pool, v_pool (device) 16-bit codes, layout above; read only
@@ -125,7 +127,10 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  * scale        host float; the pages pass 1/sqrt(head_dim)
  * out          (device) float [B, num_q_heads, head_dim]
  * workspace    (device) scratch of at least pkv_decode_workspace_bytes(...) bytes, or NULL when
- *              that size is 0; contents need no initialisation and are not meaningful after
+ *              that size is 0. It must be ZERO-FILLED before its first use: its last
+ *              B * num_kv_heads ints count finished partitions, and every call leaves them zero
+ *              again (the rest needs no initialisation). Calls that run concurrently (on
+ *              different streams) need separate workspaces.
  * split_tokens tokens per partition, a positive multiple of 64, or 0 to let the library choose
  *              from the shape (pkv_decode_split_tokens)
  * Errors: INVALID_ARG as for pkv_kv_append, plus max_context_len < 0, split_tokens not 0 or a
@@ -148,8 +153,9 @@ int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_d
                             int max_context_len);
 
 /* Workspace bytes pkv_paged_attn_decode needs for these arguments (split_tokens as passed to
- * it, 0 = the library's choice): B * num_q_heads * S * (head_dim + 2) * 4 with
- * S = ceil(max_context_len / split_tokens) partitions, or 0 when S <= 1. Host only. */
+ * it, 0 = the library's choice): B * num_q_heads * S * (head_dim + 2) * 4 partial-result bytes
+ * plus B * num_kv_heads * 4 counter bytes, with S = ceil(max_context_len / split_tokens)
+ * partitions, or 0 when S <= 1. Host only. */
 size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
                                   int max_context_len, int split_tokens);
 

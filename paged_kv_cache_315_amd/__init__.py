@@ -106,7 +106,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
                       dtype=None, stream=None):
     """Decode attention for one query token per sequence; returns out [B, Hq, D] float32.
 
-    workspace: uint8 GPU tensor of >= decode_workspace_bytes(...) bytes, allocated here if None.
+    workspace: uint8 GPU tensor of >= decode_workspace_bytes(...) bytes, zero-filled before its
+    first use (the library keeps its counters zero); allocated here (zeroed) if None.
     """
     torch = _torch()
     B, Hq, D = q.shape
@@ -115,7 +116,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
         out = torch.empty_like(q)
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens) if B else 0
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     f32 = torch.float32

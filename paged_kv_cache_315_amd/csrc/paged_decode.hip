@@ -11,29 +11,68 @@
 //    the block list are valid.)
 //
 // Work decomposition (split-K over the token axis):
-//   grid (S, Hkv, B); workgroup (s, g, b) owns tokens [s*P, min((s+1)*P, L)) of sequence b and
-//   the G query heads of KV head g, so every K/V row is read from HBM exactly once per step.
-//   Its 4 waves take interleaved 16-token tiles. Inside a wave a K or V row of D codes is
-//   spread over R = D/8 lanes (one 16-byte load each), so one dwordx4 load instruction moves
-//   64/R consecutive token rows. Scores are reduced over the R lanes with DPP row operations
-//   (every lane ends with the same sum), the online softmax keeps a running max m, sum l and
-//   weighted V sum per head in float, with exp2 on log2(e)-prescaled scores.
-//   The 4 waves merge through LDS; a sequence with one partition writes out directly, otherwise
-//   the workgroup stores (m, l, acc) and the merge kernel combines the partitions:
+//   grid (Hkv, S, B); workgroup (g, s, b) owns tokens [s*P, min((s+1)*P, L)) of sequence b and
+//   the G query heads of KV head g, so every K/V row is read from HBM once per step. The KV
+//   head is the fastest grid index: the Hkv workgroups of one (b, s) run side by side and
+//   together stream whole [bs, Hkv, D] blocks. The 4 waves of a workgroup take interleaved
+//   16-token tiles and prefetch the next tile's K and V rows while computing the current one.
+//
+// Per 16-token tile and wave:
+//   QK^T on the matrix cores: S[h][t] = sum_d Q[h][d] K[t][d] as D/32 MFMA 16x16x32 steps with
+//     A = Q (16 rows: the G heads, zero-padded), B = K^T taken straight from the loaded rows
+//     (lane l holds token l%16, 8 consecutive dims); Q is pre-scaled by scale*log2(e) and
+//     split into a 16-bit high part and a 16-bit remainder, so two MFMAs per step give the
+//     float product to ~2^-16 (bf16) / ~2^-22 (fp16) relative. For fp16 pools Q is also scaled
+//     by a power of two into the fp16 range and the scores scaled back (exact).
+//   Online softmax on the score layout (lane = token, 4 heads per lane): DPP row max, one exp2
+//     per score, running max m / sum l per head; the P tile goes to LDS ([token][head]).
+//   PV on the vector ALU: each V row is spread over D/8 lanes (16 bytes each, one dwordx4 load
+//     moves 64/(D/8) rows); acc[h][8 dims] += p[h][t] * v[t][dims]; the running sums are
+//     rescaled only in tiles where some head's max grew.
+//   The 4 waves merge through LDS. A sequence with one partition writes out directly; otherwise
+//   each workgroup stores (m, l, acc), and the last workgroup of (b, g) to finish (counted with
+//   an atomic in the workspace, which it resets to zero) merges the partitions; partials and
+//   counters are only touched with agent-scope atomic accesses, coherent across XCDs:
 //     M = max m_i, out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 //
-// Numerics: K/V codes decode exactly to float; dot products, exponentials and sums are float.
-// Tokens outside [0, L) are never multiplied in (their rows are not loaded), so NaN padding in
-// unused slots cannot leak into the result. A running max of -inf (no finite score yet) uses 0
-// as the exponent base so exp2(-inf - (-inf)) never appears.
+// Numerics: K/V codes enter the MFMA unconverted and decode exactly on the PV side; exponentials
+// and sums are float. Tokens outside [0, L) are never loaded or multiplied in, so NaN padding
+// in unused slots cannot leak into the result. A running max of -inf uses 0 as the exponent
+// base so exp2(-inf - (-inf)) never appears. One difference from a float dot product: a key
+// holding +-Inf meets the zero remainder of an exactly representable q element in the MFMA,
+// which gives NaN where float arithmetic would give an infinite score.
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
 constexpr int kWaves = 4;
-constexpr int kTileTokens = 16;          // tokens per wave per iteration
+constexpr int kTile = 16;       // tokens per wave per iteration
+constexpr int kTblCap = 512;    // block ids staged in LDS per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+
+template <bool BF16>
+struct Mma;
+template <>
+struct Mma<true> {
+    using vec = bf16x8;
+    using elem = __bf16;
+    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mma<false> {
+    using vec = f16x8;
+    using elem = _Float16;
+    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 // ---- cross-lane helpers ------------------------------------------------------------------
 template <int CTRL>
@@ -41,31 +80,36 @@ __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over groups of R consecutive lanes; every lane of a group receives the same value (each
-// step adds a lane to its partner under an involution, so both partners add the same pair).
-template <int R>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(R == 4 || R == 8 || R == 16 || R == 32, "R");
-    x += dpp_f<0xB1>(x);                      // quad_perm [1,0,3,2]: lane ^ 1
-    x += dpp_f<0x4E>(x);                      // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (R >= 8) x += dpp_f<0x141>(x);   // row_half_mirror: quad <-> quad in 8 lanes
-    if constexpr (R >= 16) x += dpp_f<0x140>(x);  // row_mirror: half <-> half in 16 lanes
-    if constexpr (R >= 32) x += __shfl_xor(x, 16);
+// Reductions over each row of 16 lanes; every lane of the row receives the same value (each
+// step combines a lane with its partner under an involution: lane^1, lane^2, the other quad
+// of the half row, the other half of the row).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
     return x;
 }
 
-// Reduction across the 64/R groups of a wave (lanes l, l ^ R, l ^ 2R, ...).
-template <int R>
-__device__ __forceinline__ float cross_group_max(float x) {
-#pragma unroll
-    for (int off = R; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
+// Sum across the 64/R lane groups of a wave (lanes l, l ^ R, l ^ 2R, ...).
 template <int R>
 __device__ __forceinline__ float cross_group_sum(float x) {
 #pragma unroll
     for (int off = R; off < 64; off <<= 1) x += __shfl_xor(x, off);
     return x;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <bool BF16>
@@ -83,6 +127,41 @@ __device__ __forceinline__ void decode8(const uint4 raw, float (&f)[8]) {
     }
 }
 
+// Unsigned division by the block size: shift for powers of two, otherwise a multiply-high
+// with a precomputed magic number (round-up method with the add fix-up, exact for all u32).
+struct BlockDiv {
+    uint32_t magic, shift;
+    bool pow2;
+    __device__ __forceinline__ uint32_t div(uint32_t n) const {
+        if (pow2) return n >> shift;
+        const uint32_t t = __umulhi(n, magic);
+        return (t + ((n - t) >> 1)) >> shift;
+    }
+};
+
+__device__ __forceinline__ BlockDiv make_div(uint32_t d) {
+    BlockDiv r;
+    r.pow2 = (d & (d - 1)) == 0;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;  // l = ceil(log2 d)
+    if (r.pow2) {
+        r.shift = l;
+        r.magic = 0;
+    } else {
+        r.magic = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+        r.shift = l - 1;
+    }
+    return r;
+}
+
+// Device-coherent accesses to the partition partials (see the merge at the end of the kernel).
+__device__ __forceinline__ void store_shared(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Attended length of a sequence: context_lens[b], capped by max_context_len and by the
 // tokens its table row can address (so every table and pool index stays in range).
 __device__ __forceinline__ int clamp_len(int L, const DecodeArgs& a) {
@@ -90,145 +169,255 @@ __device__ __forceinline__ int clamp_len(int L, const DecodeArgs& a) {
     return (int)min((int64_t)L, cap);
 }
 
-// ---- partition kernel --------------------------------------------------------------------
 template <int D, int G, bool BF16>
-__global__ __launch_bounds__(kWaves * 64) void paged_decode_part_kernel(DecodeArgs a) {
-    constexpr int R = D / 8;                 // lanes per token row (8 codes per lane)
-    constexpr int TPL = 64 / R;              // token rows per load instruction
-    constexpr int U = kTileTokens / TPL;     // loads per tile
-    static_assert(U >= 1 && U * TPL == kTileTokens, "tile");
+__global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a) {
+    using M = Mma<BF16>;
+    constexpr int NK = D / 32;          // MFMA k-steps (and K loads) per tile
+    constexpr int R = D / 8;            // lanes per V row (8 codes per lane)
+    constexpr int TPL = 64 / R;         // V rows per load instruction
+    constexpr int U = kTile / TPL;      // V loads per tile
+    static_assert(D % 32 == 0 && U * TPL == kTile, "tile shape");
+    static_assert(G >= 1 && G <= 8, "GQA group");
 
+    __shared__ float s_p[kWaves][kTile][16];
+    __shared__ float s_alpha[kWaves][16];
+    __shared__ int32_t s_tbl[kTblCap];
     __shared__ float s_acc[kWaves][G][D];
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
+    __shared__ int s_last;
 
-    const int s = blockIdx.x;
-    const int g = blockIdx.y;
+    const int g = blockIdx.x;
+    const int s = blockIdx.y;
     const int b = blockIdx.z;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int row = lane / R;
-    const int col = lane % R;
+    const int l16 = lane & 15;          // token of the score layout / row of the Q operand
+    const int q4 = lane >> 4;           // lane group: k-slice of the operands, head quad of S
+    const int vrow = lane / R;          // V layout: token row within a load
+    const int vcol = lane % R;          //           8-dim column
 
     const int L = clamp_len(a.context_lens[b], a);
-    const int t_begin = s * a.split_tokens;
-    if (t_begin >= L) return;                // whole workgroup exits together
-    const int t_end = min(L, t_begin + a.split_tokens);
-    const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
-
+    const int P = a.split_tokens;
+    const int t_begin = s * P;
+    if (t_begin >= L) return;           // whole workgroup exits together
+    const int t_end = min(L, t_begin + P);
+    const int nsplit = (L + P - 1) / P;
     const int Hq = a.Hkv * G;
-    const float qs = a.scale * kLog2e;
-    float qr[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float4* qp = reinterpret_cast<const float4*>(
-            a.q + ((int64_t)b * Hq + g * G + h) * D + col * 8);
-        const float4 q0 = qp[0], q1 = qp[1];
-        qr[h][0] = q0.x * qs; qr[h][1] = q0.y * qs; qr[h][2] = q0.z * qs; qr[h][3] = q0.w * qs;
-        qr[h][4] = q1.x * qs; qr[h][5] = q1.y * qs; qr[h][6] = q1.z * qs; qr[h][7] = q1.w * qs;
+
+    // ---- block ids of this partition -> LDS
+    const BlockDiv bdiv = make_div((uint32_t)a.bs);
+    const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+    const int first_blk = (int)bdiv.div((uint32_t)t_begin);
+    const int n_blk = (int)bdiv.div((uint32_t)(t_end - 1)) - first_blk + 1;
+    const bool tbl_in_lds = n_blk <= kTblCap;
+    const int64_t nb_max = a.num_blocks - 1;
+    if (tbl_in_lds) {
+        for (int i = threadIdx.x; i < n_blk; i += kWaves * 64) {
+            const int64_t id = trow[first_blk + i];
+            s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+        }
     }
 
-    float m[G], l[G], acc[G][8];
+    // ---- Q operand: row l16 = head (zero beyond G), k-slice q4, pre-scaled, hi + remainder
+    typename M::vec qhi[NK], qlo[NK];
+    float score_fix = 1.f;
+    {
+        const float qs = a.scale * kLog2e;
+        float qv[NK][8];
+        float qmax = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
+        for (int i = 0; i < NK; ++i) {
+            if (l16 < G) {
+                const float4* qp = reinterpret_cast<const float4*>(
+                    a.q + ((int64_t)b * Hq + g * G + l16) * D + 32 * i + 8 * q4);
+                const float4 x0 = qp[0], x1 = qp[1];
+                qv[i][0] = x0.x; qv[i][1] = x0.y; qv[i][2] = x0.z; qv[i][3] = x0.w;
+                qv[i][4] = x1.x; qv[i][5] = x1.y; qv[i][6] = x1.z; qv[i][7] = x1.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qv[i][j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                qv[i][j] *= qs;
+                qmax = fmaxf(qmax, fabsf(qv[i][j]));
+            }
+        }
+        float qscale = 1.f;
+        if constexpr (!BF16) {
+            // fp16 operand: bring max |q| below 2^14 with an exact power-of-two scale
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+            if (qmax >= 16384.f && qmax <= 3.0e38f) {
+                const int e = ilogbf(qmax) - 13;
+                qscale = ldexpf(1.f, -e);
+                score_fix = ldexpf(1.f, e);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = qv[i][j] * qscale;
+                const typename M::elem hi = (typename M::elem)x;
+                qhi[i][j] = hi;
+                qlo[i][j] = (typename M::elem)(x - (float)hi);
+            }
+        }
+    }
+    __syncthreads();  // s_tbl ready
+
+    const int64_t tok_stride = (int64_t)a.Hkv * D;   // codes between consecutive slots
+    const int64_t head_off = (int64_t)g * D;
+    auto row_off = [&](int t) -> int64_t {
+        const int j = (int)bdiv.div((uint32_t)t);
+        int64_t blk;
+        if (tbl_in_lds) {
+            blk = s_tbl[j - first_blk];
+        } else {
+            const int64_t id = trow[j];
+            blk = id < 0 ? 0 : (id > nb_max ? nb_max : id);
+        }
+        return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
+    };
+    auto load_tile = [&](int base, uint4 (&kr)[NK], uint4 (&vr)[U]) {
+        const int tk = base + l16;
+        if (tk < t_end) {
+            const uint16_t* kp = a.k_pool + row_off(tk) + 8 * q4;
+#pragma unroll
+            for (int i = 0; i < NK; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 32 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NK; ++i) kr[i] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tv = base + u * TPL + vrow;
+            vr[u] = tv < t_end
+                        ? *reinterpret_cast<const uint4*>(a.v_pool + row_off(tv) + 8 * vcol)
+                        : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    float m[4], lsum[4], acc[G][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m[r] = -INFINITY;
+        lsum[r] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-    }
 
-    const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
-    const int64_t nb_max = a.num_blocks - 1;
-    const int64_t tok_stride = (int64_t)a.Hkv * D;   // codes between slots of a block
+    int base = t_begin + wave * kTile;
+    uint4 kc[NK], vc[U];
+    if (base < t_end) load_tile(base, kc, vc);
+    for (; base < t_end; base += kWaves * kTile) {
+        const int nbase = base + kWaves * kTile;
+        uint4 kn[NK], vn[U];
+        if (nbase < t_end) load_tile(nbase, kn, vn);
 
-    for (int base = t_begin + wave * kTileTokens; base < t_end; base += kWaves * kTileTokens) {
-        uint4 kraw[U], vraw[U];
-        bool valid[U];
+        // scores S[head 4*q4 + r][token l16]
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = base + u * TPL + row;
-            valid[u] = t < t_end;
-            if (valid[u]) {
-                int64_t blk = trow[t / a.bs];
-                blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
-                const int64_t off = (blk * a.bs + t % a.bs) * tok_stride + (int64_t)g * D + col * 8;
-                kraw[u] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-                vraw[u] = *reinterpret_cast<const uint4*>(a.v_pool + off);
-            } else {
-                kraw[u] = make_uint4(0, 0, 0, 0);
-                vraw[u] = make_uint4(0, 0, 0, 0);
-            }
+        for (int i = 0; i < NK; ++i) {
+            const typename M::vec kv = __builtin_bit_cast(typename M::vec, kc[i]);
+            sacc = M::mma(qhi[i], kv, sacc);
+            sacc = M::mma(qlo[i], kv, sacc);
         }
-        float sc[U][G];
+        const bool tok_ok = base + l16 < t_end;
+        float p[4], alpha[4];
+        bool grew = false;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kf[8];
-            decode8<BF16>(kraw[u], kf);
+        for (int r = 0; r < 4; ++r) {
+            const bool ok = tok_ok && (4 * q4 + r) < G;
+            const float sc = ok ? sacc[r] * score_fix : -INFINITY;
+            const float tmax = row16_max(sc);
+            const float m_new = fmaxf(m[r], tmax);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            alpha[r] = exp2f(m[r] - m_use);
+            p[r] = exp2f(sc - m_use);
+            lsum[r] = fmaf(lsum[r], alpha[r], p[r]);
+            grew |= m_new != m[r];
+            m[r] = m_new;
+        }
+        *reinterpret_cast<float4*>(&s_p[wave][l16][4 * q4]) = make_float4(p[0], p[1], p[2], p[3]);
+        const bool rescale = __any(grew);
+        if (rescale && l16 == 0)
+            *reinterpret_cast<float4*>(&s_alpha[wave][4 * q4]) =
+                make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
+        wave_lds_sync();
+        if (rescale) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float d0 = 0.f;
+                const float al = s_alpha[wave][h];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) d0 = fmaf(qr[h][j], kf[j], d0);
-                sc[u][h] = group_sum<R>(d0);
+                for (int j = 0; j < 8; ++j) acc[h][j] *= al;
             }
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mx = -INFINITY;
+        for (int u = 0; u < U; ++u) {
+            const int tt = u * TPL + vrow;
+            float pv[G];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (valid[u]) mx = fmaxf(mx, sc[u][h]);
-            mx = cross_group_max<R>(mx);
-            const float m_new = fmaxf(m[h], mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m[h] - m_use);
-            m[h] = m_new;
-            l[h] *= alpha;
+            for (int h = 0; h < G; ++h) pv[h] = s_p[wave][tt][h];
+            float vf[8];
+            decode8<BF16>(vc[u], vf);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] *= alpha;
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (valid[u]) {
-                    const float p = exp2f(sc[u][h] - m_use);
-                    l[h] += p;
-                    float vf[8];
-                    decode8<BF16>(vraw[u], vf);
+                for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pv[h], vf[j], acc[h][j]);
+        }
+        wave_lds_sync();
+        if (nbase < t_end) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(p, vf[j], acc[h][j]);
-                }
-            }
+            for (int i = 0; i < NK; ++i) kc[i] = kn[i];
+#pragma unroll
+            for (int u = 0; u < U; ++u) vc[u] = vn[u];
         }
     }
 
-    // combine the token-row groups of the wave, then the waves of the workgroup
+    // ---- combine within the wave: l over the 16 token lanes, acc over the V row groups
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        l[h] = cross_group_sum<R>(l[h]);
+    for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] = cross_group_sum<R>(acc[h][j]);
+    if (l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * q4 + r;
+            if (h < G) {
+                s_m[wave][h] = m[r];
+                s_l[wave][h] = lsum[r];
+            }
+        }
     }
-    if (row == 0) {
+    if (vrow == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s_acc[wave][h][col * 8 + j] = acc[h][j];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            s_m[wave][h] = m[h];
-            s_l[wave][h] = l[h];
-        }
+            for (int j = 0; j < 8; ++j) s_acc[wave][h][vcol * 8 + j] = acc[h][j];
     }
     __syncthreads();
 
+    // ---- combine the waves: this partition's (M, den, num) per (head, dim)
+    // Partials and counters are shared between workgroups that may sit on different XCDs
+    // (each with its own L2), so every access to them is an agent-scope atomic: those are
+    // coherent device-wide without writing back or invalidating whole L2s, which a release /
+    // acquire fence at agent scope would do for every workgroup.
+    float* part_acc = a.part_acc;
+    float* part_ml = a.part_ml;
     for (int i = threadIdx.x; i < G * D; i += kWaves * 64) {
         const int h = i / D;
         const int d = i % D;
-        float M = -INFINITY;
+        float Mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        const float M_use = (M == -INFINITY) ? 0.f : M;
+        for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+        const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
         float num = 0.f, den = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
@@ -241,61 +430,66 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_part_kernel(DecodeAr
             a.out[((int64_t)b * Hq + hq) * D + d] = num / den;
         } else {
             const int64_t pi = ((int64_t)b * Hq + hq) * a.S + s;
-            a.part_acc[pi * D + d] = num;
+            store_shared(part_acc + pi * D + d, num);
             if (d == 0) {
-                a.part_ml[pi * 2] = M;
-                a.part_ml[pi * 2 + 1] = den;
+                store_shared(part_ml + pi * 2, Mx);
+                store_shared(part_ml + pi * 2 + 1, den);
             }
         }
     }
-}
+    if (nsplit == 1) return;
 
-// ---- merge kernel: one wave per (b, query head) --------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a) {
-    constexpr int PER_LANE = (D + 63) / 64;
-    const int Hq = a.Hkv * (a.Hq / a.Hkv);
-    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (pair >= (int64_t)a.B * Hq) return;
-    const int b = (int)(pair / Hq);
-    const int L = clamp_len(a.context_lens[b], a);
-    const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
-    if (nsplit <= 1) return;  // written by the partition kernel (or nothing to attend)
-    const float* ml = a.part_ml + pair * a.S * 2;
-    float M = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    float num[PER_LANE];
+    // ---- the last partition of (b, g) to finish merges all of them
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __syncthreads();                // ... and so are every other thread's
+    int* counter = a.counters + (int64_t)b * a.Hkv + g;
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 nsplit - 1;
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = threadIdx.x; i < G * D; i += kWaves * 64) {
+        const int h = i / D;
+        const int d = i % D;
+        const int64_t p0 = ((int64_t)b * Hq + g * G + h) * a.S;
+        float Mx = -INFINITY;
+        for (int k0 = 0; k0 < nsplit; k0 += 8) {
+            float mk[8];
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) num[k] = 0.f;
-    float den = 0.f;
-    const float* pa = a.part_acc + pair * a.S * D;
-    for (int i = 0; i < nsplit; ++i) {
-        const float e = exp2f(ml[2 * i] - M_use);
-        den = fmaf(e, ml[2 * i + 1], den);
+            for (int k = 0; k < 8; ++k)
+                mk[k] = k0 + k < nsplit ? load_shared(part_ml + (p0 + k0 + k) * 2) : -INFINITY;
 #pragma unroll
-        for (int k = 0; k < PER_LANE; ++k) {
-            const int d = lane + 64 * k;
-            if (d < D) num[k] = fmaf(e, pa[(int64_t)i * D + d], num[k]);
+            for (int k = 0; k < 8; ++k) Mx = fmaxf(Mx, mk[k]);
         }
-    }
+        const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+        float num = 0.f, den = 0.f;
+        for (int k0 = 0; k0 < nsplit; k0 += 8) {
+            float mk[8], lk[8], ak[8];
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) a.out[pair * D + d] = num[k] / den;
+            for (int k = 0; k < 8; ++k) {
+                const bool ok = k0 + k < nsplit;
+                const int64_t pk = p0 + k0 + k;
+                mk[k] = ok ? load_shared(part_ml + pk * 2) : -INFINITY;
+                lk[k] = ok ? load_shared(part_ml + pk * 2 + 1) : 0.f;
+                ak[k] = ok ? load_shared(part_acc + pk * D + d) : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float e = exp2f(mk[k] - M_use);
+                den = fmaf(e, lk[k], den);
+                num = fmaf(e, ak[k], num);
+            }
+        }
+        a.out[((int64_t)b * Hq + g * G + h) * D + d] = num / den;
     }
+    if (threadIdx.x == 0)  // ready for the next call
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G, bool BF16>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-    dim3 grid((unsigned)a.S, (unsigned)a.Hkv, (unsigned)a.B);
-    hipLaunchKernelGGL((paged_decode_part_kernel<D, G, BF16>), grid, dim3(kWaves * 64), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.S <= 1) return e;
-    const int64_t pairs = (int64_t)a.B * a.Hq;
-    hipLaunchKernelGGL((paged_decode_merge_kernel<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
-                       stream, a);
+    dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)a.B);
+    hipLaunchKernelGGL((paged_decode_kernel<D, G, BF16>), grid, dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

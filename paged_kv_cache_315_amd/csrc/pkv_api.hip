@@ -63,6 +63,22 @@ int choose_split(int B, int Hkv, int max_context_len, int cus) {
     return best;
 }
 
+// Workspace of the decode call: partial sums, partial (max, sum) pairs, merge counters.
+struct WorkspaceLayout {
+    size_t acc_off, ml_off, cnt_off, total;
+};
+
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int D, int64_t S) {
+    WorkspaceLayout w{0, 0, 0, 0};
+    if (S <= 1) return w;
+    const size_t parts = (size_t)B * Hq * S;
+    w.acc_off = 0;
+    w.ml_off = parts * D * sizeof(float);
+    w.cnt_off = w.ml_off + parts * 2 * sizeof(float);
+    w.total = w.cnt_off + (size_t)B * Hkv * sizeof(int);
+    return w;
+}
+
 bool decode_shape_supported(int Hq, int Hkv, int D) {
     const int G = Hq / Hkv;
     return (D == 32 || D == 64 || D == 128 || D == 256) && G >= 1 && G <= 8;
@@ -159,8 +175,7 @@ size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int 
                                                              max_context_len);
     if (P <= 0) return 0;
     const int64_t S = ((int64_t)max_context_len + P - 1) / P;
-    if (S <= 1) return 0;
-    return (size_t)B * num_q_heads * S * (head_dim + 2) * sizeof(float);
+    return workspace_layout(B, num_q_heads, num_kv_heads, head_dim, S).total;
 }
 
 pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void* v_pool,
@@ -202,7 +217,8 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                                    : choose_split(B, num_kv_heads, max_context_len, device_cus());
     const int64_t S = ((int64_t)max_context_len + P - 1) / P;
     if (S > 0x7FFFFFFF) return fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions");
-    const size_t need = S > 1 ? (size_t)B * num_q_heads * S * (head_dim + 2) * sizeof(float) : 0;
+    const WorkspaceLayout wl = workspace_layout(B, num_q_heads, num_kv_heads, head_dim, S);
+    const size_t need = wl.total;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes, need);
 
@@ -213,8 +229,10 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
     a.tables = block_tables;
     a.context_lens = context_lens;
     a.out = out;
-    a.part_acc = static_cast<float*>(workspace);
-    a.part_ml = need ? static_cast<float*>(workspace) + (size_t)B * num_q_heads * S * head_dim : nullptr;
+    char* ws = static_cast<char*>(workspace);
+    a.part_acc = need ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
+    a.part_ml = need ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+    a.counters = need ? reinterpret_cast<int*>(ws + wl.cnt_off) : nullptr;
     a.max_blocks = max_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.scale = scale;

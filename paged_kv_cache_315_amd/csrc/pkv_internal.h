@@ -36,6 +36,7 @@ struct DecodeArgs {
     float* out;
     float* part_acc;  // [B, Hq, S, D]
     float* part_ml;   // [B, Hq, S, 2]
+    int* counters;    // [B, Hkv] finished partitions per (sequence, KV head); zero between calls
     int max_blocks;
     int max_context_len;
     float scale;
@@ -46,7 +47,7 @@ struct DecodeArgs {
     bool bf16;
 };
 
-// Launches the partition kernel and, when S > 1, the merge kernel.
+// Launches the decode kernel (partitions + in-kernel merge by the last partition).
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -79,7 +79,7 @@ def test_workspace_formula(lib):
     # S = ceil(51 / 64) = 1 -> no partials
     assert lib.pkv_decode_workspace_bytes(2, 4, 2, 64, 51, 64) == 0
     # S = ceil(4097 / 512) = 9
-    assert lib.pkv_decode_workspace_bytes(32, 32, 8, 128, 4097, 512) == 32 * 32 * 9 * 130 * 4
+    assert lib.pkv_decode_workspace_bytes(32, 32, 8, 128, 4097, 512) == 32 * 32 * 9 * 130 * 4 + 32 * 8 * 4
     assert lib.pkv_decode_workspace_bytes(0, 32, 8, 128, 4097, 512) == 0
 
 

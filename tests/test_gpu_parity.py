@@ -169,3 +169,33 @@ def test_block_ids_beyond_32bit_element_offsets():
     assert_pools_equal(kp[idx].cpu().numpy().view(np.uint16), kref, "k_pool (used blocks)")
     del kp, vp
     torch.cuda.empty_cache()
+
+
+def test_consecutive_calls_read_fresh_partials():
+    """Back-to-back decode calls with different queries on one workspace, with many partitions
+    per sequence: every call's merge must combine that call's partials (stale partials from the
+    previous call would mix the two queries)."""
+    wl = W.make_workload(45, [4000, 2500, 777, 63], 16, 2, 128, 16, "bf16", 5e5)
+    dev = upload(wl)
+    q_ref, _, kp, vp = oracle.decode_step(wl)
+    pkv.kv_append(dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"],
+                  dev["tables"], dev["positions"], theta=wl["theta"], dtype="bf16")
+    B, Hq, Hkv, D = 4, 16, 2, 128
+    ws = torch.zeros(pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["max_context_len"], 64),
+                     dtype=torch.uint8, device="cuda:0")
+    rng = np.random.default_rng(46)
+    outs, qs = [], []
+    for call in range(6):
+        q = rng.standard_normal((B, Hq, D)).astype(np.float32) * (1 + call)
+        qs.append(q)
+        outs.append(pkv.paged_attn_decode(torch.from_numpy(q).cuda(), dev["k_pool"], dev["v_pool"],
+                                          dev["tables"], dev["context_lens"], wl["max_context_len"],
+                                          wl["scale"], workspace=ws, split_tokens=64, dtype="bf16"))
+    torch.cuda.synchronize()
+    for call, (q, o) in enumerate(zip(qs, outs)):
+        ref = oracle.paged_attn_decode(q, kp, vp, wl["tables"], wl["context_lens"], wl["scale"],
+                                       "bf16")
+        assert_close(o.cpu().numpy(), ref, f"call {call}")
+    # the counters are back to zero after every call
+    tail = ws[-B * Hkv * 4:].view(torch.int32).cpu().numpy()
+    assert np.all(tail == 0), tail
