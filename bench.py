@@ -83,7 +83,7 @@ def main() -> int:
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     B, Hq, Hkv, D = wl["B"], wl["Hq"], wl["Hkv"], wl["D"]
     split = args.split_tokens
-    ws_bytes = pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["max_context_len"], split)
+    ws_bytes = pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["bs"], wl["max_context_len"], split)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(q)
     out = torch.empty_like(q)
@@ -166,7 +166,8 @@ def main() -> int:
             "context_tokens": int(wl["context_lens"].sum()),
             "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
             "qk_norm": wl["q_norm_w"] is not None, "pool_copies": copies,
-            "split_tokens": split or pkv.decode_split_tokens(B, Hq, Hkv, D, wl["max_context_len"]),
+            "split_tokens": split or pkv.decode_split_tokens(B, Hq, Hkv, D, wl["bs"],
+                                                             wl["max_context_len"]),
             "bytes_per_step": nbytes["step"], "kv_bytes": nbytes["kv"],
         },
         "roofline": {

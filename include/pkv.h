@@ -131,10 +131,11 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *              B * num_kv_heads ints count finished partitions, and every call leaves them zero
  *              again (the rest needs no initialisation). Calls that run concurrently (on
  *              different streams) need separate workspaces.
- * split_tokens tokens per partition, a positive multiple of 64, or 0 to let the library choose
- *              from the shape (pkv_decode_split_tokens)
+ * split_tokens tokens per partition, a positive multiple of 64 of at most
+ *              1022 * block_size (a partition stages its block ids in LDS), or 0 to let the
+ *              library choose from the shape (pkv_decode_split_tokens)
  * Errors: INVALID_ARG as for pkv_kv_append, plus max_context_len < 0, split_tokens not 0 or a
- *   positive multiple of 64; UNSUPPORTED for head_dim not in {32, 64, 128, 256} or a GQA group
+ *   positive multiple of 64 up to 1022 * block_size; UNSUPPORTED for head_dim not in {32, 64, 128, 256} or a GQA group
  *   num_q_heads / num_kv_heads above 8; WORKSPACE when the workspace is too small.
  *   B == 0 or max_context_len == 0 is a no-op.
  */
@@ -150,14 +151,14 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
  * only; depends on the shape and on the current device's compute-unit count. Returns 0 on
  * invalid arguments. */
 int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_dim,
-                            int max_context_len);
+                            int block_size, int max_context_len);
 
 /* Workspace bytes pkv_paged_attn_decode needs for these arguments (split_tokens as passed to
  * it, 0 = the library's choice): B * num_q_heads * S * (head_dim + 2) * 4 partial-result bytes
  * plus B * num_kv_heads * 4 counter bytes, with S = ceil(max_context_len / split_tokens)
  * partitions, or 0 when S <= 1. Host only. */
 size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
-                                  int max_context_len, int split_tokens);
+                                  int block_size, int max_context_len, int split_tokens);
 
 /* Debug check of the device-array preconditions on HOST copies of the arrays (any may be
  * NULL to skip it): every block id a sequence uses is in [0, num_blocks); positions[b] in

@@ -93,12 +93,14 @@ def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, thet
     return q_out
 
 
-def decode_split_tokens(B, Hq, Hkv, D, max_context_len) -> int:
-    return _lib.load().pkv_decode_split_tokens(B, Hq, Hkv, D, max_context_len)
+def decode_split_tokens(B, Hq, Hkv, D, block_size, max_context_len) -> int:
+    return _lib.load().pkv_decode_split_tokens(B, Hq, Hkv, D, block_size, max_context_len)
 
 
-def decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens: int = 0) -> int:
-    return _lib.load().pkv_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens)
+def decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_context_len,
+                           split_tokens: int = 0) -> int:
+    return _lib.load().pkv_decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_context_len,
+                                                  split_tokens)
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
@@ -114,7 +116,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
     NB, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if out is None:
         out = torch.empty_like(q)
-    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, split_tokens) if B else 0
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, split_tokens) if B else 0
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None

@@ -15,7 +15,8 @@
 //   the G query heads of KV head g, so every K/V row is read from HBM once per step. The KV
 //   head is the fastest grid index: the Hkv workgroups of one (b, s) run side by side and
 //   together stream whole [bs, Hkv, D] blocks. The 4 waves of a workgroup take interleaved
-//   16-token tiles and prefetch the next tile's K and V rows while computing the current one.
+//   16-token tiles; each wave keeps the K and V rows of its next two tiles (one for G > 4) in
+//   flight while it computes the current one.
 //
 // Per 16-token tile and wave:
 //   QK^T on the matrix cores: S[h][t] = sum_d Q[h][d] K[t][d] as D/32 MFMA 16x16x32 steps with
@@ -52,7 +53,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kWaves = 4;
 constexpr int kTile = 16;       // tokens per wave per iteration
-constexpr int kTblCap = 512;    // block ids staged in LDS per workgroup
+constexpr int kTblCap = 1024;   // block ids staged in LDS per workgroup (bounds split_tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool BF16>
@@ -154,6 +155,13 @@ __device__ __forceinline__ BlockDiv make_div(uint32_t d) {
     return r;
 }
 
+// 16-byte load of streamed K/V codes, marked non-temporal: every row is read once per call.
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Device-coherent accesses to the partition partials (see the merge at the end of the kernel).
 __device__ __forceinline__ void store_shared(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -205,18 +213,15 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
     const int nsplit = (L + P - 1) / P;
     const int Hq = a.Hkv * G;
 
-    // ---- block ids of this partition -> LDS
+    // ---- block ids of this partition -> LDS (the host keeps split_tokens within kTblCap ids)
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
     const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
     const int first_blk = (int)bdiv.div((uint32_t)t_begin);
-    const int n_blk = (int)bdiv.div((uint32_t)(t_end - 1)) - first_blk + 1;
-    const bool tbl_in_lds = n_blk <= kTblCap;
+    const int n_blk = min((int)bdiv.div((uint32_t)(t_end - 1)) - first_blk + 1, kTblCap);
     const int64_t nb_max = a.num_blocks - 1;
-    if (tbl_in_lds) {
-        for (int i = threadIdx.x; i < n_blk; i += kWaves * 64) {
-            const int64_t id = trow[first_blk + i];
-            s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
-        }
+    for (int i = threadIdx.x; i < n_blk; i += kWaves * 64) {
+        const int64_t id = trow[first_blk + i];
+        s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
     }
 
     // ---- Q operand: row l16 = head (zero beyond G), k-slice q4, pre-scaled, hi + remainder
@@ -270,33 +275,22 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 
     const int64_t tok_stride = (int64_t)a.Hkv * D;   // codes between consecutive slots
     const int64_t head_off = (int64_t)g * D;
+    // Loads are issued unconditionally (tokens past the partition end are clamped to its last
+    // token and masked where they are used): a load behind a branch makes the compiler wait for
+    // every outstanding load before it, which would drain the prefetch pipeline.
     auto row_off = [&](int t) -> int64_t {
         const int j = (int)bdiv.div((uint32_t)t);
-        int64_t blk;
-        if (tbl_in_lds) {
-            blk = s_tbl[j - first_blk];
-        } else {
-            const int64_t id = trow[j];
-            blk = id < 0 ? 0 : (id > nb_max ? nb_max : id);
-        }
+        const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
         return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
     };
     auto load_tile = [&](int base, uint4 (&kr)[NK], uint4 (&vr)[U]) {
-        const int tk = base + l16;
-        if (tk < t_end) {
-            const uint16_t* kp = a.k_pool + row_off(tk) + 8 * q4;
+        const uint16_t* kp = a.k_pool + row_off(min(base + l16, t_end - 1)) + 8 * q4;
 #pragma unroll
-            for (int i = 0; i < NK; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 32 * i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NK; ++i) kr[i] = make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < NK; ++i) kr[i] = load_stream(kp + 32 * i);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tv = base + u * TPL + vrow;
-            vr[u] = tv < t_end
-                        ? *reinterpret_cast<const uint4*>(a.v_pool + row_off(tv) + 8 * vcol)
-                        : make_uint4(0, 0, 0, 0);
+            const int tv = min(base + u * TPL + vrow, t_end - 1);
+            vr[u] = load_stream(a.v_pool + row_off(tv) + 8 * vcol);
         }
     };
 
@@ -311,15 +305,8 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
 
-    int base = t_begin + wave * kTile;
-    uint4 kc[NK], vc[U];
-    if (base < t_end) load_tile(base, kc, vc);
-    for (; base < t_end; base += kWaves * kTile) {
-        const int nbase = base + kWaves * kTile;
-        uint4 kn[NK], vn[U];
-        if (nbase < t_end) load_tile(nbase, kn, vn);
-
-        // scores S[head 4*q4 + r][token l16]
+    // one 16-token tile: scores on the matrix cores, online softmax, P through LDS, PV on VALU
+    auto compute_tile = [&](int base, const uint4 (&kc)[NK], const uint4 (&vc)[U]) {
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
@@ -363,19 +350,52 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
             float pv[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) pv[h] = s_p[wave][tt][h];
+            const bool v_ok = base + tt < t_end;   // rows past the end were clamped: drop them
+            const uint4 raw = v_ok ? vc[u] : make_uint4(0, 0, 0, 0);
             float vf[8];
-            decode8<BF16>(vc[u], vf);
+            decode8<BF16>(raw, vf);
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pv[h], vf[j], acc[h][j]);
         }
         wave_lds_sync();
-        if (nbase < t_end) {
-#pragma unroll
-            for (int i = 0; i < NK; ++i) kc[i] = kn[i];
-#pragma unroll
-            for (int u = 0; u < U; ++u) vc[u] = vn[u];
+    };
+
+    // Register buffers for tiles in flight, loop unrolled so each buffer keeps its registers
+    // (no copies between iterations): three buffers (two tiles ahead of the compute) while the
+    // accumulators are small (G <= 4), two buffers (one ahead) otherwise to stay at two waves
+    // per SIMD.
+    constexpr int kStride = kWaves * kTile;
+    int base = t_begin + wave * kTile;
+    if constexpr (G <= 4) {
+        uint4 ka[NK], va[U], kb[NK], vb[U], kcb[NK], vcb[U];
+        load_tile(base, ka, va);
+        load_tile(base + kStride, kb, vb);
+        while (base < t_end) {
+            load_tile(base + 2 * kStride, kcb, vcb);
+            compute_tile(base, ka, va);
+            base += kStride;
+            if (base >= t_end) break;
+            load_tile(base + 2 * kStride, ka, va);
+            compute_tile(base, kb, vb);
+            base += kStride;
+            if (base >= t_end) break;
+            load_tile(base + 2 * kStride, kb, vb);
+            compute_tile(base, kcb, vcb);
+            base += kStride;
+        }
+    } else {
+        uint4 ka[NK], va[U], kb[NK], vb[U];
+        load_tile(base, ka, va);
+        while (base < t_end) {
+            load_tile(base + kStride, kb, vb);
+            compute_tile(base, ka, va);
+            base += kStride;
+            if (base >= t_end) break;
+            load_tile(base + kStride, ka, va);
+            compute_tile(base, kb, vb);
+            base += kStride;
         }
     }
 

@@ -28,6 +28,11 @@ bool valid_dtype(pkv_dtype d) { return d == PKV_F16 || d == PKV_BF16; }
 
 constexpr int kMaxGridDim = 65535;  // y / z grid limit used for Hkv and B
 constexpr int kDefaultCUs = 256;
+constexpr int kTblCap = 1024;  // block ids one decode workgroup stages (paged_decode.hip)
+
+// Largest split_tokens whose partition spans at most kTblCap blocks (a partition starts at a
+// multiple of 64 tokens, so it can straddle one extra block).
+int64_t max_split_for(int block_size) { return (int64_t)(kTblCap - 2) * block_size; }
 
 // Compute units of the current device, cached per device id.
 int device_cus() {
@@ -50,10 +55,11 @@ int device_cus() {
 // Tokens per partition: the largest multiple of 64 in [256, 4096] that still gives about
 // eight workgroups per compute unit over the whole batch (B * Hkv * ceil(Lmax / P) >= 8 * CUs),
 // so short batches split finely and long ones keep the partials small.
-int choose_split(int B, int Hkv, int max_context_len, int cus) {
+int choose_split(int B, int Hkv, int max_context_len, int block_size, int cus) {
     const int64_t target = 8LL * cus;
-    int best = 256;
-    for (int p = 4096; p >= 256; p -= 64) {
+    const int cap = (int)std::min<int64_t>(4096, max_split_for(block_size) / 64 * 64);
+    int best = std::min(256, cap);
+    for (int p = cap; p >= 256; p -= 64) {
         const int64_t items = (int64_t)B * Hkv * ((max_context_len + p - 1) / p);
         if (items >= target) {
             best = p;
@@ -159,20 +165,22 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
 }
 
 int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_dim,
-                            int max_context_len) {
-    if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+                            int block_size, int max_context_len) {
+    if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_context_len <= 0)
         return 0;
     (void)num_q_heads;
-    return choose_split(B, num_kv_heads, max_context_len, device_cus());
+    return choose_split(B, num_kv_heads, max_context_len, block_size, device_cus());
 }
 
 size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
-                                  int max_context_len, int split_tokens) {
-    if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+                                  int block_size, int max_context_len, int split_tokens) {
+    if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_context_len <= 0)
         return 0;
     const int P = split_tokens > 0 ? split_tokens
                                    : pkv_decode_split_tokens(B, num_q_heads, num_kv_heads, head_dim,
-                                                             max_context_len);
+                                                             block_size, max_context_len);
     if (P <= 0) return 0;
     const int64_t S = ((int64_t)max_context_len + P - 1) / P;
     return workspace_layout(B, num_q_heads, num_kv_heads, head_dim, S).total;
@@ -199,9 +207,11 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
         return fail(PKV_ERR_INVALID_ARG, "decode: Hq=%d not a multiple of Hkv=%d", num_q_heads,
                     num_kv_heads);
     if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "decode: unknown dtype %d", (int)dtype);
-    if (split_tokens < 0 || split_tokens % 64)
-        return fail(PKV_ERR_INVALID_ARG, "decode: split_tokens=%d must be 0 or a positive multiple of 64",
-                    split_tokens);
+    if (split_tokens < 0 || split_tokens % 64 || split_tokens > max_split_for(block_size))
+        return fail(PKV_ERR_INVALID_ARG,
+                    "decode: split_tokens=%d must be 0 or a positive multiple of 64 of at most "
+                    "%lld (= %d block ids per partition)",
+                    split_tokens, (long long)max_split_for(block_size), kTblCap - 2);
     if (!decode_shape_supported(num_q_heads, num_kv_heads, head_dim))
         return fail(PKV_ERR_UNSUPPORTED,
                     "decode: head_dim=%d (need 32/64/128/256) or GQA group %d (need 1..8) not built",
@@ -213,8 +223,9 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
         return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer argument");
 
-    const int P = split_tokens > 0 ? split_tokens
-                                   : choose_split(B, num_kv_heads, max_context_len, device_cus());
+    const int P = split_tokens > 0
+                      ? split_tokens
+                      : choose_split(B, num_kv_heads, max_context_len, block_size, device_cus());
     const int64_t S = ((int64_t)max_context_len + P - 1) / P;
     if (S > 0x7FFFFFFF) return fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions");
     const WorkspaceLayout wl = workspace_layout(B, num_q_heads, num_kv_heads, head_dim, S);

@@ -70,6 +70,7 @@ def test_append_argument_checks(lib, kw, status):
     (dict(split=-64), 1), (dict(D=96), 2), (dict(Hq=32, Hkv=2), 2), (dict(dt=0), 1),
     (dict(out=None), 1), (dict(ws=None, wsb=0), 3), (dict(ws=FAKE, wsb=10), 3),
     (dict(B=0), 0), (dict(mcl=0), 0), (dict(B=70000), 2),
+    (dict(split=1024, bs=1), 1),                      # 1024 > 1022 * block_size
 ])
 def test_decode_argument_checks(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -77,10 +78,11 @@ def test_decode_argument_checks(lib, kw, status):
 
 def test_workspace_formula(lib):
     # S = ceil(51 / 64) = 1 -> no partials
-    assert lib.pkv_decode_workspace_bytes(2, 4, 2, 64, 51, 64) == 0
+    assert lib.pkv_decode_workspace_bytes(2, 4, 2, 64, 16, 51, 64) == 0
     # S = ceil(4097 / 512) = 9
-    assert lib.pkv_decode_workspace_bytes(32, 32, 8, 128, 4097, 512) == 32 * 32 * 9 * 130 * 4 + 32 * 8 * 4
-    assert lib.pkv_decode_workspace_bytes(0, 32, 8, 128, 4097, 512) == 0
+    assert lib.pkv_decode_workspace_bytes(32, 32, 8, 128, 16, 4097, 512) == \
+        32 * 32 * 9 * 130 * 4 + 32 * 8 * 4
+    assert lib.pkv_decode_workspace_bytes(0, 32, 8, 128, 16, 4097, 512) == 0
 
 
 def test_validate_tables():

@@ -181,7 +181,7 @@ def test_consecutive_calls_read_fresh_partials():
     pkv.kv_append(dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"],
                   dev["tables"], dev["positions"], theta=wl["theta"], dtype="bf16")
     B, Hq, Hkv, D = 4, 16, 2, 128
-    ws = torch.zeros(pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["max_context_len"], 64),
+    ws = torch.zeros(pkv.decode_workspace_bytes(B, Hq, Hkv, D, 16, wl["max_context_len"], 64),
                      dtype=torch.uint8, device="cuda:0")
     rng = np.random.default_rng(46)
     outs, qs = [], []
