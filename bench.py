@@ -2,16 +2,17 @@
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--copies R] [--no-cpu-baseline]
 
-A step is one pass of the whole path over one batch: pkv_kv_append then
-pkv_paged_attn_decode, on the Llama-3-8B-shaped workload by default (32 sequences, cached
+A step is one pass of the whole path over one batch: pkv_decode_step (the append of every
+sequence's new token and the paged-attention decode, in one kernel launch), on the
+Llama-3-8B-shaped workload by default (32 sequences, cached
 lengths U{512..4096}, 32 query / 8 KV heads, head_dim 128, block_size 16, bf16 pool,
 RoPE theta 5e5). Inputs are seeded synthetic data resident in HBM before timing starts.
 The pools exist in R identical copies and step i uses copy i % R, so the K/V stream of one
 step is not still in the 256 MB last-level cache from the previous step.
 
-Prints ONE JSON line. `value` is the step's algorithmic bytes over the step time (GB/s);
-`roofline` is the paged-decode kernel alone, timed with HIP events
-on its stream; `cpu_baseline` is the single-threaded CPU oracle on one full step of the same
+Prints ONE JSON line. `value` is the step's algorithmic bytes over the step time (GB/s); the
+step is one kernel launch, so `roofline` reports that kernel (HIP events on its stream around
+the timed steps); `decode_only` times pkv_paged_attn_decode alone on the same inputs; `cpu_baseline` is the single-threaded CPU oracle on one full step of the same
 workload.
 """
 from __future__ import annotations
@@ -83,7 +84,8 @@ def main() -> int:
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     B, Hq, Hkv, D = wl["B"], wl["Hq"], wl["Hkv"], wl["D"]
     split = args.split_tokens
-    ws_bytes = pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["bs"], wl["max_context_len"], split)
+    ws_bytes = max(pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["bs"], wl["max_context_len"], split),
+                   pkv.decode_step_workspace_bytes(B, Hq, Hkv, D, wl["bs"], wl["max_blocks"]))
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(q)
     out = torch.empty_like(q)
@@ -91,12 +93,9 @@ def main() -> int:
 
     def step(i):
         kp, vp = pools[i % copies]
-        pkv.kv_append(q, k_new, v_new, kp, vp, tables, positions, theta=wl["theta"],
-                      q_norm_w=qn, k_norm_w=kn, eps=wl["eps"], q_out=q_out, dtype=wl["dtype"],
-                      stream=stream)
-        pkv.paged_attn_decode(q_out, kp, vp, tables, ctx, wl["max_context_len"], wl["scale"],
-                              out=out, workspace=ws, split_tokens=split, dtype=wl["dtype"],
-                              stream=stream)
+        pkv.decode_step(q, k_new, v_new, kp, vp, tables, positions, theta=wl["theta"],
+                        scale=wl["scale"], q_norm_w=qn, k_norm_w=kn, eps=wl["eps"], q_out=q_out,
+                        out=out, workspace=ws, dtype=wl["dtype"], stream=stream)
 
     def decode_only(i):
         kp, vp = pools[i % copies]
@@ -130,7 +129,6 @@ def main() -> int:
     decode_ms = e0.elapsed_time(e1) / args.steps
 
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    decode_gbs = nbytes["decode"] / (decode_ms * 1e-3) / 1e9
     tokens_per_s = B / (ms_per_step * 1e-3)
 
     cpu = None
@@ -170,12 +168,15 @@ def main() -> int:
                                                              wl["max_context_len"]),
             "bytes_per_step": nbytes["step"], "kv_bytes": nbytes["kv"],
         },
+        # the step is one launch of the fused kernel, so the step time is its launch time
         "roofline": {
-            "bound": "hbm", "kernel": "paged_decode_kernel",
-            "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(decode_ms * 1e3, 3),
+            "bound": "hbm", "kernel": "decode_balanced_kernel (append fused, pkv_decode_step)",
+            "achieved": round(step_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": nbytes["step"], "avg_launch_us": round(ms_per_step * 1e3, 3),
         },
+        "decode_only": {"kernel": "pkv_paged_attn_decode", "avg_launch_us": round(decode_ms * 1e3, 3),
+                        "gb_per_s": round(nbytes["decode"] / (decode_ms * 1e-3) / 1e9, 2)},
         "cpu_baseline": cpu,
         "wall_ms_timed_steps": round(wall_ms, 2),
     }

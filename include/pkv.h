@@ -114,9 +114,12 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *   out[b][h] = sum_t exp(s_t - max s) V[t][g] / sum_t exp(s_t - max s).
  * Arithmetic is float (fp16/bf16 codes decode exactly; q . k runs on the matrix cores with q
  * split into a 16-bit high part and a 16-bit remainder, accurate to about 2^-16 relative);
- * the token axis is cut into partitions of split_tokens tokens, each partition keeps a
- * running max / sum / weighted V (online softmax), and the last partition of each
- * (sequence, KV head) to finish merges them with their max-rescaled weights.
+ * each piece of the token axis keeps a running max / sum / weighted V (online softmax), and the
+ * last piece of each (sequence, KV head) to finish merges the pieces with their max-rescaled
+ * weights. With split_tokens == 0 (and B <= 2048) the pieces come from a balanced schedule:
+ * the K/V tiles of the whole batch are cut into equal contiguous ranges, one per resident
+ * workgroup. With split_tokens > 0 every sequence is cut into partitions of split_tokens
+ * tokens, one workgroup each.
  *
  * q            (device) float [B, num_q_heads, head_dim] (q_out of pkv_kv_append)
  * k_pool, v_pool (device) 16-bit codes, layout above; read only
@@ -131,9 +134,8 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *              B * num_kv_heads ints count finished partitions, and every call leaves them zero
  *              again (the rest needs no initialisation). Calls that run concurrently (on
  *              different streams) need separate workspaces.
- * split_tokens tokens per partition, a positive multiple of 64 of at most
- *              1022 * block_size (a partition stages its block ids in LDS), or 0 to let the
- *              library choose from the shape (pkv_decode_split_tokens)
+ * split_tokens 0 for the balanced schedule, or tokens per partition: a positive multiple of
+ *              64 of at most 1022 * block_size (a partition stages its block ids in LDS)
  * Errors: INVALID_ARG as for pkv_kv_append, plus max_context_len < 0, split_tokens not 0 or a
  *   positive multiple of 64 up to 1022 * block_size; UNSUPPORTED for head_dim not in {32, 64, 128, 256} or a GQA group
  *   num_q_heads / num_kv_heads above 8; WORKSPACE when the workspace is too small.
@@ -147,16 +149,51 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                                  int head_dim, int block_size, int64_t num_blocks,
                                  pkv_dtype dtype, void* stream);
 
-/* Tokens per split-K partition that pkv_paged_attn_decode uses for split_tokens == 0. Host
- * only; depends on the shape and on the current device's compute-unit count. Returns 0 on
- * invalid arguments. */
+/*
+ * pkv_decode_step — pkv_kv_append followed by pkv_paged_attn_decode, in one kernel launch.
+ *
+ * For each sequence b with p = positions[b]: the new token is appended exactly as
+ * pkv_kv_append does (stored bits identical), q_out[b] receives the rotated query, and
+ * out[b] = attention of q_out[b] over the L = p + 1 tokens now in the cache, exactly as
+ * pkv_paged_attn_decode with context_lens[b] = p + 1 computes it.
+ *
+ * Schedule: the K/V tiles of the whole batch are cut into equal contiguous ranges, one per
+ * resident workgroup; each workgroup rotates the query heads it needs itself, and the one that
+ * holds a sequence's last tile writes that KV head's new row before streaming it. Batches above
+ * 2048 sequences run the append kernel and the partitioned decode instead.
+ *
+ * Arguments as for pkv_kv_append and pkv_paged_attn_decode; q_out must not alias q_in.
+ * workspace: at least pkv_decode_step_workspace_bytes(...) bytes, zero-filled before first use
+ * (counters the call leaves zero again). A sequence whose position is outside
+ * [0, max_blocks_per_seq * block_size) is skipped (its q_out and out rows are not written).
+ * Errors: the union of those of pkv_kv_append and pkv_paged_attn_decode; INVALID_ARG when
+ * q_out == q_in.
+ */
+pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                           void* k_pool, void* v_pool, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* positions,
+                           const float* q_norm_w, const float* k_norm_w, float rms_eps,
+                           float rope_theta, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, int B, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
+                           void* stream);
+
+/* Workspace bytes pkv_decode_step needs. Host only. */
+size_t pkv_decode_step_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq);
+
+/* Tokens per partition of the partitioned schedule when pkv_paged_attn_decode has to choose
+ * one itself (split_tokens == 0 with more than 2048 sequences). Host only; depends on the shape
+ * and on the current device's compute-unit count. Returns 0 on invalid arguments. */
 int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_dim,
                             int block_size, int max_context_len);
 
 /* Workspace bytes pkv_paged_attn_decode needs for these arguments (split_tokens as passed to
- * it, 0 = the library's choice): B * num_q_heads * S * (head_dim + 2) * 4 partial-result bytes
- * plus B * num_kv_heads * 4 counter bytes, with S = ceil(max_context_len / split_tokens)
- * partitions, or 0 when S <= 1. Host only. */
+ * it). Layout: B * num_kv_heads int counters (rounded up to 256 bytes), then the partial
+ * results: for the balanced schedule 4096 pieces of G * (head_dim + 2) floats
+ * (G = num_q_heads / num_kv_heads); for the partitioned one B * num_q_heads * S * (head_dim + 2)
+ * floats with S = ceil(max_context_len / split_tokens), or nothing at all when S <= 1. Each
+ * part is rounded up to 256 bytes. Host only. */
 size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
                                   int block_size, int max_context_len, int split_tokens);
 

@@ -7,7 +7,7 @@ on the GPU, passes their pointers to libpkv and enqueues the kernels on the curr
     kv_append(...)          new token per sequence: QK-norm (optional), RoPE, fp16/bf16
                             round-to-nearest-even, scatter into the block pools
     paged_attn_decode(...)  softmax(scale q.K^T).V over each sequence's block list (GQA)
-    decode_step(...)        both, as one decoder layer's attention step
+    decode_step(...)        both, as one decoder layer's attention step (one kernel launch)
 """
 from __future__ import annotations
 
@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import PKV_BF16, PKV_F16, PkvError
 
 __all__ = ["kv_append", "paged_attn_decode", "decode_step", "decode_workspace_bytes",
-           "decode_split_tokens", "validate_tables", "version", "PkvError", "pool_dtype_code"]
+           "decode_step_workspace_bytes", "append_then_decode", "decode_split_tokens", "validate_tables", "version",
+           "PkvError", "pool_dtype_code"]
 
 
 def _torch():
@@ -133,12 +134,52 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
     return out
 
 
-def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, context_lens,
-                max_context_len: int, *, theta: float, scale: float, q_norm_w=None,
-                k_norm_w=None, eps: float = 1e-6, q_out=None, out=None, workspace=None,
-                split_tokens: int = 0, dtype=None, stream=None):
-    """One layer's decode step: kv_append then paged_attn_decode on the same stream.
-    Returns (q_out, out)."""
+def decode_step_workspace_bytes(B, Hq, Hkv, D, block_size, max_blocks_per_seq) -> int:
+    return _lib.load().pkv_decode_step_workspace_bytes(B, Hq, Hkv, D, block_size,
+                                                       max_blocks_per_seq)
+
+
+def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, theta: float,
+                scale: float, q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None,
+                out=None, workspace=None, dtype=None, stream=None):
+    """One layer's decode step in one launch: append the new token of every sequence, then
+    attend over positions + 1 tokens. Returns (q_out, out), both [B, Hq, D] float32.
+
+    workspace: uint8 GPU tensor of >= decode_step_workspace_bytes(...) bytes, zero-filled before
+    its first use; allocated here (zeroed) if None.
+    """
+    torch = _torch()
+    B, Hq, D = q_in.shape
+    Hkv = k_in.shape[1]
+    NB, bs = k_pool.shape[0], k_pool.shape[1]
+    if q_out is None:
+        q_out = torch.empty_like(q_in)
+    if out is None:
+        out = torch.empty_like(q_in)
+    need = decode_step_workspace_bytes(B, Hq, Hkv, D, bs, block_tables.shape[1]) if B else 0
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q_in.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    f32 = torch.float32
+    args = (
+        _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
+        _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2), _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
+        _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
+        _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
+        float(eps), float(theta), float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3),
+        ws_ptr, ws_bytes, B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype), _stream(stream))
+    _lib.check(_lib.load().pkv_decode_step(*args), "pkv_decode_step")
+    return q_out, out
+
+
+def append_then_decode(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, context_lens,
+                       max_context_len: int, *, theta: float, scale: float, q_norm_w=None,
+                       k_norm_w=None, eps: float = 1e-6, q_out=None, out=None, workspace=None,
+                       split_tokens: int = 0, dtype=None, stream=None):
+    """The same step as two calls (kv_append, then paged_attn_decode). Returns (q_out, out)."""
     q_out = kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, theta=theta,
                       q_norm_w=q_norm_w, k_norm_w=k_norm_w, eps=eps, q_out=q_out, dtype=dtype,
                       stream=stream)

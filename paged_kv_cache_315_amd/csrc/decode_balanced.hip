@@ -1,0 +1,551 @@
+// decode_balanced.hip — paged-attention decode with a balanced schedule over the whole batch,
+// optionally fused with the new-token append (gfx950).
+//
+// What it computes is the decode of paged_decode.hip (and, fused, the append of kv_append.hip):
+//   out[b][h] = softmax_t(scale * q[b][h] . K[t][g]) . V[t][g], g = h / G, t < L_b,
+// with K/V read through the block table of each sequence
+//   (page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlockBatch;
+//    page "soft3/glia/run/arch/decoder/forward.rs", forward_layer CPU attention path;
+//    page "makarna/pkg/kvcache/paged_cache.go", GetBlockForPosition / GetBlockOffset / Append).
+//
+// Schedule. The K/V rows of the batch form one list of 16-token tiles: segment (b, g) holds the
+// ceil(L_b / 16) tiles of KV head g of sequence b, segments in (b, g) order. The grid has one
+// workgroup per resident slot (normally two per compute unit) and workgroup w takes tiles
+// [w*T, (w+1)*T), T = ceil(total / grid): every workgroup streams the same number of bytes
+// whatever the mix of lengths, and all of them are resident from start to end. Inside a
+// workgroup the 4 waves interleave the 16-token tiles of each unit (the part of one segment
+// that falls in the range) exactly as the partitioned kernel does: QK^T on the matrix cores,
+// online softmax, P through LDS, PV on the vector ALU, the next tile's K/V loads in flight.
+//
+// Pieces. A segment that lies inside one range is finished there (out = acc / l). A segment cut
+// by range boundaries leaves one piece (m, l, acc) per workgroup it touches; a workgroup holds at
+// most two such pieces (its first and its last segment), in slots 2w and 2w+1 of the workspace.
+// The last workgroup to finish a segment (an agent-scope atomic counter per segment, reset after
+// use) merges its pieces:  M = max m_i, out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+//
+// Fused append (APPEND): L_b = positions[b] + 1. Every unit rotates the query heads of its
+// segment itself (norm + RoPE in double, like kv_append.hip; cos/sin computed once per unit and
+// shared by its heads), the unit holding the segment's first tile writes q_out, and the unit
+// holding its last tile (the new token p = L_b - 1) rotates and converts the new K row, converts
+// the V row and stores both into the pool row (tables[b][p / bs], p % bs) before it streams its
+// tiles; a workgroup barrier (release / acquire at workgroup scope) orders those stores before
+// its own loads of the row. No other workgroup reads that row, so one launch does the step.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+using namespace dev;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTile = 16;
+constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
+constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
+
+// Query rotation of one unit and, for the unit holding a segment's last tile, the new token's
+// K/V row (norm + RoPE in double, round-to-nearest-even codes; see kv_append.hip), stored into
+// the pool before the unit streams its tiles. Expects s_q to hold the raw query heads (written
+// by this thread block, not yet synchronised); ends with a barrier, after which this
+// workgroup's own loads of the new row see the stored codes.
+template <int D, int G, bool BF16>
+__device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, int g, int pnew,
+                                               bool owns_new, bool seg_first, float* s_q,
+                                               float* s_kx, double* s_cs, double* s_r) {
+    constexpr int HALF = D / 2;
+    const int tid = threadIdx.x;
+    const int Hkv = a.Hkv;
+    const int Hq = Hkv * G;
+    const int64_t tok_stride = (int64_t)Hkv * D;
+    const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
+    if (owns_new)
+        for (int i = tid; i < D; i += kThreads) s_kx[i] = ksrc[i];
+    for (int i = tid; i < HALF; i += kThreads)
+        rope_cs(pnew, a.theta, i, D, s_cs[2 * i], s_cs[2 * i + 1]);
+    __syncthreads();
+    const bool norm = a.q_norm_w != nullptr;
+    if (norm) {
+        if (tid < G) s_r[tid] = rms_inv(s_q + tid * D, D, a.eps);
+        if (tid == G && owns_new) s_r[G] = rms_inv(s_kx, D, a.eps);
+        __syncthreads();
+    }
+    float* qo = a.q_out + ((int64_t)b * Hq + g * G) * D;
+    for (int idx = tid; idx < G * HALF; idx += kThreads) {
+        const int h = idx / HALF;
+        const int i = idx % HALF;
+        float x0 = s_q[h * D + i], x1 = s_q[h * D + i + HALF];
+        if (norm) {
+            x0 = norm_elem(x0, s_r[h], a.q_norm_w[i]);
+            x1 = norm_elem(x1, s_r[h], a.q_norm_w[i + HALF]);
+        }
+        float y0, y1;
+        rope_rotate(x0, x1, s_cs[2 * i], s_cs[2 * i + 1], y0, y1);
+        s_q[h * D + i] = y0;
+        s_q[h * D + i + HALF] = y1;
+        if (seg_first) {
+            qo[h * D + i] = y0;
+            qo[h * D + i + HALF] = y1;
+        }
+    }
+    if (owns_new) {
+        int64_t row = -1;
+        const int64_t blk = a.tables[(int64_t)b * a.max_blocks + pnew / a.bs];
+        if (blk >= 0 && blk < a.num_blocks)
+            row = (blk * a.bs + pnew % a.bs) * tok_stride + (int64_t)g * D;
+        for (int i = tid; i < HALF; i += kThreads) {
+            float x0 = s_kx[i], x1 = s_kx[i + HALF];
+            if (norm) {
+                x0 = norm_elem(x0, s_r[G], a.k_norm_w[i]);
+                x1 = norm_elem(x1, s_r[G], a.k_norm_w[i + HALF]);
+            }
+            float y0, y1;
+            rope_rotate(x0, x1, s_cs[2 * i], s_cs[2 * i + 1], y0, y1);
+            if (row >= 0) {
+                a.k_pool[row + i] = encode16(y0, BF16);
+                a.k_pool[row + i + HALF] = encode16(y1, BF16);
+            }
+        }
+        const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
+        if (row >= 0)
+            for (int i = tid; i < D; i += kThreads) a.v_pool[row + i] = encode16(vsrc[i], BF16);
+    }
+    __syncthreads();
+}
+
+template <int D, int G, bool BF16, bool APPEND>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void decode_balanced_kernel(BalancedArgs a) {
+    using M = Mma<BF16>;
+    constexpr int NK = D / 32;          // MFMA k-steps (and K loads) per tile
+    constexpr int R = D / 8;            // lanes per V row (8 codes per lane)
+    constexpr int TPL = 64 / R;         // V rows per load instruction
+    constexpr int U = kTile / TPL;      // V loads per tile
+    constexpr int HALF = D / 2;
+    static_assert(D % 32 == 0 && U * TPL == kTile, "tile shape");
+    static_assert(G >= 1 && G <= 8, "GQA group");
+
+    __shared__ int s_len[kMaxBalancedBatch];
+    __shared__ int s_pre[kMaxBalancedBatch + 1];
+    __shared__ int s_scan[kThreads];
+    __shared__ int32_t s_tbl[kTblCap];
+    __shared__ __align__(16) float s_q[G][D];
+    __shared__ float s_kx[APPEND ? D : 1];
+    __shared__ double s_cs[APPEND ? HALF : 1][2];
+    __shared__ double s_r[G + 1];
+    __shared__ __align__(16) float s_p[kWaves][kTile][16];
+    __shared__ __align__(16) float s_alpha[kWaves][16];
+    __shared__ float s_acc[kWaves][G][D];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l16 = lane & 15;          // token of the score layout / row of the Q operand
+    const int q4 = lane >> 4;           // lane group: k-slice of the operands, head quad of S
+    const int vrow = lane / R;          // V layout: token row within a load
+    const int vcol = lane % R;          //           8-dim column
+    const int B = a.B;
+    const int Hkv = a.Hkv;
+    const int Hq = Hkv * G;
+
+    // ---- 1. lengths and the tile prefix of every sequence (all heads) -> LDS
+    const int64_t cap64 = (int64_t)a.max_blocks * a.bs;
+    const int cap = (int)min(cap64, (int64_t)(APPEND ? 0x7FFFFFFF : a.max_context_len));
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int b = tid * kPerThread + k;
+        if (b < B) {
+            int L;
+            if constexpr (APPEND) {
+                const int p = a.lens[b];  // positions: out-of-range sequences get no work
+                L = (p >= 0 && p < cap) ? p + 1 : 0;
+            } else {
+                L = max(0, min(a.lens[b], cap));
+            }
+            s_len[b] = L;
+            cnt += (L + kTile - 1) / kTile;
+        }
+    }
+    s_scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    {
+        int run = (s_scan[tid] - cnt) * Hkv;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int b = tid * kPerThread + k;
+            if (b < B) {
+                s_pre[b] = run;
+                run += Hkv * ((s_len[b] + kTile - 1) / kTile);
+            }
+        }
+        if (tid == kThreads - 1) s_pre[B] = s_scan[tid] * Hkv;
+    }
+    __syncthreads();
+
+    // ---- 2. this workgroup's tile range
+    const int total = s_pre[B];
+    const int T = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int r0 = (int)min((int64_t)blockIdx.x * T, (int64_t)total);
+    const int r1 = min(total, r0 + T);
+    if (r0 >= r1) return;  // whole workgroup together
+
+    int b;
+    {  // last sequence whose prefix is <= r0 (its segment list contains tile r0)
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= r0) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    }
+    int g = (r0 - s_pre[b]) / ((s_len[b] + kTile - 1) / kTile);
+
+    const BlockDiv bdiv = make_div((uint32_t)a.bs);
+    const int64_t nb_max = a.num_blocks - 1;
+    const int64_t tok_stride = (int64_t)Hkv * D;   // codes between consecutive slots
+    const int chunk_tokens = ((kTblCap - 2) * a.bs) / 64 * 64;
+    float* part_acc = a.part_acc;
+    float* part_ml = a.part_ml;
+
+    for (int x = r0; x < r1;) {
+        // ---- one unit: tiles [x, u_end) of segment (b, g)
+        const int L = s_len[b];
+        const int nb = (L + kTile - 1) / kTile;
+        const int seg_start = s_pre[b] + g * nb;
+        const int seg_end = seg_start + nb;
+        const int u_end = min(seg_end, r1);
+        const int tok_lo = (x - seg_start) * kTile;
+        const int tok_hi = min((u_end - seg_start) * kTile, L);
+        const bool seg_first = x == seg_start;
+        const bool owns_new = APPEND && u_end == seg_end;
+        const int pnew = L - 1;
+        const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+        const int64_t head_off = (int64_t)g * D;
+
+        float m[4], lsum[4], acc[G][8];
+        typename M::vec qhi[NK], qlo[NK];
+        float score_fix = 1.f;
+
+        // Q of this segment (rotated here when the append is fused), then the MFMA operands.
+        auto setup_q = [&]() {
+            const float* qsrc = a.q + ((int64_t)b * Hq + g * G) * D;
+            for (int i = tid; i < G * D; i += kThreads) s_q[i / D][i % D] = qsrc[i];
+            if constexpr (APPEND) {
+                rotate_and_append<D, G, BF16>(a, b, g, pnew, owns_new, seg_first, &s_q[0][0],
+                                              s_kx, &s_cs[0][0], s_r);
+            } else {
+                __syncthreads();
+            }
+            const float qs = a.scale * kLog2e;
+            float qv[NK][8];
+            float qmax = 0.f;
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    qv[i][j] = l16 < G ? s_q[l16][32 * i + 8 * q4 + j] * qs : 0.f;
+                    qmax = fmaxf(qmax, fabsf(qv[i][j]));
+                }
+            float qscale = 1.f;
+            score_fix = 1.f;
+            if constexpr (!BF16) {
+                // fp16 operand: bring max |q| below 2^14 with an exact power-of-two scale
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+                if (qmax >= 16384.f && qmax <= 3.0e38f) {
+                    const int e = ilogbf(qmax) - 13;
+                    qscale = ldexpf(1.f, -e);
+                    score_fix = ldexpf(1.f, e);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float xq = qv[i][j] * qscale;
+                    const typename M::elem hi = (typename M::elem)xq;
+                    qhi[i][j] = hi;
+                    qlo[i][j] = (typename M::elem)(xq - (float)hi);
+                }
+        };
+
+        setup_q();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            m[r] = -INFINITY;
+            lsum[r] = 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+        for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
+            const int c_hi = min(tok_hi, c_lo + chunk_tokens);
+            const int first_blk = (int)bdiv.div((uint32_t)c_lo);
+            const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
+            __syncthreads();  // previous readers of s_tbl are done
+            for (int i = tid; i < n_blk; i += kThreads) {
+                const int64_t id = trow[first_blk + i];
+                s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+            }
+            __syncthreads();
+
+            auto row_off = [&](int t) -> int64_t {
+                const int j = (int)bdiv.div((uint32_t)t);
+                const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
+                return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
+            };
+            // loads are unconditional (tokens past the chunk clamp to its last row, masked at
+            // use) so that no load sits behind a branch and the prefetch is never drained
+            auto load_tile = [&](int base, uint4 (&kr)[NK], uint4 (&vr)[U]) {
+                const uint16_t* kp = a.k_pool + row_off(min(base + l16, c_hi - 1)) + 8 * q4;
+#pragma unroll
+                for (int i = 0; i < NK; ++i) kr[i] = load_stream(kp + 32 * i);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int tv = min(base + u * TPL + vrow, c_hi - 1);
+                    vr[u] = load_stream(a.v_pool + row_off(tv) + 8 * vcol);
+                }
+            };
+            auto compute_tile = [&](int base, const uint4 (&kc)[NK], const uint4 (&vc)[U]) {
+                f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    const typename M::vec kv = __builtin_bit_cast(typename M::vec, kc[i]);
+                    sacc = M::mma(qhi[i], kv, sacc);
+                    sacc = M::mma(qlo[i], kv, sacc);
+                }
+                const bool tok_ok = base + l16 < c_hi;
+                float p[4], alpha[4];
+                bool grew = false;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok = tok_ok && (4 * q4 + r) < G;
+                    const float sc = ok ? sacc[r] * score_fix : -INFINITY;
+                    const float tmax = row16_max(sc);
+                    const float m_new = fmaxf(m[r], tmax);
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    alpha[r] = exp2f(m[r] - m_use);
+                    p[r] = exp2f(sc - m_use);
+                    lsum[r] = fmaf(lsum[r], alpha[r], p[r]);
+                    grew |= m_new != m[r];
+                    m[r] = m_new;
+                }
+                *reinterpret_cast<float4*>(&s_p[wave][l16][4 * q4]) =
+                    make_float4(p[0], p[1], p[2], p[3]);
+                const bool rescale = __any(grew);
+                if (rescale && l16 == 0)
+                    *reinterpret_cast<float4*>(&s_alpha[wave][4 * q4]) =
+                        make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
+                wave_lds_sync();
+                if (rescale) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float al = s_alpha[wave][h];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[h][j] *= al;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int tt = u * TPL + vrow;
+                    float pv[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) pv[h] = s_p[wave][tt][h];
+                    const uint4 raw = base + tt < c_hi ? vc[u] : make_uint4(0, 0, 0, 0);
+                    float vf[8];
+                    decode8<BF16>(raw, vf);
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pv[h], vf[j], acc[h][j]);
+                }
+                wave_lds_sync();
+            };
+
+            // two register buffers: the next tile's K/V rows load while this one is computed
+            // (the loop is unrolled by two so each buffer keeps its registers)
+            constexpr int kStride = kWaves * kTile;
+            int base = c_lo + wave * kTile;
+            uint4 ka[NK], va[U], kb[NK], vb[U];
+            load_tile(base, ka, va);
+            while (base < c_hi) {
+                load_tile(base + kStride, kb, vb);
+                compute_tile(base, ka, va);
+                base += kStride;
+                if (base >= c_hi) break;
+                load_tile(base + kStride, ka, va);
+                compute_tile(base, kb, vb);
+                base += kStride;
+            }
+        }
+
+        // ---- combine within each wave, then across the waves
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] = cross_group_sum<R>(acc[h][j]);
+        if (l16 == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = 4 * q4 + r;
+                if (h < G) {
+                    s_m[wave][h] = m[r];
+                    s_l[wave][h] = lsum[r];
+                }
+            }
+        }
+        if (vrow == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s_acc[wave][h][vcol * 8 + j] = acc[h][j];
+        }
+        __syncthreads();
+
+        const bool full = seg_first && u_end == seg_end;
+        const int slot = blockIdx.x * 2 + (seg_start > r0 ? 1 : 0);
+        for (int i = tid; i < G * D; i += kThreads) {
+            const int h = i / D;
+            const int d = i % D;
+            float Mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+            const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float e = exp2f(s_m[w][h] - M_use);
+                num = fmaf(e, s_acc[w][h][d], num);
+                den = fmaf(e, s_l[w][h], den);
+            }
+            if (full) {
+                a.out[((int64_t)b * Hq + g * G + h) * D + d] = num / den;
+            } else {
+                store_shared(part_acc + ((int64_t)slot * G + h) * D + d, num);
+                if (d == 0) {
+                    store_shared(part_ml + ((int64_t)slot * G + h) * 2, Mx);
+                    store_shared(part_ml + ((int64_t)slot * G + h) * 2 + 1, den);
+                }
+            }
+        }
+        if (!full) {
+            const int w_a = seg_start / T;
+            const int w_b = (seg_end - 1) / T;
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores are complete
+            __syncthreads();                // ... and so are every other thread's
+            int* counter = a.counters + (int64_t)b * Hkv + g;
+            if (tid == 0) s_last = fetch_add_shared(counter, 1) == w_b - w_a;
+            __syncthreads();
+            if (s_last) {
+                for (int i = tid; i < G * D; i += kThreads) {
+                    const int h = i / D;
+                    const int d = i % D;
+                    float Mx = -INFINITY;
+                    for (int w0 = w_a; w0 <= w_b; w0 += 8) {
+                        float mk[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            const int w = w0 + k;
+                            const int sl = w * 2 + (w == w_a && seg_start != w_a * T ? 1 : 0);
+                            mk[k] = w <= w_b ? load_shared(part_ml + ((int64_t)sl * G + h) * 2)
+                                             : -INFINITY;
+                        }
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) Mx = fmaxf(Mx, mk[k]);
+                    }
+                    const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+                    float num = 0.f, den = 0.f;
+                    for (int w0 = w_a; w0 <= w_b; w0 += 8) {
+                        float mk[8], lk[8], ak[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            const int w = w0 + k;
+                            const int sl = w * 2 + (w == w_a && seg_start != w_a * T ? 1 : 0);
+                            const bool ok = w <= w_b;
+                            mk[k] = ok ? load_shared(part_ml + ((int64_t)sl * G + h) * 2) : -INFINITY;
+                            lk[k] = ok ? load_shared(part_ml + ((int64_t)sl * G + h) * 2 + 1) : 0.f;
+                            ak[k] = ok ? load_shared(part_acc + ((int64_t)sl * G + h) * D + d) : 0.f;
+                        }
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            const float e = exp2f(mk[k] - M_use);
+                            den = fmaf(e, lk[k], den);
+                            num = fmaf(e, ak[k], num);
+                        }
+                    }
+                    a.out[((int64_t)b * Hq + g * G + h) * D + d] = num / den;
+                }
+                if (tid == 0) store_shared(counter, 0);  // ready for the next call
+            }
+        }
+        __syncthreads();  // LDS (s_q, s_acc, s_m, s_l, s_tbl) is reused by the next unit
+
+        x = u_end;
+        if (x < r1) {
+            if (++g == Hkv) {
+                g = 0;
+                do { ++b; } while (b < B - 1 && s_len[b] == 0);
+            }
+        }
+    }
+}
+
+template <int D, int G, bool BF16, bool APPEND>
+hipError_t launch_typed(const BalancedArgs& a, hipStream_t stream) {
+    auto kern = decode_balanced_kernel<D, G, BF16, APPEND>;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const int grid = (int)std::min<int64_t>((int64_t)per_cu * a.num_cus, kMaxBalancedGrid);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool BF16, bool APPEND>
+hipError_t dispatch_g(const BalancedArgs& a, hipStream_t stream) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return launch_typed<D, 1, BF16, APPEND>(a, stream);
+        case 2: return launch_typed<D, 2, BF16, APPEND>(a, stream);
+        case 3: return launch_typed<D, 3, BF16, APPEND>(a, stream);
+        case 4: return launch_typed<D, 4, BF16, APPEND>(a, stream);
+        case 5: return launch_typed<D, 5, BF16, APPEND>(a, stream);
+        case 6: return launch_typed<D, 6, BF16, APPEND>(a, stream);
+        case 7: return launch_typed<D, 7, BF16, APPEND>(a, stream);
+        case 8: return launch_typed<D, 8, BF16, APPEND>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool BF16, bool APPEND>
+hipError_t dispatch_d(const BalancedArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 32: return dispatch_g<32, BF16, APPEND>(a, stream);
+        case 64: return dispatch_g<64, BF16, APPEND>(a, stream);
+        case 128: return dispatch_g<128, BF16, APPEND>(a, stream);
+        case 256: return dispatch_g<256, BF16, APPEND>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_balanced(const BalancedArgs& a, hipStream_t stream) {
+    if (a.append) return a.bf16 ? dispatch_d<true, true>(a, stream) : dispatch_d<false, true>(a, stream);
+    return a.bf16 ? dispatch_d<true, false>(a, stream) : dispatch_d<false, false>(a, stream);
+}
+
+}  // namespace pkv

@@ -13,7 +13,8 @@
 //     (page "makarna/pkg/kvcache/paged_cache.go": float32ToFloat16Bits, float32ToBFloat16Bits,
 //      GetBlockForPosition, GetBlockOffset, Append).
 //
-// Numerics, chosen so the stored bits are reproducible on any IEEE machine:
+// Numerics (helpers in pkv_device.h), chosen so the stored bits are reproducible on any IEEE
+// machine:
 //   - the sum of squares is accumulated in double in index order, every product and sum
 //     rounded separately (no contraction in this file);
 //   - angle, cos, sin and both rotation terms are double; each result is rounded once to float;
@@ -21,61 +22,13 @@
 //     (IEEE 754 leaves its sign and payload to the implementation); V is converted untouched,
 //     so its NaN payloads follow the conversion rule.
 // The kernel is latency bound (a few hundred KiB per step), so it favours exactness over speed.
+#include "pkv_device.h"
 #include "pkv_internal.h"
-
-#pragma clang fp contract(off)
 
 namespace pkv {
 namespace {
 
-// f32 bits -> IEEE binary16 bits, round to nearest even. Normal results use the
-// "add half-ulp minus one plus the kept lsb, then truncate" form on the re-biased word, so a
-// carry out of the fraction bumps the exponent by itself; subnormal results shift the
-// significand (with its implicit bit) into the 2^-24 grid and round on the dropped bits.
-__device__ __forceinline__ uint16_t f32_to_f16_bits(uint32_t u) {
-    const uint32_t sign = (u >> 16) & 0x8000u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) {  // NaN: sign, all-ones exponent, 10 leading payload bits, non-zero
-        uint32_t pl = (a >> 13) & 0x3FFu;
-        return (uint16_t)(sign | 0x7C00u | (pl ? pl : 1u));
-    }
-    if (a >= 0x477FF000u)   // >= 65520 (max + half ulp) and +-Inf: infinity
-        return (uint16_t)(sign | 0x7C00u);
-    if (a >= 0x38800000u) { // >= 2^-14: normal binary16
-        const uint32_t r = a - 0x38000000u;  // exponent bias 127 -> 15
-        return (uint16_t)(sign | ((r + 0x0FFFu + ((r >> 13) & 1u)) >> 13));
-    }
-    if (a <= 0x33000000u)   // <= 2^-25: rounds to zero (2^-25 itself is a tie to even 0)
-        return (uint16_t)sign;
-    const uint32_t e = a >> 23;                     // 102 .. 112
-    const uint32_t m = (a & 0x007FFFFFu) | 0x00800000u;
-    const uint32_t sh = 126u - e;                   // 14 .. 24
-    uint32_t q = m >> sh;
-    const uint32_t rem = m & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1u);
-    q += (rem > half) | ((rem == half) & (q & 1u));
-    return (uint16_t)(sign | q);  // q == 0x400 is the smallest normal, encoded correctly
-}
-
-// f32 bits -> bfloat16 bits, round to nearest even on the low half word (carries into the
-// exponent and overflows to Inf by themselves); NaN keeps sign and 7 leading payload bits,
-// forced non-zero.
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(uint32_t u) {
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
-        uint32_t pl = (u >> 16) & 0x7Fu;
-        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7F80u | (pl ? pl : 1u));
-    }
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ uint16_t encode16(float x, bool bf16) {
-    const uint32_t u = __float_as_uint(x);
-    return bf16 ? f32_to_bf16_bits(u) : f32_to_f16_bits(u);
-}
-
-__device__ __forceinline__ float canonical_if_nan(float v) {
-    return __builtin_isnan(v) ? __uint_as_float(0x7FC00000u) : v;
-}
+using namespace dev;
 
 constexpr int kWaves = 4;
 constexpr int kMaxD = 256;
@@ -107,15 +60,7 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
 
     const float* x = xs[wave];
     const float* w = is_q ? a.q_norm_w : a.k_norm_w;
-    double r = 1.0;
-    if (w != nullptr) {
-        double ss = 0.0;
-        for (int d = 0; d < D; ++d) {
-            const double xd = (double)x[d];
-            ss = ss + xd * xd;
-        }
-        r = 1.0 / sqrt(ss / (double)D + (double)a.eps);
-    }
+    const double r = w != nullptr ? rms_inv(x, D, a.eps) : 1.0;
 
     const int pos = a.positions[b];
     // destination row; an out-of-range position or block id skips the pool store
@@ -130,19 +75,13 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
         float x0 = x[i];
         float x1 = x[i + half];
         if (w != nullptr) {
-            x0 = (float)(((double)x0 * r) * (double)w[i]);
-            x1 = (float)(((double)x1 * r) * (double)w[i + half]);
+            x0 = norm_elem(x0, r, w[i]);
+            x1 = norm_elem(x1, r, w[i + half]);
         }
-        const double inv_freq = pow((double)a.theta, -(2.0 * (double)i) / (double)D);
-        const double angle = (double)pos * inv_freq;
-        double s, c;
-        sincos(angle, &s, &c);
-        const double t0 = (double)x0 * c;
-        const double t1 = (double)x1 * s;
-        const double t2 = (double)x1 * c;
-        const double t3 = (double)x0 * s;
-        const float y0 = canonical_if_nan((float)(t0 - t1));
-        const float y1 = canonical_if_nan((float)(t2 + t3));
+        double c, s;
+        rope_cs(pos, a.theta, i, D, c, s);
+        float y0, y1;
+        rope_rotate(x0, x1, c, s, y0, y1);
         if (is_q) {
             float* qo = a.q_out + ((int64_t)b * a.Hq + head) * D;
             qo[i] = y0;

@@ -42,138 +42,23 @@
 // base so exp2(-inf - (-inf)) never appears. One difference from a float dot product: a key
 // holding +-Inf meets the zero remainder of an exactly representable q element in the MFMA,
 // which gives NaN where float arithmetic would give an infinite score.
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
+using namespace dev;
 
 constexpr int kWaves = 4;
 constexpr int kTile = 16;       // tokens per wave per iteration
 constexpr int kTblCap = 1024;   // block ids staged in LDS per workgroup (bounds split_tokens)
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <bool BF16>
-struct Mma;
-template <>
-struct Mma<true> {
-    using vec = bf16x8;
-    using elem = __bf16;
-    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <>
-struct Mma<false> {
-    using vec = f16x8;
-    using elem = _Float16;
-    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-};
-
-// ---- cross-lane helpers ------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-// Reductions over each row of 16 lanes; every lane of the row receives the same value (each
-// step combines a lane with its partner under an involution: lane^1, lane^2, the other quad
-// of the half row, the other half of the row).
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp_f<0xB1>(x));
-    x = fmaxf(x, dpp_f<0x4E>(x));
-    x = fmaxf(x, dpp_f<0x141>(x));
-    x = fmaxf(x, dpp_f<0x140>(x));
-    return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp_f<0xB1>(x);
-    x += dpp_f<0x4E>(x);
-    x += dpp_f<0x141>(x);
-    x += dpp_f<0x140>(x);
-    return x;
-}
-
-// Sum across the 64/R lane groups of a wave (lanes l, l ^ R, l ^ 2R, ...).
-template <int R>
-__device__ __forceinline__ float cross_group_sum(float x) {
-#pragma unroll
-    for (int off = R; off < 64; off <<= 1) x += __shfl_xor(x, off);
-    return x;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <bool BF16>
-__device__ __forceinline__ void decode8(const uint4 raw, float (&f)[8]) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (BF16) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        } else {
-            f[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xFFFFu));
-            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
-        }
-    }
-}
-
-// Unsigned division by the block size: shift for powers of two, otherwise a multiply-high
-// with a precomputed magic number (round-up method with the add fix-up, exact for all u32).
-struct BlockDiv {
-    uint32_t magic, shift;
-    bool pow2;
-    __device__ __forceinline__ uint32_t div(uint32_t n) const {
-        if (pow2) return n >> shift;
-        const uint32_t t = __umulhi(n, magic);
-        return (t + ((n - t) >> 1)) >> shift;
-    }
-};
-
-__device__ __forceinline__ BlockDiv make_div(uint32_t d) {
-    BlockDiv r;
-    r.pow2 = (d & (d - 1)) == 0;
-    uint32_t l = 0;
-    while ((1ull << l) < d) ++l;  // l = ceil(log2 d)
-    if (r.pow2) {
-        r.shift = l;
-        r.magic = 0;
-    } else {
-        r.magic = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
-        r.shift = l - 1;
-    }
-    return r;
-}
-
-// 16-byte load of streamed K/V codes, marked non-temporal: every row is read once per call.
-__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
-    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Device-coherent accesses to the partition partials (see the merge at the end of the kernel).
-__device__ __forceinline__ void store_shared(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_shared(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Attended length of a sequence: context_lens[b], capped by max_context_len and by the
 // tokens its table row can address (so every table and pool index stays in range).
 __device__ __forceinline__ int clamp_len(int L, const DecodeArgs& a) {
     const int64_t cap = min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
+    if (a.lens_are_positions) return (L >= 0 && L < cap) ? L + 1 : 0;
     return (int)min((int64_t)L, cap);
 }
 
@@ -463,9 +348,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();                // ... and so are every other thread's
     int* counter = a.counters + (int64_t)b * a.Hkv + g;
-    if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 nsplit - 1;
+    if (threadIdx.x == 0) s_last = fetch_add_shared(counter, 1) == nsplit - 1;
     __syncthreads();
     if (!s_last) return;
     for (int i = threadIdx.x; i < G * D; i += kWaves * 64) {
@@ -502,8 +385,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
         }
         a.out[((int64_t)b * Hq + g * G + h) * D + d] = num / den;
     }
-    if (threadIdx.x == 0)  // ready for the next call
-        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) store_shared(counter, 0);  // ready for the next call
 }
 
 template <int D, int G, bool BF16>

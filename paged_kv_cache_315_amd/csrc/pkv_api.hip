@@ -69,25 +69,81 @@ int choose_split(int B, int Hkv, int max_context_len, int block_size, int cus) {
     return best;
 }
 
-// Workspace of the decode call: partial sums, partial (max, sum) pairs, merge counters.
+// Workspace of the decode calls: the merge counters first (a fixed place whichever schedule a
+// call uses, so they stay zero across calls of either kind), then the partial results.
 struct WorkspaceLayout {
-    size_t acc_off, ml_off, cnt_off, total;
+    size_t cnt_off, acc_off, ml_off, total;
+    bool balanced;
+    int64_t S;  // partitions per sequence (partitioned schedule)
 };
 
-WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int D, int64_t S) {
-    WorkspaceLayout w{0, 0, 0, 0};
-    if (S <= 1) return w;
-    const size_t parts = (size_t)B * Hq * S;
-    w.acc_off = 0;
-    w.ml_off = parts * D * sizeof(float);
-    w.cnt_off = w.ml_off + parts * 2 * sizeof(float);
-    w.total = w.cnt_off + (size_t)B * Hkv * sizeof(int);
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// The balanced schedule needs the per-sequence tile prefix in LDS and int32 tile counts.
+bool balanced_ok(int B, int Hkv, int64_t max_tokens) {
+    return B <= pkv::kMaxBalancedBatch && (int64_t)B * Hkv * ((max_tokens + 15) / 16) < (1LL << 31);
+}
+
+WorkspaceLayout layout_for(int B, int Hq, int Hkv, int D, int64_t max_tokens, int split_tokens,
+                           int block_size, bool balanced) {
+    WorkspaceLayout w{0, 0, 0, 0, balanced, 1};
+    const size_t cnt = align256((size_t)B * Hkv * sizeof(int));
+    size_t parts;
+    if (balanced) {
+        parts = (size_t)pkv::kMaxBalancedGrid * 2 * (Hq / Hkv);
+    } else {
+        const int P = split_tokens;
+        w.S = (max_tokens + P - 1) / P;
+        if (w.S <= 1) return w;  // one partition per sequence: no partials, no counters
+        parts = (size_t)B * Hq * w.S;
+    }
+    (void)block_size;
+    w.cnt_off = 0;
+    w.acc_off = cnt;
+    w.ml_off = w.acc_off + align256(parts * D * sizeof(float));
+    w.total = w.ml_off + align256(parts * 2 * sizeof(float));
     return w;
 }
 
 bool decode_shape_supported(int Hq, int Hkv, int D) {
     const int G = Hq / Hkv;
     return (D == 32 || D == 64 || D == 128 || D == 256) && G >= 1 && G <= 8;
+}
+
+// Size / shape checks shared by the calls; returns PKV_OK or sets the error text.
+pkv_status check_common(const char* who, int B, int Hq, int Hkv, int D, int bs, int64_t nb,
+                        int max_blocks, pkv_dtype dtype) {
+    if (B < 0) return fail(PKV_ERR_INVALID_ARG, "%s: B = %d < 0", who, B);
+    if (Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || nb <= 0 || max_blocks <= 0)
+        return fail(PKV_ERR_INVALID_ARG,
+                    "%s: sizes must be positive (Hq=%d Hkv=%d D=%d bs=%d num_blocks=%lld "
+                    "max_blocks_per_seq=%d)",
+                    who, Hq, Hkv, D, bs, (long long)nb, max_blocks);
+    if (Hq % Hkv)
+        return fail(PKV_ERR_INVALID_ARG, "%s: Hq=%d not a multiple of Hkv=%d", who, Hq, Hkv);
+    if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dtype);
+    return PKV_OK;
+}
+
+pkv_status check_rope(const char* who, float theta, const float* qn, const float* kn, int D) {
+    if (!(theta > 0.f) || !isfinite(theta))
+        return fail(PKV_ERR_INVALID_ARG, "%s: rope_theta=%g must be finite and > 0", who,
+                    (double)theta);
+    if ((qn == nullptr) != (kn == nullptr))
+        return fail(PKV_ERR_INVALID_ARG, "%s: give both QK-norm weights or neither", who);
+    if ((D & 1) || D > 256)
+        return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d must be even and <= 256", who, D);
+    return PKV_OK;
+}
+
+pkv_status check_decode_shape(const char* who, int B, int Hq, int Hkv, int D) {
+    if (!decode_shape_supported(Hq, Hkv, D))
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "%s: head_dim=%d (need 32/64/128/256) or GQA group %d (need 1..8) not built",
+                    who, D, Hq / Hkv);
+    if (B > kMaxGridDim || Hkv > kMaxGridDim)
+        return fail(PKV_ERR_UNSUPPORTED, "%s: B=%d or Hkv=%d above %d", who, B, Hkv, kMaxGridDim);
+    return PKV_OK;
 }
 
 }  // namespace
@@ -115,25 +171,11 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
                          const float* k_norm_w, float rms_eps, float rope_theta, int B,
                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                          int64_t num_blocks, pkv_dtype dtype, void* stream) {
-    if (B < 0) return fail(PKV_ERR_INVALID_ARG, "kv_append: B = %d < 0", B);
-    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_blocks <= 0 || max_blocks_per_seq <= 0)
-        return fail(PKV_ERR_INVALID_ARG,
-                    "kv_append: sizes must be positive (Hq=%d Hkv=%d D=%d bs=%d num_blocks=%lld "
-                    "max_blocks_per_seq=%d)",
-                    num_q_heads, num_kv_heads, head_dim, block_size, (long long)num_blocks,
-                    max_blocks_per_seq);
-    if (num_q_heads % num_kv_heads)
-        return fail(PKV_ERR_INVALID_ARG, "kv_append: Hq=%d not a multiple of Hkv=%d", num_q_heads,
-                    num_kv_heads);
-    if (!(rope_theta > 0.f) || !isfinite(rope_theta))
-        return fail(PKV_ERR_INVALID_ARG, "kv_append: rope_theta=%g must be finite and > 0",
-                    (double)rope_theta);
-    if ((q_norm_w == nullptr) != (k_norm_w == nullptr))
-        return fail(PKV_ERR_INVALID_ARG, "kv_append: give both QK-norm weights or neither");
-    if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "kv_append: unknown dtype %d", (int)dtype);
-    if ((head_dim & 1) || head_dim > 256)
-        return fail(PKV_ERR_UNSUPPORTED, "kv_append: head_dim=%d must be even and <= 256", head_dim);
+    pkv_status st = check_common("kv_append", B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    st = check_rope("kv_append", rope_theta, q_norm_w, k_norm_w, head_dim);
+    if (st != PKV_OK) return st;
     if (B == 0) return PKV_OK;
     if (!q_in || !k_in || !v_in || !q_out || !k_pool || !v_pool || !block_tables || !positions)
         return fail(PKV_ERR_INVALID_ARG, "kv_append: NULL pointer argument");
@@ -169,22 +211,100 @@ int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_d
     if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         max_context_len <= 0)
         return 0;
-    (void)num_q_heads;
     return choose_split(B, num_kv_heads, max_context_len, block_size, device_cus());
 }
 
 size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
                                   int block_size, int max_context_len, int split_tokens) {
     if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        max_context_len <= 0)
+        max_context_len <= 0 || split_tokens < 0 || num_q_heads % num_kv_heads)
         return 0;
-    const int P = split_tokens > 0 ? split_tokens
-                                   : pkv_decode_split_tokens(B, num_q_heads, num_kv_heads, head_dim,
-                                                             block_size, max_context_len);
-    if (P <= 0) return 0;
-    const int64_t S = ((int64_t)max_context_len + P - 1) / P;
-    return workspace_layout(B, num_q_heads, num_kv_heads, head_dim, S).total;
+    const bool bal = split_tokens == 0 && balanced_ok(B, num_kv_heads, max_context_len);
+    int P = split_tokens;
+    if (!bal && P == 0) P = pkv_decode_split_tokens(B, num_q_heads, num_kv_heads, head_dim,
+                                                    block_size, max_context_len);
+    return layout_for(B, num_q_heads, num_kv_heads, head_dim, max_context_len, P, block_size, bal)
+        .total;
 }
+
+size_t pkv_decode_step_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq) {
+    if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads)
+        return 0;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    const int max_ctx = (int)std::min<int64_t>(cap, 0x7FFFFFFF);
+    return pkv_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_ctx, 0);
+}
+
+namespace {
+
+// Runs the decode on the schedule `wl` describes (q already rotated).
+pkv_status run_decode(const float* q, const void* k_pool, const void* v_pool,
+                      const int32_t* tables, int max_blocks, const int32_t* context_lens,
+                      int max_context_len, float scale, float* out, void* workspace,
+                      const WorkspaceLayout& wl, int P, int B, int Hq, int Hkv, int D, int bs,
+                      int64_t nb, pkv_dtype dtype, hipStream_t stream,
+                      bool lens_are_positions = false) {
+    char* ws = static_cast<char*>(workspace);
+    const bool has_ws = wl.total > 0;
+    hipError_t e;
+    if (wl.balanced) {
+        pkv::BalancedArgs a{};
+        a.q = q;
+        a.k_pool = static_cast<uint16_t*>(const_cast<void*>(k_pool));
+        a.v_pool = static_cast<uint16_t*>(const_cast<void*>(v_pool));
+        a.tables = tables;
+        a.lens = context_lens;
+        a.out = out;
+        a.part_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+        a.part_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+        a.counters = reinterpret_cast<int*>(ws + wl.cnt_off);
+        a.max_blocks = max_blocks;
+        a.max_context_len = max_context_len;
+        a.scale = scale;
+        a.B = B;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.D = D;
+        a.bs = bs;
+        a.num_blocks = nb;
+        a.num_cus = device_cus();
+        a.bf16 = dtype == PKV_BF16;
+        a.append = false;
+        e = pkv::launch_decode_balanced(a, stream);
+    } else {
+        pkv::DecodeArgs a;
+        a.q = q;
+        a.k_pool = static_cast<const uint16_t*>(k_pool);
+        a.v_pool = static_cast<const uint16_t*>(v_pool);
+        a.tables = tables;
+        a.context_lens = context_lens;
+        a.out = out;
+        a.part_acc = has_ws ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
+        a.part_ml = has_ws ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+        a.counters = has_ws ? reinterpret_cast<int*>(ws + wl.cnt_off) : nullptr;
+        a.max_blocks = max_blocks;
+        a.max_context_len = max_context_len;
+        a.scale = scale;
+        a.split_tokens = P;
+        a.S = (int)wl.S;
+        a.B = B;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.D = D;
+        a.bs = bs;
+        a.num_blocks = nb;
+        a.bf16 = dtype == PKV_BF16;
+        a.lens_are_positions = lens_are_positions;
+        e = pkv::launch_paged_decode(a, stream);
+    }
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+}  // namespace
 
 pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void* v_pool,
                                  const int32_t* block_tables, int max_blocks_per_seq,
@@ -193,71 +313,117 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                                  int split_tokens, int B, int num_q_heads, int num_kv_heads,
                                  int head_dim, int block_size, int64_t num_blocks,
                                  pkv_dtype dtype, void* stream) {
-    if (B < 0 || max_context_len < 0)
-        return fail(PKV_ERR_INVALID_ARG, "decode: B=%d and max_context_len=%d must be >= 0", B,
-                    max_context_len);
-    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_blocks <= 0 || max_blocks_per_seq <= 0)
-        return fail(PKV_ERR_INVALID_ARG,
-                    "decode: sizes must be positive (Hq=%d Hkv=%d D=%d bs=%d num_blocks=%lld "
-                    "max_blocks_per_seq=%d)",
-                    num_q_heads, num_kv_heads, head_dim, block_size, (long long)num_blocks,
-                    max_blocks_per_seq);
-    if (num_q_heads % num_kv_heads)
-        return fail(PKV_ERR_INVALID_ARG, "decode: Hq=%d not a multiple of Hkv=%d", num_q_heads,
-                    num_kv_heads);
-    if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "decode: unknown dtype %d", (int)dtype);
+    pkv_status st = check_common("decode", B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    if (max_context_len < 0)
+        return fail(PKV_ERR_INVALID_ARG, "decode: max_context_len=%d must be >= 0", max_context_len);
     if (split_tokens < 0 || split_tokens % 64 || split_tokens > max_split_for(block_size))
         return fail(PKV_ERR_INVALID_ARG,
                     "decode: split_tokens=%d must be 0 or a positive multiple of 64 of at most "
                     "%lld (= %d block ids per partition)",
                     split_tokens, (long long)max_split_for(block_size), kTblCap - 2);
-    if (!decode_shape_supported(num_q_heads, num_kv_heads, head_dim))
-        return fail(PKV_ERR_UNSUPPORTED,
-                    "decode: head_dim=%d (need 32/64/128/256) or GQA group %d (need 1..8) not built",
-                    head_dim, num_q_heads / num_kv_heads);
-    if (B > kMaxGridDim || num_kv_heads > kMaxGridDim)
-        return fail(PKV_ERR_UNSUPPORTED, "decode: B=%d or Hkv=%d above %d", B, num_kv_heads,
-                    kMaxGridDim);
+    st = check_decode_shape("decode", B, num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
     if (B == 0 || max_context_len == 0) return PKV_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
         return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer argument");
 
-    const int P = split_tokens > 0
-                      ? split_tokens
-                      : choose_split(B, num_kv_heads, max_context_len, block_size, device_cus());
-    const int64_t S = ((int64_t)max_context_len + P - 1) / P;
-    if (S > 0x7FFFFFFF) return fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions");
-    const WorkspaceLayout wl = workspace_layout(B, num_q_heads, num_kv_heads, head_dim, S);
-    const size_t need = wl.total;
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-        return fail(PKV_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes, need);
+    const bool bal = split_tokens == 0 && balanced_ok(B, num_kv_heads, max_context_len);
+    const int P = bal ? 0
+                      : (split_tokens > 0 ? split_tokens
+                                          : choose_split(B, num_kv_heads, max_context_len,
+                                                         block_size, device_cus()));
+    if (!bal && ((int64_t)max_context_len + P - 1) / P > 0x7FFFFFFF)
+        return fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions");
+    const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim,
+                                          max_context_len, P, block_size, bal);
+    if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
+        return fail(PKV_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
+                    wl.total);
+    return run_decode(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                      max_context_len, scale, out, workspace, wl, P, B, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, dtype, static_cast<hipStream_t>(stream));
+}
 
-    pkv::DecodeArgs a;
-    a.q = q;
-    a.k_pool = static_cast<const uint16_t*>(k_pool);
-    a.v_pool = static_cast<const uint16_t*>(v_pool);
-    a.tables = block_tables;
-    a.context_lens = context_lens;
-    a.out = out;
+pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                           void* k_pool, void* v_pool, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* positions,
+                           const float* q_norm_w, const float* k_norm_w, float rms_eps,
+                           float rope_theta, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, int B, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
+                           void* stream) {
+    pkv_status st = check_common("decode_step", B, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    st = check_rope("decode_step", rope_theta, q_norm_w, k_norm_w, head_dim);
+    if (st != PKV_OK) return st;
+    st = check_decode_shape("decode_step", B, num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if (B == 0) return PKV_OK;
+    if (!q_in || !k_in || !v_in || !q_out || !k_pool || !v_pool || !block_tables || !positions ||
+        !out)
+        return fail(PKV_ERR_INVALID_ARG, "decode_step: NULL pointer argument");
+    if (q_out == q_in)
+        return fail(PKV_ERR_INVALID_ARG,
+                    "decode_step: q_out must not alias q_in (workgroups of one sequence read "
+                    "q_in while another writes q_out)");
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    const int max_ctx = (int)std::min<int64_t>(cap, 0x7FFFFFFF);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bal = balanced_ok(B, num_kv_heads, max_ctx);
+    const int P = bal ? 0 : choose_split(B, num_kv_heads, max_ctx, block_size, device_cus());
+    const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim, max_ctx, P,
+                                          block_size, bal);
+    if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
+        return fail(PKV_ERR_WORKSPACE, "decode_step: workspace %zu bytes, need %zu",
+                    workspace_bytes, wl.total);
+    if (!bal) {
+        // batches too large for the balanced schedule: the append kernel, then the partitioned
+        // decode reading positions + 1 as the attended lengths
+        st = pkv_kv_append(q_in, k_in, v_in, q_out, k_pool, v_pool, block_tables,
+                           max_blocks_per_seq, positions, q_norm_w, k_norm_w, rms_eps, rope_theta,
+                           B, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype,
+                           stream);
+        if (st != PKV_OK) return st;
+        return run_decode(q_out, k_pool, v_pool, block_tables, max_blocks_per_seq, positions,
+                          max_ctx, scale, out, workspace, wl, P, B, num_q_heads, num_kv_heads,
+                          head_dim, block_size, num_blocks, dtype, s, true);
+    }
     char* ws = static_cast<char*>(workspace);
-    a.part_acc = need ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
-    a.part_ml = need ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
-    a.counters = need ? reinterpret_cast<int*>(ws + wl.cnt_off) : nullptr;
+    pkv::BalancedArgs a{};
+    a.q = q_in;
+    a.k_in = k_in;
+    a.v_in = v_in;
+    a.q_out = q_out;
+    a.k_pool = static_cast<uint16_t*>(k_pool);
+    a.v_pool = static_cast<uint16_t*>(v_pool);
+    a.tables = block_tables;
+    a.lens = positions;
+    a.q_norm_w = q_norm_w;
+    a.k_norm_w = k_norm_w;
+    a.out = out;
+    a.part_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+    a.part_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+    a.counters = reinterpret_cast<int*>(ws + wl.cnt_off);
     a.max_blocks = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
+    a.max_context_len = max_ctx;
     a.scale = scale;
-    a.split_tokens = P;
-    a.S = (int)S;
+    a.eps = rms_eps;
+    a.theta = rope_theta;
     a.B = B;
     a.Hq = num_q_heads;
     a.Hkv = num_kv_heads;
     a.D = head_dim;
     a.bs = block_size;
     a.num_blocks = num_blocks;
+    a.num_cus = device_cus();
     a.bf16 = dtype == PKV_BF16;
-    const hipError_t e = pkv::launch_paged_decode(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
+    a.append = true;
+    const hipError_t e = pkv::launch_decode_balanced(a, s);
+    if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, "decode_step: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
 

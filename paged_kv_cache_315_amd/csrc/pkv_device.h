@@ -1,0 +1,234 @@
+// pkv_device.h — device helpers shared by the HIP kernels of libpkv (internal, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+namespace dev {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- f32 -> 16-bit codes (page "makarna/pkg/kvcache/paged_cache.go": float32ToFloat16Bits,
+// float32ToBFloat16Bits; round to nearest even, overflow to infinity, NaN keeps sign and leading
+// payload bits forced non-zero) -------------------------------------------------------------
+
+// binary16: normal results use the "add half-ulp minus one plus the kept lsb, then truncate"
+// form on the re-biased word, so a carry out of the fraction bumps the exponent by itself;
+// subnormal results shift the significand (with its implicit bit) into the 2^-24 grid and round
+// on the dropped bits.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(uint32_t u) {
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) {  // NaN
+        const uint32_t pl = (a >> 13) & 0x3FFu;
+        return (uint16_t)(sign | 0x7C00u | (pl ? pl : 1u));
+    }
+    if (a >= 0x477FF000u)   // >= 65520 (max + half ulp) and +-Inf
+        return (uint16_t)(sign | 0x7C00u);
+    if (a >= 0x38800000u) { // >= 2^-14: normal binary16
+        const uint32_t r = a - 0x38000000u;  // exponent bias 127 -> 15
+        return (uint16_t)(sign | ((r + 0x0FFFu + ((r >> 13) & 1u)) >> 13));
+    }
+    if (a <= 0x33000000u)   // <= 2^-25: zero (2^-25 itself is a tie to even 0)
+        return (uint16_t)sign;
+    const uint32_t e = a >> 23;                     // 102 .. 112
+    const uint32_t m = (a & 0x007FFFFFu) | 0x00800000u;
+    const uint32_t sh = 126u - e;                   // 14 .. 24
+    uint32_t q = m >> sh;
+    const uint32_t rem = m & ((1u << sh) - 1u);
+    const uint32_t half = 1u << (sh - 1u);
+    q += (rem > half) | ((rem == half) & (q & 1u));
+    return (uint16_t)(sign | q);  // q == 0x400 is the smallest normal, encoded correctly
+}
+
+// bfloat16: round to nearest even on the low half word (carries into the exponent and
+// overflows to Inf by themselves); NaN keeps sign and 7 leading payload bits, forced non-zero.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(uint32_t u) {
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
+        const uint32_t pl = (u >> 16) & 0x7Fu;
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7F80u | (pl ? pl : 1u));
+    }
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint16_t encode16(float x, bool bf16) {
+    const uint32_t u = __float_as_uint(x);
+    return bf16 ? f32_to_bf16_bits(u) : f32_to_f16_bits(u);
+}
+
+__device__ __forceinline__ float canonical_if_nan(float v) {
+    return __builtin_isnan(v) ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// ---- per-head QK-RMSNorm and RoPE, in double with every product and sum rounded separately
+// (pages "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock: norm then RoPE;
+// "soft3/glia/run/arch/decoder/forward.rs", forward_layer: per-head norm, full-dim RoPE) -------
+
+// 1 / sqrt(mean(x^2) + eps) for a head vector, the squares summed in index order.
+__device__ __forceinline__ double rms_inv(const float* x, int D, float eps) {
+#pragma clang fp contract(off)
+    double ss = 0.0;
+    for (int d = 0; d < D; ++d) {
+        const double xd = (double)x[d];
+        ss = ss + xd * xd;
+    }
+    return 1.0 / sqrt(ss / (double)D + (double)eps);
+}
+
+__device__ __forceinline__ float norm_elem(float x, double r, float w) {
+#pragma clang fp contract(off)
+    return (float)(((double)x * r) * (double)w);
+}
+
+// cos / sin of the angle pos * theta^(-2i/D) of rotary pair i.
+__device__ __forceinline__ void rope_cs(int pos, float theta, int i, int D, double& c, double& s) {
+#pragma clang fp contract(off)
+    const double inv_freq = pow((double)theta, -(2.0 * (double)i) / (double)D);
+    const double angle = (double)pos * inv_freq;
+    sincos(angle, &s, &c);
+}
+
+// Rotate the pair (x0, x1) = (x[i], x[i + D/2]); a NaN result becomes the canonical quiet NaN.
+__device__ __forceinline__ void rope_rotate(float x0, float x1, double c, double s, float& y0,
+                                            float& y1) {
+#pragma clang fp contract(off)
+    const double t0 = (double)x0 * c;
+    const double t1 = (double)x1 * s;
+    const double t2 = (double)x1 * c;
+    const double t3 = (double)x0 * s;
+    y0 = canonical_if_nan((float)(t0 - t1));
+    y1 = canonical_if_nan((float)(t2 + t3));
+}
+
+// ---- matrix cores -----------------------------------------------------------------------
+template <bool BF16>
+struct Mma;
+template <>
+struct Mma<true> {
+    using vec = bf16x8;
+    using elem = __bf16;
+    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mma<false> {
+    using vec = f16x8;
+    using elem = _Float16;
+    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// ---- cross-lane helpers -------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Reductions over each row of 16 lanes; every lane of the row receives the same value (each
+// step combines a lane with its partner under an involution: lane^1, lane^2, the other quad
+// of the half row, the other half of the row).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
+    return x;
+}
+
+// Sum across the 64/R lane groups of a wave (lanes l, l ^ R, l ^ 2R, ...).
+template <int R>
+__device__ __forceinline__ float cross_group_sum(float x) {
+#pragma unroll
+    for (int off = R; off < 64; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- K/V codes ----------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ void decode8(const uint4 raw, float (&f)[8]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        } else {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xFFFFu));
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
+        }
+    }
+}
+
+// 16-byte load of streamed K/V codes, marked non-temporal: every row is read once per call.
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Unsigned division by the block size: shift for powers of two, otherwise a multiply-high
+// with a precomputed magic number (round-up method with the add fix-up, exact for all u32).
+struct BlockDiv {
+    uint32_t magic, shift;
+    bool pow2;
+    __device__ __forceinline__ uint32_t div(uint32_t n) const {
+        if (pow2) return n >> shift;
+        const uint32_t t = __umulhi(n, magic);
+        return (t + ((n - t) >> 1)) >> shift;
+    }
+};
+
+__device__ __forceinline__ BlockDiv make_div(uint32_t d) {
+    BlockDiv r;
+    r.pow2 = (d & (d - 1)) == 0;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;  // l = ceil(log2 d)
+    if (r.pow2) {
+        r.shift = l;
+        r.magic = 0;
+    } else {
+        r.magic = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+        r.shift = l - 1;
+    }
+    return r;
+}
+
+// ---- values shared between workgroups -----------------------------------------------------
+// Partials and counters may be written and read by workgroups on different XCDs (each with its
+// own L2). Agent-scope atomic accesses are coherent device-wide without writing back or
+// invalidating whole L2s, which an agent-scope release / acquire fence would do.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int fetch_add_shared(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace dev
+}  // namespace pkv

@@ -45,9 +45,43 @@ struct DecodeArgs {
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
     bool bf16;
+    bool lens_are_positions;  // context_lens holds positions: L = p + 1 (fused-step fallback)
 };
 
 // Launches the decode kernel (partitions + in-kernel merge by the last partition).
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Balanced schedule (decode_balanced.hip): one resident workgroup per slot, equal tile ranges.
+constexpr int kMaxBalancedBatch = 2048;  // sequences whose tile prefix fits in LDS
+constexpr int kMaxBalancedGrid = 2048;   // workgroups; each owns two partial-piece slots
+
+struct BalancedArgs {
+    const float* q;         // append: q_in (rotated in-kernel); decode: rotated q
+    const float* k_in;      // append only
+    const float* v_in;      // append only
+    float* q_out;           // append only (must not alias q)
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    const int32_t* tables;
+    const int32_t* lens;    // append: positions (L = p + 1); decode: context_lens
+    const float* q_norm_w;  // append only, nullptr: no QK-norm
+    const float* k_norm_w;
+    float* out;
+    float* part_acc;        // [kMaxBalancedGrid * 2, G, D]
+    float* part_ml;         // [kMaxBalancedGrid * 2, G, 2]
+    int* counters;          // [B, Hkv], zero between calls
+    int max_blocks;
+    int max_context_len;    // decode only
+    float scale;
+    float eps;
+    float theta;
+    int B, Hq, Hkv, D, bs;
+    int64_t num_blocks;
+    int num_cus;
+    bool bf16;
+    bool append;
+};
+
+hipError_t launch_decode_balanced(const BalancedArgs& a, hipStream_t stream);
 
 }  // namespace pkv

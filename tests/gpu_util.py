@@ -38,13 +38,21 @@ def upload(wl: dict, device="cuda:0") -> dict:
     return d
 
 
-def gpu_step(wl: dict, dev: dict, split_tokens: int = 0):
-    """Append + decode on the GPU; returns (q_out, out) as host arrays (pools stay in dev)."""
-    q_out, out = pkv.decode_step(
-        dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["tables"],
-        dev["positions"], dev["context_lens"], wl["max_context_len"], theta=wl["theta"],
-        scale=wl["scale"], q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"], eps=wl["eps"],
-        split_tokens=split_tokens, dtype=wl["dtype"])
+def gpu_step(wl: dict, dev: dict, split_tokens: int = 0, fused: bool = False):
+    """One decode step on the GPU; returns (q_out, out) as host arrays (pools stay in dev).
+    fused: the one-launch pkv_decode_step; otherwise pkv_kv_append then pkv_paged_attn_decode
+    (split_tokens 0 = balanced schedule, > 0 = partitions of that many tokens)."""
+    if fused:
+        q_out, out = pkv.decode_step(
+            dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["tables"],
+            dev["positions"], theta=wl["theta"], scale=wl["scale"], q_norm_w=dev["q_norm_w"],
+            k_norm_w=dev["k_norm_w"], eps=wl["eps"], dtype=wl["dtype"])
+    else:
+        q_out, out = pkv.append_then_decode(
+            dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["tables"],
+            dev["positions"], dev["context_lens"], wl["max_context_len"], theta=wl["theta"],
+            scale=wl["scale"], q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"], eps=wl["eps"],
+            split_tokens=split_tokens, dtype=wl["dtype"])
     torch.cuda.synchronize()
     return q_out.cpu().numpy(), out.cpu().numpy()
 

@@ -17,11 +17,12 @@ from gpu_util import assert_close, assert_pools_equal, gpu_step, log, pool_host,
 pytestmark = pytest.mark.gpu
 
 
-def _check_workload(wl, split_tokens=0, row_mask=None, label=""):
+def _check_workload(wl, split_tokens=0, row_mask=None, label="", fused=False):
     log(f"[parity] {label or wl['name']}: B={wl['B']} Hq={wl['Hq']} Hkv={wl['Hkv']} D={wl['D']} "
-        f"bs={wl['bs']} {wl['dtype']} max_ctx={wl['max_context_len']} split={split_tokens}")
+        f"bs={wl['bs']} {wl['dtype']} max_ctx={wl['max_context_len']} split={split_tokens} "
+        f"fused={fused}")
     dev = upload(wl)
-    q_out, out = gpu_step(wl, dev, split_tokens)
+    q_out, out = gpu_step(wl, dev, split_tokens, fused=fused)
     kp = wl["k_pool"].copy()
     vp = wl["v_pool"].copy()
     q_ref = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"],
@@ -38,11 +39,12 @@ def _check_workload(wl, split_tokens=0, row_mask=None, label=""):
     return dev, q_out, out
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "two-call"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_config_parity(cfg):
-    """The five decode workloads at full size, in the launch configuration the bench times."""
+def test_config_parity(cfg, fused):
+    """The five decode workloads at full size; fused is the one-launch step the bench times."""
     wl = W.config(cfg)
-    dev, q_out, out = _check_workload(wl, label=f"config {cfg} {wl['name']}")
+    dev, q_out, out = _check_workload(wl, label=f"config {cfg} {wl['name']}", fused=fused)
     if cfg == 3:
         # edge values: NaN in a K head poisons that KV group's heads; +-Inf in V reaches out
         G = wl["Hq"] // wl["Hkv"]
@@ -55,10 +57,11 @@ def test_config_parity(cfg):
 
 
 def test_split_invariance():
-    """Changing the partition size only reorders float sums: results agree to ~1e-6."""
+    """Changing the schedule (balanced, partitions of 64..4096 tokens) only reorders float sums:
+    results agree to ~1e-6."""
     wl = W.make_workload(21, [63, 64, 65, 700, 1500, 2047], 16, 4, 128, 16, "bf16", 5e5)
     outs = []
-    for split in (64, 192, 1024, 4096):
+    for split in (0, 64, 192, 1024, 4096):
         _, _, out = _check_workload(wl, split_tokens=split, label=f"split {split}")
         outs.append(out)
     for o in outs[1:]:
@@ -84,16 +87,20 @@ def test_shapes(shape):
     wl = W.make_workload(30 + SHAPES.index(shape), cached, Hq, Hkv, D, bs, dt, theta,
                          qk_norm=norm, spare_blocks=2, extra_table_cols=1)
     _check_workload(wl, label=f"shape {shape}")
+    _check_workload(wl, label=f"shape {shape} fused", fused=True)
     _check_workload(wl, split_tokens=64, label=f"shape {shape} split 64")
 
 
-def test_many_short_sequences():
-    """B = 2048 (grid z) with short ragged lengths."""
-    cached = np.random.default_rng(40).integers(0, 200, 2048)
+@pytest.mark.parametrize("B", [2048, 2049])
+def test_many_short_sequences(B):
+    """B = 2048 (largest batch of the balanced schedule) and 2049 (the partitioned fallback),
+    short ragged lengths; every 16th row is attended by the oracle."""
+    cached = np.random.default_rng(40).integers(0, 200, B)
     wl = W.make_workload(40, cached, 8, 2, 128, 16, "bf16", 1e4)
-    mask = np.zeros(2048, dtype=np.uint8)
+    mask = np.zeros(B, dtype=np.uint8)
     mask[::16] = 1
-    _check_workload(wl, row_mask=mask, label="B=2048 (every 16th row attended by the oracle)")
+    _check_workload(wl, row_mask=mask, label=f"B={B}")
+    _check_workload(wl, row_mask=mask, label=f"B={B} fused", fused=True)
 
 
 def test_empty_batch_is_noop():
@@ -161,8 +168,8 @@ def test_block_ids_beyond_32bit_element_offsets():
     vp[idx] = dev["v_pool"]
     tables = torch.from_numpy(big_ids[small["tables"]]).cuda()
     q_out, out = pkv.decode_step(dev["q"], dev["k_new"], dev["v_new"], kp, vp, tables,
-                                 dev["positions"], dev["context_lens"], small["max_context_len"],
-                                 theta=small["theta"], scale=small["scale"], dtype="bf16")
+                                 dev["positions"], theta=small["theta"], scale=small["scale"],
+                                 dtype="bf16")
     torch.cuda.synchronize()
     q_ref, out_ref, kref, vref = oracle.decode_step(small)
     assert_close(out.cpu().numpy(), out_ref, "out")
