@@ -14,7 +14,8 @@
  *   makarna/pkg/model/arch/hybrid_decoder.go — runHybridAttentionBlock (QK-norm before RoPE,
  *     scale = 1/sqrt(HeadDim), fused-RoPE limits: even HeadDim <= 256) and
  *     runHybridAttentionBlockBatch (one query row per sequence, per-sequence block lists,
- *     kvLen = startPos + 1, queryPos = startPos, maxKvLen passed for grid sizing).
+ *     the attended length is the cached length plus one, the query position is the cached
+ *     length, and the longest length is passed for grid sizing).
  *   makarna/pkg/kvcache/paged_cache.go — float32ToFloat16Bits / float32ToBFloat16Bits (stored
  *     bits), GetBlockForPosition / GetBlockOffset (block = list[pos / BlockSize],
  *     slot = pos % BlockSize), Append (a token's row of kvDim = kv_heads * head_dim elements at
@@ -70,7 +71,7 @@ typedef enum {
  * pkv_kv_append — write the new token of each of B sequences into the cache.
  *
  * For each sequence b, with p = positions[b] (the number of tokens already cached, which is
- * both the write slot and the RoPE position; makarna's startPos = SeqLen()):
+ * both the write slot and the RoPE position, as in the makarna batch path):
  *   1. if q_norm_w and k_norm_w are given: every head vector x of q and of k becomes
  *      x / sqrt(mean(x^2) + rms_eps) * w (w = q_norm_w for q heads, k_norm_w for k heads);
  *   2. RoPE: for i < D/2 the pair (x[i], x[i + D/2]) is rotated by the angle

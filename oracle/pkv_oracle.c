@@ -11,21 +11,25 @@
  *
  * Sources (web pages, cited by title and section):
  *   [MK-DEC]  makarna/pkg/model/arch/hybrid_decoder.go
- *             - runHybridAttentionBlock: QK-norm before RoPE, scale = 1/sqrt(HeadDim),
- *               startPos = cache.SeqLen(), kvLen = startPos + seqLen.
- *             - runHybridAttentionBlockBatch: one new token per sequence, kvLen = startPos + 1,
- *               queryPos = startPos, per-sequence block lists.
+ *             - runHybridAttentionBlock: QK-norm before RoPE; the attention scale is one over the
+ *               square root of the head dimension, held as a float; the new tokens go in at the
+ *               cache's current length, and attention covers that length plus the new tokens.
+ *             - runHybridAttentionBlockBatch: one new token per sequence; its position is the
+ *               number of tokens already cached and it attends to one more token than that;
+ *               per-sequence block lists.
  *   [MK-KV]   makarna/pkg/kvcache/paged_cache.go
  *             - float32ToFloat16Bits / float32ToBFloat16Bits: the stored-bit rules.
  *             - GetBlockForPosition / GetBlockOffset: block = list[pos / BlockSize], slot = pos % BlockSize.
- *             - Append: a token's kvDim row is written at blockOffset * kvDim inside its block
- *               (token-major block rows), K and V kept in separate tensors per block.
+ *             - Append: inside its block, a token's row of (KV heads x head dim) values starts at
+ *               its slot times the row length (token-major block rows); K and V are separate
+ *               tensors per block.
  *             - viewsLockedAt: only the first kvLen tokens of the block list are valid.
  *   [GL-FWD]  soft3/glia/run/arch/decoder/forward.rs
  *             - forward_layer, QK-norm step: RMS normalisation per head vector with q_norm/k_norm.
  *             - forward_layer, RoPE step: full head_dim rotary for LlamaStyle layers.
- *             - forward_layer, CPU attention path: kv_h = h / (num_heads / kv_heads),
- *               scores = (q.k) * scale, max, exp(s - max), normalise, out += p * v.
+ *             - forward_layer, CPU attention path: query head h reads KV head h divided by the
+ *               group size; scores are scaled dot products, exponentials are taken after
+ *               subtracting the maximum, normalised by their sum, and weight the value rows.
  *
  * Readings where the pages are silent (each one is listed with its reason in the design notes):
  *   R-ROPE   rotate-half pairing (i, i + D/2), angle pos * theta^(-2i/D), all in double,
@@ -207,9 +211,9 @@ void pkvo_rmsnorm_head(const float* x, const float* w, float eps, int D, float* 
 
 /* ------------------------------------------------------------------------------------------
  * RoPE on one head vector, reading R-ROPE.
- * [MK-DEC] runHybridAttentionBlock rotates Q and K with HybridRoPE(positions, HeadDim, RopeTheta)
+ * [MK-DEC] runHybridAttentionBlock rotates Q and K with the RoPE op (positions, head dim, base)
  * after the QK-norm (and only fuses it when HeadDim is even and at most 256); [GL-FWD]
- * forward_layer uses Op::Rope with rope_dim = head_dim for LlamaStyle layers.
+ * forward_layer rotates the full head dimension for LlamaStyle layers.
  * Each rotated element that comes out NaN is stored as the canonical quiet NaN (R-NAN).
  * Pinned by: position 0 is the identity bit for bit, norm preservation, the relative-position
  * property, an independent complex-exponential formulation in numpy.
@@ -239,7 +243,7 @@ void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
 }
 
 /* Pool element offset of (block, slot, kv head, dim) in a [num_blocks, bs, Hkv, D] pool
- * ([MK-KV] Append: row of token at blockOffset * kvDim, kvDim = Hkv * D, head-minor). */
+ * ([MK-KV] Append: a token's row of Hkv * D values starts at slot * (Hkv * D), head-minor). */
 static int64_t pool_offset(int64_t blk, int slot, int g, int d, int bs, int Hkv, int D)
 {
     return ((blk * bs + slot) * Hkv + g) * (int64_t)D + d;
@@ -248,7 +252,8 @@ static int64_t pool_offset(int64_t blk, int slot, int g, int d, int bs, int Hkv,
 /* ------------------------------------------------------------------------------------------
  * KV append for a batch of one new token per sequence.
  * [MK-DEC] runHybridAttentionBlockBatch: for each sequence the new K/V row is appended at
- * startPos = SeqLen() (the number of tokens already cached) and RoPE uses that position.
+ * the sequence's current length (the number of tokens already cached), and RoPE uses that
+ * position.
  * [MK-KV] Append: the block is list[pos / BlockSize], the slot pos % BlockSize, and the value is
  * converted f32 -> fp16 (CastF32ToF16 on the GPU path, float32ToFloat16Bits on the CPU path).
  *
@@ -321,7 +326,7 @@ int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, floa
 
 /* ------------------------------------------------------------------------------------------
  * Paged-attention decode for one query token per sequence.
- * [MK-DEC] runHybridAttentionBlockBatch passes q [B, Hq*D], per-sequence block lists, kvLens and
+ * [MK-DEC] runHybridAttentionBlockBatch passes q [B, Hq*D], per-sequence block lists, the attended lengths and
  * scale = 1/sqrt(HeadDim); [MK-KV] viewsLockedAt clips the last block to kvLen tokens;
  * [GL-FWD] forward_layer's CPU attention path fixes the arithmetic: the query head h reads KV head
  * h / (Hq/Hkv); s_t = (q . k_t) * scale; m = max s_t; e_t = exp(s_t - m); out = sum e_t v_t / sum e_t.

@@ -6,8 +6,8 @@
 //     (page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock: QNorm/KNorm
 //      before RoPE; page "soft3/glia/run/arch/decoder/forward.rs", forward_layer: per-head norm)
 //   RoPE, rotate-half pairs (i, i + D/2) by pos * theta^(-2i/D)
-//     (hybrid_decoder.go, runHybridAttentionBlock: HybridRoPE(positions, HeadDim, RopeTheta);
-//      forward.rs, forward_layer: rope_dim = head_dim for LlamaStyle layers)
+//     (hybrid_decoder.go, runHybridAttentionBlock: the RoPE op takes positions, head dim and
+//      base; forward.rs, forward_layer: the full head dimension rotates for LlamaStyle layers)
 //   f32 -> 16-bit code, round to nearest even, and the store into row
 //   (tables[b][pos / bs], pos % bs) of the [num_blocks, bs, Hkv, D] pool
 //     (page "makarna/pkg/kvcache/paged_cache.go": float32ToFloat16Bits, float32ToBFloat16Bits,

@@ -4,7 +4,7 @@
 // token t of sequence b at block tables[b][t / bs], slot t % bs of the
 // [num_blocks, bs, Hkv, D] pools.
 //   (page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlockBatch: one query
-//    row per sequence over per-sequence block lists, kvLens, scale = 1/sqrt(HeadDim);
+//    row per sequence over per-sequence block lists and lengths, scale one over sqrt(head dim);
 //    page "soft3/glia/run/arch/decoder/forward.rs", forward_layer CPU attention path: kv head
 //    h / (Hq / Hkv), max-subtracted exponentials normalised by their sum;
 //    page "makarna/pkg/kvcache/paged_cache.go", viewsLockedAt: only the first kvLen tokens of
