@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("paged_kv_cache_315_amd/csrc/decode_balanced.hip",
-                  "paged_kv_cache_315_amd/csrc/pkv_device.h")
+                  "paged_kv_cache_315_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_315_amd/csrc/pkv_internal.h")
 
 
 def profiled_traffic(workload: str):

@@ -15,7 +15,9 @@
 // whatever the mix of lengths, and all of them are resident from start to end. Inside a
 // workgroup the 4 waves interleave the 16-token tiles of each unit (the part of one segment
 // that falls in the range) exactly as the partitioned kernel does: QK^T on the matrix cores,
-// online softmax, P through LDS, PV on the vector ALU, the next tile's K/V loads in flight.
+// online softmax, P through LDS, PV on the vector ALU, the next tile's K/V loads in flight. A
+// unit requests its query heads (and, fused, the new K row) together with its first chunk of
+// block ids, and the angles per position of the rotary pairs are computed once per workgroup.
 //
 // Pieces. A segment that lies inside one range is finished there (out = acc / l). A segment cut
 // by range boundaries leaves one piece (m, l, acc) per workgroup it touches; a workgroup holds at
@@ -46,23 +48,22 @@ constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 
 // Query rotation of one unit and, for the unit holding a segment's last tile, the new token's
 // K/V row (norm + RoPE in double, round-to-nearest-even codes; see kv_append.hip), stored into
-// the pool before the unit streams its tiles. Expects s_q to hold the raw query heads (written
-// by this thread block, not yet synchronised); ends with a barrier, after which this
-// workgroup's own loads of the new row see the stored codes.
+// the pool before the unit streams its tiles. Expects s_q to hold the raw query heads and s_kx
+// the new K row (written by this thread block, not yet synchronised) and s_inv the angles per
+// position of the rotary pairs; ends with a barrier, after which this workgroup's own loads of
+// the new row see the stored codes.
 template <int D, int G, bool BF16>
 __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, int g, int pnew,
                                                bool owns_new, bool seg_first, float* s_q,
-                                               float* s_kx, double* s_cs, double* s_r) {
+                                               float* s_kx, const double* s_inv, double* s_cs,
+                                               double* s_r) {
     constexpr int HALF = D / 2;
     const int tid = threadIdx.x;
     const int Hkv = a.Hkv;
     const int Hq = Hkv * G;
     const int64_t tok_stride = (int64_t)Hkv * D;
-    const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
-    if (owns_new)
-        for (int i = tid; i < D; i += kThreads) s_kx[i] = ksrc[i];
     for (int i = tid; i < HALF; i += kThreads)
-        rope_cs(pnew, a.theta, i, D, s_cs[2 * i], s_cs[2 * i + 1]);
+        rope_cs_from(pnew, s_inv[i], s_cs[2 * i], s_cs[2 * i + 1]);
     __syncthreads();
     const bool norm = a.q_norm_w != nullptr;
     if (norm) {
@@ -131,6 +132,7 @@ void decode_balanced_kernel(BalancedArgs a) {
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ __align__(16) float s_q[G][D];
     __shared__ float s_kx[APPEND ? D : 1];
+    __shared__ double s_inv[APPEND ? HALF : 1];  // theta^(-2i/D) of rotary pair i
     __shared__ double s_cs[APPEND ? HALF : 1][2];
     __shared__ double s_r[G + 1];
     __shared__ __align__(16) float s_p[kWaves][kTile][16];
@@ -169,6 +171,9 @@ void decode_balanced_kernel(BalancedArgs a) {
             s_len[b] = L;
             cnt += (L + kTile - 1) / kTile;
         }
+    }
+    if constexpr (APPEND) {  // while the lengths arrive
+        for (int i = tid; i < HALF; i += kThreads) s_inv[i] = rope_inv_freq(a.theta, i, D);
     }
     s_scan[tid] = cnt;
     __syncthreads();
@@ -236,13 +241,29 @@ void decode_balanced_kernel(BalancedArgs a) {
         typename M::vec qhi[NK], qlo[NK];
         float score_fix = 1.f;
 
-        // Q of this segment (rotated here when the append is fused), then the MFMA operands.
+        // chunk of the block table staged in LDS (kTblCap ids cover chunk_tokens tokens)
+        auto stage_table = [&](int c_lo, int c_hi) {
+            const int first_blk = (int)bdiv.div((uint32_t)c_lo);
+            const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
+            for (int i = tid; i < n_blk; i += kThreads) {
+                const int64_t id = trow[first_blk + i];
+                s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+            }
+        };
+
+        // Q of this segment (rotated here when the append is fused) and the first table chunk,
+        // requested together; then the MFMA operands.
         auto setup_q = [&]() {
+            stage_table(tok_lo, min(tok_hi, tok_lo + chunk_tokens));
             const float* qsrc = a.q + ((int64_t)b * Hq + g * G) * D;
             for (int i = tid; i < G * D; i += kThreads) s_q[i / D][i % D] = qsrc[i];
             if constexpr (APPEND) {
+                if (owns_new) {
+                    const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
+                    for (int i = tid; i < D; i += kThreads) s_kx[i] = ksrc[i];
+                }
                 rotate_and_append<D, G, BF16>(a, b, g, pnew, owns_new, seg_first, &s_q[0][0],
-                                              s_kx, &s_cs[0][0], s_r);
+                                              s_kx, s_inv, &s_cs[0][0], s_r);
             } else {
                 __syncthreads();
             }
@@ -292,13 +313,11 @@ void decode_balanced_kernel(BalancedArgs a) {
         for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
             const int c_hi = min(tok_hi, c_lo + chunk_tokens);
             const int first_blk = (int)bdiv.div((uint32_t)c_lo);
-            const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
-            __syncthreads();  // previous readers of s_tbl are done
-            for (int i = tid; i < n_blk; i += kThreads) {
-                const int64_t id = trow[first_blk + i];
-                s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+            if (c_lo != tok_lo) {  // the first chunk was staged with the query
+                __syncthreads();  // previous readers of s_tbl are done
+                stage_table(c_lo, c_hi);
+                __syncthreads();
             }
-            __syncthreads();
 
             auto row_off = [&](int t) -> int64_t {
                 const int j = (int)bdiv.div((uint32_t)t);

@@ -85,12 +85,22 @@ __device__ __forceinline__ float norm_elem(float x, double r, float w) {
     return (float)(((double)x * r) * (double)w);
 }
 
-// cos / sin of the angle pos * theta^(-2i/D) of rotary pair i.
-__device__ __forceinline__ void rope_cs(int pos, float theta, int i, int D, double& c, double& s) {
+// theta^(-2i/D), the angle per position of rotary pair i.
+__device__ __forceinline__ double rope_inv_freq(float theta, int i, int D) {
 #pragma clang fp contract(off)
-    const double inv_freq = pow((double)theta, -(2.0 * (double)i) / (double)D);
+    return pow((double)theta, -(2.0 * (double)i) / (double)D);
+}
+
+// cos / sin of the angle pos * inv_freq (inv_freq from rope_inv_freq).
+__device__ __forceinline__ void rope_cs_from(int pos, double inv_freq, double& c, double& s) {
+#pragma clang fp contract(off)
     const double angle = (double)pos * inv_freq;
     sincos(angle, &s, &c);
+}
+
+// cos / sin of the angle pos * theta^(-2i/D) of rotary pair i.
+__device__ __forceinline__ void rope_cs(int pos, float theta, int i, int D, double& c, double& s) {
+    rope_cs_from(pos, rope_inv_freq(theta, i, D), c, s);
 }
 
 // Rotate the pair (x0, x1) = (x[i], x[i + D/2]); a NaN result becomes the canonical quiet NaN.
