@@ -249,6 +249,51 @@ static int64_t pool_offset(int64_t blk, int slot, int g, int d, int bs, int Hkv,
     return ((blk * bs + slot) * Hkv + g) * (int64_t)D + d;
 }
 
+/* One new token: the query heads are normed (optional) and rotated into q_out; the K heads are
+ * normed, rotated, converted and stored, and the V heads converted and stored, into the pool row
+ * (table_row[pos / bs], pos % bs). Returns PKVO_ERR_RANGE (storing nothing) if the position or
+ * its block id is out of range. tmp / rot: scratch of D floats. */
+static int append_token(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                        uint16_t* k_pool, uint16_t* v_pool, const int32_t* table_row,
+                        int max_blocks, int pos, const float* q_norm_w, const float* k_norm_w,
+                        float eps, float theta, int Hq, int Hkv, int D, int bs,
+                        int64_t num_blocks, int dtype, float* tmp, float* rot)
+{
+    if (pos < 0 || pos / bs >= max_blocks)
+        return PKVO_ERR_RANGE;
+    const int64_t blk = table_row[pos / bs];
+    const int slot = pos % bs;
+    if (blk < 0 || blk >= num_blocks)
+        return PKVO_ERR_RANGE;
+    /* Q: optional norm, then RoPE; the float result is the output (not stored in the pool). */
+    for (int h = 0; h < Hq; ++h) {
+        const float* x = q_in + (int64_t)h * D;
+        const float* src = x;
+        if (q_norm_w) {
+            pkvo_rmsnorm_head(x, q_norm_w, eps, D, tmp);
+            src = tmp;
+        }
+        pkvo_rope_head(src, D, pos, theta, q_out + (int64_t)h * D);
+    }
+    /* K: optional norm, RoPE, convert, store. V: convert, store. */
+    for (int g = 0; g < Hkv; ++g) {
+        const float* x = k_in + (int64_t)g * D;
+        const float* src = x;
+        if (k_norm_w) {
+            pkvo_rmsnorm_head(x, k_norm_w, eps, D, tmp);
+            src = tmp;
+        }
+        pkvo_rope_head(src, D, pos, theta, rot);
+        const float* v = v_in + (int64_t)g * D;
+        for (int d = 0; d < D; ++d) {
+            const int64_t o = pool_offset(blk, slot, g, d, bs, Hkv, D);
+            k_pool[o] = encode(rot[d], dtype);
+            v_pool[o] = encode(v[d], dtype);
+        }
+    }
+    return PKVO_OK;
+}
+
 /* ------------------------------------------------------------------------------------------
  * KV append for a batch of one new token per sequence.
  * [MK-DEC] runHybridAttentionBlockBatch: for each sequence the new K/V row is appended at
@@ -280,47 +325,141 @@ int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, floa
         return PKVO_ERR_ARG;
     }
     int status = PKVO_OK;
-    for (int b = 0; b < B && status == PKVO_OK; ++b) {
-        const int pos = positions[b];
-        if (pos < 0 || pos / bs >= max_blocks) {
-            status = PKVO_ERR_RANGE;
-            break;
-        }
-        const int64_t blk = tables[(int64_t)b * max_blocks + pos / bs];
-        const int slot = pos % bs;
-        if (blk < 0 || blk >= num_blocks) {
-            status = PKVO_ERR_RANGE;
-            break;
-        }
-        /* Q: optional norm, then RoPE; the float result is the output (not stored in the pool). */
-        for (int h = 0; h < Hq; ++h) {
-            const float* x = q_in + ((int64_t)b * Hq + h) * D;
-            const float* src = x;
-            if (q_norm_w) {
-                pkvo_rmsnorm_head(x, q_norm_w, eps, D, tmp);
-                src = tmp;
-            }
-            pkvo_rope_head(src, D, pos, theta, q_out + ((int64_t)b * Hq + h) * D);
-        }
-        /* K: optional norm, RoPE, convert, store. V: convert, store. */
-        for (int g = 0; g < Hkv; ++g) {
-            const float* x = k_in + ((int64_t)b * Hkv + g) * D;
-            const float* src = x;
-            if (k_norm_w) {
-                pkvo_rmsnorm_head(x, k_norm_w, eps, D, tmp);
-                src = tmp;
-            }
-            pkvo_rope_head(src, D, pos, theta, rot);
-            const float* v = v_in + ((int64_t)b * Hkv + g) * D;
-            for (int d = 0; d < D; ++d) {
-                const int64_t o = pool_offset(blk, slot, g, d, bs, Hkv, D);
-                k_pool[o] = encode(rot[d], dtype);
-                v_pool[o] = encode(v[d], dtype);
-            }
-        }
-    }
+    for (int b = 0; b < B && status == PKVO_OK; ++b)
+        status = append_token(q_in + (int64_t)b * Hq * D, k_in + (int64_t)b * Hkv * D,
+                              v_in + (int64_t)b * Hkv * D, q_out + (int64_t)b * Hq * D, k_pool,
+                              v_pool, tables + (int64_t)b * max_blocks, max_blocks, positions[b],
+                              q_norm_w, k_norm_w, eps, theta, Hq, Hkv, D, bs, num_blocks, dtype,
+                              tmp, rot);
     free(tmp);
     free(rot);
+    return status;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * KV append of a chunk of new tokens per sequence (prefill, or several tokens at a time).
+ * [MK-DEC] runHybridAttentionBlock: a block of seqLen tokens (token-major q [seqLen, Hq*D],
+ * k / v [seqLen, Hkv*D]) goes into the cache at its current length startPos, token i at position
+ * startPos + i, RoPE taking each token's own position; [MK-KV] Append fills the block list from
+ * that position on, spanning as many blocks as needed.
+ * Tokens of sequence b are q_in rows cu_seqlens[b] .. cu_seqlens[b+1]-1, at positions
+ * start_pos[b] + i; they are processed in that order. With one token per sequence this is
+ * pkvo_kv_append with positions = start_pos.
+ * Pinned by: equality with pkvo_kv_append when every sequence has one token, equality of one call
+ * with a chunk split over two calls, and the per-token rows stored where the table says.
+ * ------------------------------------------------------------------------------------------ */
+int pkvo_prefill_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                        uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                        const int32_t* cu_seqlens, const int32_t* start_pos,
+                        const float* q_norm_w, const float* k_norm_w, float eps, float theta,
+                        int B, int Hq, int Hkv, int D, int bs, int64_t num_blocks, int dtype)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (D & 1) || bs <= 0 || Hq % Hkv)
+        return PKVO_ERR_ARG;
+    if ((q_norm_w == NULL) != (k_norm_w == NULL))
+        return PKVO_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (cu_seqlens[b + 1] < cu_seqlens[b])
+            return PKVO_ERR_ARG;
+    float* tmp = (float*)malloc(sizeof(float) * (size_t)D);
+    float* rot = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!tmp || !rot) {
+        free(tmp);
+        free(rot);
+        return PKVO_ERR_ARG;
+    }
+    int status = PKVO_OK;
+    for (int b = 0; b < B && status == PKVO_OK; ++b)
+        for (int r = cu_seqlens[b]; r < cu_seqlens[b + 1] && status == PKVO_OK; ++r) {
+            const int pos = start_pos[b] + (r - cu_seqlens[b]) + (MUT(10) ? 1 : 0);
+            status = append_token(q_in + (int64_t)r * Hq * D, k_in + (int64_t)r * Hkv * D,
+                                  v_in + (int64_t)r * Hkv * D, q_out + (int64_t)r * Hq * D,
+                                  k_pool, v_pool, tables + (int64_t)b * max_blocks, max_blocks,
+                                  pos, q_norm_w, k_norm_w, eps, theta, Hq, Hkv, D, bs,
+                                  num_blocks, dtype, tmp, rot);
+        }
+    free(tmp);
+    free(rot);
+    return status;
+}
+
+/* Attention of one query token (all Hq heads, q_row [Hq, D]) over the first L tokens of the
+ * sequence whose block list is table_row; writes out_row [Hq, D]. kc / vc: scratch of
+ * L * Hkv * D floats, e: scratch of L doubles. */
+static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t* v_pool,
+                      const int32_t* table_row, int max_blocks, int L, float scale,
+                      float* out_row, int Hq, int Hkv, int D, int bs, int64_t num_blocks,
+                      int dtype, float* kc, float* vc, double* e)
+{
+    const int G = Hq / Hkv;
+    if (L < 1 || (L + bs - 1) / bs > max_blocks)
+        return PKVO_ERR_RANGE;
+    /* gather: token t lives in block table_row[t / bs] at slot t % bs */
+    for (int t = 0; t < L; ++t) {
+        const int64_t blk = table_row[t / bs];
+        if (blk < 0 || blk >= num_blocks)
+            return PKVO_ERR_RANGE;
+        for (int g = 0; g < Hkv; ++g)
+            for (int d = 0; d < D; ++d) {
+                const int64_t o = pool_offset(blk, (t + (MUT(5) ? 1 : 0)) % bs, g, d, bs, Hkv, D);
+                kc[((int64_t)t * Hkv + g) * D + d] = decode(k_pool[o], dtype);
+                vc[((int64_t)t * Hkv + g) * D + d] = decode(v_pool[o], dtype);
+            }
+    }
+    for (int h = 0; h < Hq; ++h) {
+        const int g = MUT(4) ? h % Hkv : h / G;
+        const float* qh = q_row + (int64_t)h * D;
+        double m = -INFINITY;
+        for (int t = 0; t < L; ++t) {
+            const float* kt = kc + ((int64_t)t * Hkv + g) * D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += (double)qh[d] * (double)kt[d];
+            e[t] = (MUT(6) ? 1.0 : (double)scale) * dot;
+            if (e[t] > m) /* NaN never compares greater: ignored by the max */
+                m = e[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t < L; ++t) {
+            e[t] = exp(e[t] - m);
+            l += e[t];
+        }
+        for (int d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int t = 0; t < L; ++t)
+                acc += e[t] * (double)vc[((int64_t)t * Hkv + g) * D + d];
+            out_row[(int64_t)h * D + d] = (float)(acc / l);
+        }
+    }
+    return PKVO_OK;
+}
+
+/* Runs attend_row over n rows: row r reads q + r*Hq*D, the block list of sequence seq[r] and
+ * L = lens[r] tokens, writes out + r*Hq*D (rows with row_mask[r] == 0 are skipped). */
+static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                       const int32_t* tables, int max_blocks, const int* seq, const int* lens,
+                       float scale, float* out, int n, int Hq, int Hkv, int D, int bs,
+                       int64_t num_blocks, int dtype, const uint8_t* row_mask)
+{
+    int Lmax = 1;
+    for (int r = 0; r < n; ++r)
+        if ((!row_mask || row_mask[r]) && lens[r] > Lmax)
+            Lmax = lens[r];
+    float* kc = (float*)malloc(sizeof(float) * (size_t)Lmax * Hkv * D);
+    float* vc = (float*)malloc(sizeof(float) * (size_t)Lmax * Hkv * D);
+    double* e = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    int status = (kc && vc && e) ? PKVO_OK : PKVO_ERR_ARG;
+    for (int r = 0; r < n && status == PKVO_OK; ++r) {
+        if (row_mask && !row_mask[r])
+            continue;
+        status = attend_row(q + (int64_t)r * Hq * D, k_pool, v_pool,
+                            tables + (int64_t)seq[r] * max_blocks, max_blocks, lens[r], scale,
+                            out + (int64_t)r * Hq * D, Hq, Hkv, D, bs, num_blocks, dtype, kc, vc,
+                            e);
+    }
+    free(kc);
+    free(vc);
+    free(e);
     return status;
 }
 
@@ -345,67 +484,65 @@ int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv)
         return PKVO_ERR_ARG;
-    const int G = Hq / Hkv;
-    for (int b = 0; b < B; ++b) {
-        if (row_mask && !row_mask[b])
-            continue;
-        const int L = context_lens[b] - (MUT(9) && context_lens[b] > 1 ? 1 : 0);
-        if (L < 1 || (L + bs - 1) / bs > max_blocks)
-            return PKVO_ERR_RANGE;
-        float* kc = (float*)malloc(sizeof(float) * (size_t)L * Hkv * D);
-        float* vc = (float*)malloc(sizeof(float) * (size_t)L * Hkv * D);
-        double* e = (double*)malloc(sizeof(double) * (size_t)L);
-        if (!kc || !vc || !e) {
-            free(kc);
-            free(vc);
-            free(e);
-            return PKVO_ERR_ARG;
-        }
-        int status = PKVO_OK;
-        /* gather: token t lives in block tables[b][t / bs] at slot t % bs */
-        for (int t = 0; t < L && status == PKVO_OK; ++t) {
-            const int64_t blk = tables[(int64_t)b * max_blocks + t / bs];
-            if (blk < 0 || blk >= num_blocks) {
-                status = PKVO_ERR_RANGE;
-                break;
-            }
-            for (int g = 0; g < Hkv; ++g)
-                for (int d = 0; d < D; ++d) {
-                    const int64_t o = pool_offset(blk, (t + (MUT(5) ? 1 : 0)) % bs, g, d, bs, Hkv, D);
-                    kc[((int64_t)t * Hkv + g) * D + d] = decode(k_pool[o], dtype);
-                    vc[((int64_t)t * Hkv + g) * D + d] = decode(v_pool[o], dtype);
-                }
-        }
-        for (int h = 0; h < Hq && status == PKVO_OK; ++h) {
-            const int g = MUT(4) ? h % Hkv : h / G;
-            const float* qh = q + ((int64_t)b * Hq + h) * D;
-            double m = -INFINITY;
-            for (int t = 0; t < L; ++t) {
-                const float* kt = kc + ((int64_t)t * Hkv + g) * D;
-                double dot = 0.0;
-                for (int d = 0; d < D; ++d)
-                    dot += (double)qh[d] * (double)kt[d];
-                e[t] = (MUT(6) ? 1.0 : (double)scale) * dot;
-                if (e[t] > m) /* NaN never compares greater: ignored by the max */
-                    m = e[t];
-            }
-            double l = 0.0;
-            for (int t = 0; t < L; ++t) {
-                e[t] = exp(e[t] - m);
-                l += e[t];
-            }
-            for (int d = 0; d < D; ++d) {
-                double acc = 0.0;
-                for (int t = 0; t < L; ++t)
-                    acc += e[t] * (double)vc[((int64_t)t * Hkv + g) * D + d];
-                out[((int64_t)b * Hq + h) * D + d] = (float)(acc / l);
-            }
-        }
-        free(kc);
-        free(vc);
-        free(e);
-        if (status != PKVO_OK)
-            return status;
+    int* seq = (int*)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
+    int* lens = (int*)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
+    if (!seq || !lens) {
+        free(seq);
+        free(lens);
+        return PKVO_ERR_ARG;
     }
-    return PKVO_OK;
+    for (int b = 0; b < B; ++b) {
+        seq[b] = b;
+        lens[b] = context_lens[b] - (MUT(9) && context_lens[b] > 1 ? 1 : 0);
+    }
+    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, scale, out,
+                                   B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
+    free(seq);
+    free(lens);
+    return status;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Paged attention of a chunk of query tokens per sequence, causal.
+ * [MK-DEC] runHybridAttentionBlock: after a block of seqLen tokens is appended at startPos, the
+ * attention covers kvLen = startPos + seqLen tokens and is causal from startPos: query token i
+ * (position startPos + i) sees the cached tokens and the new tokens up to and including itself,
+ * that is the first startPos + i + 1 tokens of the sequence. The arithmetic of each query token
+ * is that of the decode above with that length.
+ * q / out [N, Hq, D] token-major; tokens of sequence b are rows cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1 at positions start_pos[b] + i. row_mask (may be NULL) selects rows.
+ * Pinned by: equality with pkvo_paged_attn_decode for one token per sequence, an independent
+ * numpy formulation with an explicit causal mask, insensitivity of each row to the K/V of later
+ * positions, and equality of one call with a chunk split over two calls.
+ * ------------------------------------------------------------------------------------------ */
+int pkvo_paged_attn_prefill(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* tables, int max_blocks, const int32_t* cu_seqlens,
+                            const int32_t* start_pos, float scale, float* out, int B, int Hq,
+                            int Hkv, int D, int bs, int64_t num_blocks, int dtype,
+                            const uint8_t* row_mask)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv)
+        return PKVO_ERR_ARG;
+    const int n = B > 0 ? cu_seqlens[B] : 0;
+    for (int b = 0; b < B; ++b)
+        if (cu_seqlens[b + 1] < cu_seqlens[b])
+            return PKVO_ERR_ARG;
+    int* seq = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+    int* lens = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+    if (!seq || !lens) {
+        free(seq);
+        free(lens);
+        return PKVO_ERR_ARG;
+    }
+    for (int b = 0; b < B; ++b)
+        for (int r = cu_seqlens[b]; r < cu_seqlens[b + 1]; ++r) {
+            seq[r] = b;
+            /* query token i of the chunk attends positions 0 .. start_pos[b] + i */
+            lens[r] = start_pos[b] + (r - cu_seqlens[b]) + (MUT(11) ? 0 : 1);
+        }
+    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, scale, out,
+                                   n, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
+    free(seq);
+    free(lens);
+    return status;
 }

@@ -9,7 +9,8 @@ torch ``bfloat16``); they are inputs, any valid codes would do.
 Every named input has its own PCG64 stream, seeded ``[workload_id, stream_id]``, so a workload
 is a pure function of its parameters.
 
-Workload shapes follow the five decode workloads the method is measured on:
+Workload shapes follow the five decode workloads the method is measured on (and, for chunked
+prefill, ``make_prefill_workload`` with the same head shapes):
   1 tiny        B=2, cached 37 / 50 tokens, 4/2 heads, D=64, bs=16, 16-block pool, fp16, theta 1e4
   2 llama3-8b   B=32, cached U{512..4096}, 32/8 heads, D=128, bs=16, bf16, theta 5e5
   3 qwen3-norm  B=64, cached 8192, 32/8 heads, D=128, bs=16, fp16, QK-RMSNorm eps 1e-6,
@@ -187,3 +188,105 @@ def unique_kv_bytes(wl: dict) -> int:
             blk = int(wl["tables"][b, j])
             rows[blk] = max(rows.get(blk, 0), min(bs, L - j * bs))
     return sum(rows.values()) * 2 * wl["Hkv"] * wl["D"] * 2
+
+
+def make_prefill_workload(wid: int, cached, chunk, Hq: int, Hkv: int, D: int, bs: int,
+                          dtype: str, theta: float, *, qk_norm: bool = False, eps: float = 1e-6,
+                          pool_std: float = 1.0, spare_blocks: int = 1,
+                          extra_table_cols: int = 0, name: str | None = None) -> dict:
+    """Draw one chunked-prefill workload: sequence b has cached[b] tokens in the cache and
+    chunk[b] new tokens (token-major rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of q / k_new /
+    v_new) at positions cached[b] .. cached[b] + chunk[b] - 1. Pool slots from position
+    cached[b] on, and spare blocks, are poisoned."""
+    cached = np.asarray(cached, dtype=np.int64)
+    chunk = np.asarray(chunk, dtype=np.int64)
+    B = int(cached.shape[0])
+    assert chunk.shape == cached.shape and np.all(chunk >= 0)
+    assert Hq % Hkv == 0 and D % 2 == 0
+    total = cached + chunk
+    need = np.maximum((total + bs - 1) // bs, 1)
+    n_assigned = int(need.sum())
+    NB = n_assigned + int(spare_blocks)
+    perm = _rng(wid, S_PERM).permutation(NB).astype(np.int32)
+    max_blocks = (int(need.max()) if B else 1) + int(extra_table_cols)
+    spare_ids = perm[n_assigned:]
+    pad_id = int(spare_ids[0]) if len(spare_ids) else int(perm[0])
+    tables = np.full((B, max_blocks), pad_id, dtype=np.int32)
+    cur = 0
+    for b in range(B):
+        n = int(need[b])
+        tables[b, :n] = perm[cur:cur + n]
+        cur += n
+    shape = (NB, bs, Hkv, D)
+    k_pool = _fill_pool(_rng(wid, S_KPOOL), shape, dtype, pool_std)
+    v_pool = _fill_pool(_rng(wid, S_VPOOL), shape, dtype, pool_std)
+    poison = POISON[dtype]
+    for pid in spare_ids:
+        k_pool[pid] = poison
+        v_pool[pid] = poison
+    for b in range(B):
+        c0 = int(cached[b])
+        for j in range(c0 // bs, int(need[b])):
+            s0 = c0 % bs if j == c0 // bs else 0
+            k_pool[tables[b, j], s0:] = poison
+            v_pool[tables[b, j], s0:] = poison
+    N = int(chunk.sum())
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(chunk)
+    q = _rng(wid, S_Q).standard_normal((N, Hq, D), dtype=np.float32)
+    k_new = _rng(wid, S_KNEW).standard_normal((N, Hkv, D), dtype=np.float32)
+    v_new = _rng(wid, S_VNEW).standard_normal((N, Hkv, D), dtype=np.float32)
+    q_norm_w = k_norm_w = None
+    if qk_norm:
+        rn = _rng(wid, S_NORM)
+        q_norm_w = rn.uniform(0.5, 1.5, D).astype(np.float32)
+        k_norm_w = rn.uniform(0.5, 1.5, D).astype(np.float32)
+    # per query token: the sequence it belongs to and the number of tokens it attends
+    tok_seq = np.repeat(np.arange(B, dtype=np.int32), chunk)
+    tok_len = (np.repeat(cached, chunk) + np.concatenate(
+        [np.arange(int(c)) for c in chunk] or [np.zeros(0, np.int64)]) + 1).astype(np.int32)
+    return {
+        "name": name or f"p{wid}", "wid": wid, "B": B, "N": N, "Hq": Hq, "Hkv": Hkv, "D": D,
+        "bs": bs, "dtype": dtype, "theta": float(theta), "eps": float(eps),
+        "start_pos": cached.astype(np.int32), "chunk": chunk.astype(np.int32),
+        "cu_seqlens": cu, "tok_seq": tok_seq, "tok_len": tok_len,
+        "max_chunk": int(chunk.max()) if B else 0,
+        "max_context_len": int(total.max()) if B else 0,
+        "tables": tables, "max_blocks": max_blocks, "num_blocks": NB,
+        "k_pool": k_pool, "v_pool": v_pool, "q": q, "k_new": k_new, "v_new": v_new,
+        "q_norm_w": q_norm_w, "k_norm_w": k_norm_w,
+        "scale": float(np.float32(1.0 / math.sqrt(D))), "spare_ids": spare_ids,
+    }
+
+
+def prefill_config(cfg_id: int) -> dict:
+    """Chunked-prefill workloads with the decode workloads' head shapes:
+      1 tiny        B=3, cached 0 / 21 / 40, chunks 7 / 30 / 1, 4/2 heads, D=64, bs=16, fp16
+      2 llama3-8b   B=4, cached U{0..2048}, chunks of 512, 32/8 heads, D=128, bs=16, bf16
+      3 spec-decode B=32, cached U{512..4096}, 4 new tokens each (draft verification), as 2
+    """
+    if cfg_id == 1:
+        return make_prefill_workload(101, [0, 21, 40], [7, 30, 1], 4, 2, 64, 16, "f16", 1e4,
+                                     spare_blocks=3, name="prefill-tiny")
+    if cfg_id == 2:
+        cached = _rng(102, S_CTX).integers(0, 2048, size=4, endpoint=True)
+        return make_prefill_workload(102, cached, [512] * 4, 32, 8, 128, 16, "bf16", 5e5,
+                                     name="prefill-llama3-8b")
+    if cfg_id == 3:
+        cached = _rng(103, S_CTX).integers(512, 4096, size=32, endpoint=True)
+        return make_prefill_workload(103, cached, [4] * 32, 32, 8, 128, 16, "bf16", 5e5,
+                                     name="spec-decode-4")
+    raise ValueError(f"unknown prefill workload {cfg_id}")
+
+
+def prefill_kv_bytes(wl: dict) -> int:
+    """K+V bytes the per-token reading of a prefill step reads: sum over query tokens of
+    their attended lengths * 2 * Hkv * D * 2 (each token reading its own prefix)."""
+    return int(wl["tok_len"].astype(np.int64).sum()) * 2 * wl["Hkv"] * wl["D"] * 2
+
+
+def prefill_unique_kv_bytes(wl: dict) -> int:
+    """K+V bytes of the distinct rows a prefill step reads: per sequence its
+    cached + chunk tokens, once."""
+    tot = (wl["start_pos"].astype(np.int64) + wl["chunk"]).sum()
+    return int(tot) * 2 * wl["Hkv"] * wl["D"] * 2

@@ -349,4 +349,120 @@ def pin_append_q_is_rotated_input(lib):
             assert _ulps(q_out[b, h], ref).max() <= 1
 
 
+# ------------------------------------------------------------------ chunked prefill
+def _prefill_small():
+    yield W.prefill_config(1)
+    yield W.make_prefill_workload(111, [5, 0, 16], [12, 17, 3], 6, 2, 32, 8, "bf16", 5e5,
+                                  qk_norm=True, spare_blocks=2)
+    yield W.make_prefill_workload(112, [33], [40], 4, 4, 16, 4, "f16", 1e6, spare_blocks=1)
+
+
+def numpy_causal_attention(q, k_pool, v_pool, tables, cu, start, scale, dtype):
+    """Independent float64 dense attention with an explicit causal mask: query token i of
+    sequence b sees key positions t <= start[b] + i."""
+    N, Hq, D = q.shape
+    bs, Hkv = k_pool.shape[1], k_pool.shape[2]
+    G = Hq // Hkv
+    kf = _decode_np(k_pool, dtype)
+    vf = _decode_np(v_pool, dtype)
+    out = np.zeros((N, Hq, D))
+    for b in range(len(start)):
+        T = int(cu[b + 1] - cu[b])
+        if T == 0:
+            continue
+        Ltot = int(start[b]) + T
+        t = np.arange(Ltot)
+        blk = tables[b, t // bs]
+        K = kf[blk, t % bs]            # [Ltot, Hkv, D]
+        V = vf[blk, t % bs]
+        mask = t[None, :] <= (int(start[b]) + np.arange(T))[:, None]   # [T, Ltot]
+        for h in range(Hq):
+            Q = q[cu[b]:cu[b + 1], h].astype(np.float64)               # [T, D]
+            s = (Q @ K[:, h // G, :].T) * float(scale)
+            s = np.where(mask, s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            out[cu[b]:cu[b + 1], h] = (e @ V[:, h // G, :]) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def pin_prefill_brute_force(lib):
+    """Chunked prefill (append then causal attention) against an independent numpy
+    formulation; every new token's V row lands where the table says."""
+    for wl in _prefill_small():
+        q_out, out, kp, vp = oracle.prefill_step(wl, lib=lib)
+        ref = numpy_causal_attention(q_out, kp, vp, wl["tables"], wl["cu_seqlens"],
+                                     wl["start_pos"], wl["scale"], wl["dtype"])
+        np.testing.assert_allclose(out, ref, rtol=2.5e-7, atol=1e-12, err_msg=wl["name"])
+        assert np.all(np.isfinite(out)), "a poisoned slot was read"
+        bs = wl["bs"]
+        for r in range(wl["N"]):
+            b = int(wl["tok_seq"][r])
+            p = int(wl["tok_len"][r]) - 1
+            blk, slot = wl["tables"][b, p // bs], p % bs
+            assert np.array_equal(vp[blk, slot], _codes(wl["v_new"][r], wl["dtype"]))
+
+
+def pin_prefill_one_token_is_decode(lib):
+    """With one new token per sequence, chunked prefill is the decode step bit for bit."""
+    wl = W.make_prefill_workload(113, [0, 7, 31, 64], [1, 1, 1, 1], 8, 2, 32, 16, "f16", 1e4,
+                                 spare_blocks=2)
+    q_p, out_p, kp_p, vp_p = oracle.prefill_step(wl, lib=lib)
+    kp = wl["k_pool"].copy()
+    vp = wl["v_pool"].copy()
+    q_d = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"],
+                           wl["start_pos"], None, None, wl["eps"], wl["theta"], "f16", lib=lib)
+    out_d = oracle.paged_attn_decode(q_d, kp, vp, wl["tables"], wl["start_pos"] + 1,
+                                     wl["scale"], "f16", lib=lib)
+    assert np.array_equal(kp, kp_p) and np.array_equal(vp, vp_p)
+    assert np.array_equal(q_d.view(np.uint32), q_p.view(np.uint32))
+    assert np.array_equal(out_d.view(np.uint32), out_p.view(np.uint32))
+
+
+def pin_prefill_causal(lib):
+    """A query token's output does not depend on the K/V of later tokens of its chunk."""
+    wl = W.make_prefill_workload(114, [9], [20], 4, 2, 32, 8, "bf16", 1e4, spare_blocks=1)
+    _, out0, _, _ = oracle.prefill_step(wl, lib=lib)
+    i = 11
+    wl2 = dict(wl)
+    wl2["k_new"] = wl["k_new"].copy()
+    wl2["v_new"] = wl["v_new"].copy()
+    wl2["k_new"][i + 1:] *= -3.0
+    wl2["v_new"][i + 1:] += 5.0
+    _, out1, _, _ = oracle.prefill_step(wl2, lib=lib)
+    assert np.array_equal(out0[:i + 1].view(np.uint32), out1[:i + 1].view(np.uint32))
+    assert not np.array_equal(out0[i + 1:], out1[i + 1:])
+
+
+def pin_prefill_chunk_split(lib):
+    """One chunk of T tokens equals the same tokens appended and attended in two chunks."""
+    wl = W.make_prefill_workload(115, [6, 0], [23, 17], 4, 2, 32, 8, "f16", 1e4,
+                                 spare_blocks=1)
+    q1, out1, kp1, vp1 = oracle.prefill_step(wl, lib=lib)
+    split = [10, 5]
+    kp = wl["k_pool"].copy()
+    vp = wl["v_pool"].copy()
+    cu = wl["cu_seqlens"]
+    rows_a = np.concatenate([np.arange(cu[b], cu[b] + split[b]) for b in range(2)])
+    rows_b = np.concatenate([np.arange(cu[b] + split[b], cu[b + 1]) for b in range(2)])
+    cu_a = np.array([0, split[0], split[0] + split[1]], dtype=np.int32)
+    rest = wl["chunk"] - np.array(split)
+    cu_b = np.array([0, rest[0], rest[0] + rest[1]], dtype=np.int32)
+    start_b = wl["start_pos"] + np.array(split, dtype=np.int32)
+    qa = oracle.prefill_append(wl["q"][rows_a], wl["k_new"][rows_a], wl["v_new"][rows_a], kp, vp,
+                               wl["tables"], cu_a, wl["start_pos"], None, None, wl["eps"],
+                               wl["theta"], "f16", lib=lib)
+    oa = oracle.paged_attn_prefill(qa, kp, vp, wl["tables"], cu_a, wl["start_pos"], wl["scale"],
+                                   "f16", lib=lib)
+    qb = oracle.prefill_append(wl["q"][rows_b], wl["k_new"][rows_b], wl["v_new"][rows_b], kp, vp,
+                               wl["tables"], cu_b, start_b, None, None, wl["eps"], wl["theta"],
+                               "f16", lib=lib)
+    ob = oracle.paged_attn_prefill(qb, kp, vp, wl["tables"], cu_b, start_b, wl["scale"], "f16",
+                                   lib=lib)
+    assert np.array_equal(kp, kp1) and np.array_equal(vp, vp1)
+    assert np.array_equal(q1[rows_a].view(np.uint32), qa.view(np.uint32))
+    assert np.array_equal(q1[rows_b].view(np.uint32), qb.view(np.uint32))
+    assert np.array_equal(out1[rows_a].view(np.uint32), oa.view(np.uint32))
+    assert np.array_equal(out1[rows_b].view(np.uint32), ob.view(np.uint32))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

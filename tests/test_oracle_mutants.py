@@ -15,6 +15,8 @@ MUTANTS = {
     7: "conversion: ties rounded away from zero",
     8: "RoPE: position off by one",
     9: "attention: one token short",
+    10: "prefill append: positions off by one",
+    11: "prefill attention: a query token does not see itself",
 }
 
 
