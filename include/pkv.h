@@ -198,6 +198,75 @@ int pkv_decode_split_tokens(int B, int num_q_heads, int num_kv_heads, int head_d
 size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
                                   int block_size, int max_context_len, int split_tokens);
 
+/*
+ * pkv_prefill_append — append a chunk of new tokens per sequence (prefill, or several tokens
+ * at a time).
+ *
+ * Page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock: a block of seqLen
+ * tokens (token-major q [seqLen, Hq*D], k / v [seqLen, Hkv*D]) goes into the cache at its
+ * current length startPos, token i at position startPos + i, RoPE at each token's own position;
+ * page "makarna/pkg/kvcache/paged_cache.go", Append: the rows fill the block list from there on.
+ * Token rows of sequence b are cu_seqlens[b] .. cu_seqlens[b+1]-1; token i of them is treated
+ * exactly as pkv_kv_append treats sequence b's new token at position start_pos[b] + i (same
+ * norm, RoPE, codes and pool row); with one token per sequence the two calls store identical bits.
+ *
+ * q_in, q_out (device) float [num_tokens, num_q_heads, head_dim]; q_out may equal q_in
+ * k_in, v_in   (device) float [num_tokens, num_kv_heads, head_dim]
+ * cu_seqlens   (device) int32 [B + 1], non-decreasing, cu_seqlens[0] = 0,
+ *              cu_seqlens[B] = num_tokens
+ * start_pos    (device) int32 [B]: tokens already cached = position of the chunk's first token
+ * Other arguments as for pkv_kv_append. A token whose position or block id is out of range is
+ * not stored (its q_out row is still written). Chunks of different sequences must not share a
+ * pool slot. Errors: as pkv_kv_append, plus num_tokens < 0. B == 0 or num_tokens == 0 is a
+ * no-op.
+ */
+pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float* v_in,
+                              float* q_out, void* k_pool, void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* cu_seqlens, const int32_t* start_pos,
+                              const float* q_norm_w, const float* k_norm_w, float rms_eps,
+                              float rope_theta, int B, int num_tokens, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                              pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_paged_attn_prefill — causal paged attention of a chunk of query tokens per sequence.
+ *
+ * Page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock: after a block of
+ * tokens is appended at startPos the attention covers startPos + seqLen tokens and is causal
+ * from startPos. Query row r = token i of sequence b (rows as in pkv_prefill_append), at
+ * position p = start_pos[b] + i, attends the first p + 1 tokens of sequence b's block list:
+ * out[r][h] is what pkv_paged_attn_decode computes for that row with context length p + 1.
+ * q . k and P . V run on the matrix cores with the query and the weights split into a 16-bit
+ * high part and a 16-bit remainder (about 2^-16 relative); a key tile holding an Inf or NaN
+ * value is multiplied out in float instead.
+ *
+ * q, out       (device) float [num_tokens, num_q_heads, head_dim] (q rotated: pkv_prefill_append)
+ * cu_seqlens, start_pos  (device) as for pkv_prefill_append
+ * max_chunk    host int >= every chunk length (sizes the grid)
+ * max_context_len  host int >= every start_pos[b] + chunk length (keys beyond it are not
+ *              attended)
+ * workspace    (device) at least pkv_prefill_workspace_bytes(...) bytes (NULL when that is 0),
+ *              ZERO-FILLED before its first use: its first ints are counters every call leaves
+ *              zero. Concurrent calls need separate workspaces.
+ * Other arguments as for pkv_paged_attn_decode. Errors: as pkv_paged_attn_decode, plus
+ *   num_tokens, max_chunk or max_context_len < 0; UNSUPPORTED when B * ceil(max_chunk / (16 /
+ *   G)) exceeds 65535. A zero size is a no-op.
+ */
+pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* cu_seqlens, const int32_t* start_pos,
+                                  int max_chunk, int max_context_len, float scale, float* out,
+                                  void* workspace, size_t workspace_bytes, int B, int num_tokens,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                  int64_t num_blocks, pkv_dtype dtype, void* stream);
+
+/* Workspace bytes pkv_paged_attn_prefill needs: 0 when one partition covers every query
+ * tile's keys, otherwise counters and partial results of the partitions. Host only; depends on
+ * the current device's compute-unit count. */
+size_t pkv_prefill_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int max_chunk, int max_context_len);
+
 /* Debug check of the device-array preconditions on HOST copies of the arrays (any may be
  * NULL to skip it): every block id a sequence uses is in [0, num_blocks); positions[b] in
  * [0, max_blocks_per_seq * block_size); context_lens[b] in [1, max_context_len] and covered

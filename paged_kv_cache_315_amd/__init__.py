@@ -17,6 +17,7 @@ from . import _lib
 from ._lib import PKV_BF16, PKV_F16, PkvError
 
 __all__ = ["kv_append", "paged_attn_decode", "decode_step", "decode_workspace_bytes",
+           "prefill_append", "paged_attn_prefill", "prefill_workspace_bytes", "prefill_step",
            "decode_step_workspace_bytes", "append_then_decode", "decode_split_tokens", "validate_tables", "version",
            "PkvError", "pool_dtype_code"]
 
@@ -204,3 +205,88 @@ def validate_tables(block_tables, positions, context_lens, block_size: int, num_
         None if p is None else p.ctypes.data, None if c is None else c.ctypes.data, B,
         block_size, num_blocks, max_context_len)
     _lib.check(st, "pkv_validate_tables")
+
+
+def prefill_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens, start_pos, *,
+                   theta: float, q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None,
+                   dtype=None, stream=None):
+    """Append a chunk of tokens per sequence; returns q_out ([N, Hq, D] float32).
+
+    q_in [N,Hq,D], k_in / v_in [N,Hkv,D] float32 token-major; cu_seqlens [B+1] int32 (rows of
+    sequence b are cu_seqlens[b] .. cu_seqlens[b+1]-1); start_pos [B] int32 (position of the
+    chunk's first token).
+    """
+    torch = _torch()
+    N, Hq, D = q_in.shape
+    Hkv = k_in.shape[1]
+    B = start_pos.shape[0]
+    NB, bs = k_pool.shape[0], k_pool.shape[1]
+    if q_out is None:
+        q_out = torch.empty_like(q_in)
+    f32 = torch.float32
+    args = (
+        _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
+        _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
+        _dev_ptr(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1),
+        _dev_ptr(start_pos, "start_pos", dtype=torch.int32, ndim=1),
+        _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
+        float(eps), float(theta), B, N, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
+        _stream(stream))
+    _lib.check(_lib.load().pkv_prefill_append(*args), "pkv_prefill_append")
+    return q_out
+
+
+def prefill_workspace_bytes(B, Hq, Hkv, D, block_size, max_chunk, max_context_len) -> int:
+    return _lib.load().pkv_prefill_workspace_bytes(B, Hq, Hkv, D, block_size, max_chunk,
+                                                   max_context_len)
+
+
+def paged_attn_prefill(q, k_pool, v_pool, block_tables, cu_seqlens, start_pos, max_chunk: int,
+                       max_context_len: int, scale: float, *, out=None, workspace=None,
+                       dtype=None, stream=None):
+    """Causal attention of a chunk of query tokens per sequence; returns out [N, Hq, D].
+
+    workspace: uint8 GPU tensor of >= prefill_workspace_bytes(...) bytes, zero-filled before
+    its first use; allocated here (zeroed) if None and needed.
+    """
+    torch = _torch()
+    N, Hq, D = q.shape
+    B = start_pos.shape[0]
+    NB, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    need = prefill_workspace_bytes(B, Hq, Hkv, D, bs, max_chunk, max_context_len) \
+        if B and N and max_chunk and max_context_len else 0
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    f32 = torch.float32
+    args = (
+        _dev_ptr(q, "q", dtype=f32, ndim=3), _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
+        _dev_ptr(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1),
+        _dev_ptr(start_pos, "start_pos", dtype=torch.int32, ndim=1), int(max_chunk),
+        int(max_context_len), float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3), ws_ptr,
+        ws_bytes, B, N, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype), _stream(stream))
+    _lib.check(_lib.load().pkv_paged_attn_prefill(*args), "pkv_paged_attn_prefill")
+    return out
+
+
+def prefill_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens, start_pos,
+                 max_chunk: int, max_context_len: int, *, theta: float, scale: float,
+                 q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None, out=None,
+                 workspace=None, dtype=None, stream=None):
+    """pkv_prefill_append then pkv_paged_attn_prefill on the same stream; returns
+    (q_out, out)."""
+    q_out = prefill_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens,
+                           start_pos, theta=theta, q_norm_w=q_norm_w, k_norm_w=k_norm_w,
+                           eps=eps, q_out=q_out, dtype=dtype, stream=stream)
+    out = paged_attn_prefill(q_out, k_pool, v_pool, block_tables, cu_seqlens, start_pos,
+                             max_chunk, max_context_len, scale, out=out, workspace=workspace,
+                             dtype=dtype, stream=stream)
+    return q_out, out

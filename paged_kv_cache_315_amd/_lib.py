@@ -36,6 +36,11 @@ SIGNATURES = {
     "pkv_decode_step_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "pkv_decode_split_tokens": (_I, [_I, _I, _I, _I, _I, _I]),
     "pkv_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "pkv_prefill_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _F, _F,
+                                _I, _I, _I, _I, _I, _I, _I64, _I, _P]),
+    "pkv_paged_attn_prefill": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _F, _P, _P, _SZ,
+                                    _I, _I, _I, _I, _I, _I, _I64, _I, _P]),
+    "pkv_prefill_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "pkv_validate_tables": (_I, [_P, _I, _P, _P, _I, _I, _I64, _I]),
     "pkv_status_string": (ctypes.c_char_p, [_I]),
     "pkv_last_error": (ctypes.c_char_p, []),

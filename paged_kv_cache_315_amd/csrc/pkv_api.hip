@@ -148,6 +148,37 @@ pkv_status check_decode_shape(const char* who, int B, int Hq, int Hkv, int D) {
 
 }  // namespace
 
+// Chunked prefill attention: query tiles per sequence, keys per partition and partitions.
+struct PrefillPlan {
+    int QTmax, P, S;
+    size_t cnt_off, acc_off, ml_off, total;
+};
+
+PrefillPlan prefill_plan(int B, int Hq, int Hkv, int D, int bs, int max_chunk, int max_ctx,
+                         int cus) {
+    PrefillPlan p{};
+    const int QT = pkv::prefill_tile_tokens(Hq / Hkv);
+    p.QTmax = (max_chunk + QT - 1) / QT;
+    const int64_t items = (int64_t)B * p.QTmax * Hkv;
+    // split the keys only as far as needed to give every compute unit a few workgroups
+    const int64_t target = 4LL * cus;
+    int64_t S = items >= target ? 1 : (target + items - 1) / items;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, ((int64_t)max_ctx + 255) / 256));
+    const int64_t cap = max_split_for(bs) / 64 * 64;
+    int64_t P = ((max_ctx + S - 1) / S + 63) / 64 * 64;
+    P = std::max<int64_t>(64, std::min<int64_t>(P, cap));
+    p.P = (int)P;
+    p.S = (int)((max_ctx + P - 1) / P);
+    if (p.S > 1) {
+        const size_t parts = (size_t)items * p.S * 16;
+        p.cnt_off = 0;
+        p.acc_off = align256((size_t)items * sizeof(int));
+        p.ml_off = p.acc_off + align256(parts * D * sizeof(float));
+        p.total = p.ml_off + align256(parts * 2 * sizeof(float));
+    }
+    return p;
+}
+
 extern "C" {
 
 const char* pkv_version(void) { return "0.1.0"; }
@@ -189,6 +220,8 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
     a.v_pool = static_cast<uint16_t*>(v_pool);
     a.tables = block_tables;
     a.positions = positions;
+    a.cu_seqlens = nullptr;
+    a.rows = B;
     a.q_norm_w = q_norm_w;
     a.k_norm_w = k_norm_w;
     a.max_blocks = max_blocks_per_seq;
@@ -424,6 +457,122 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
     const hipError_t e = pkv::launch_decode_balanced(a, s);
     if (e != hipSuccess)
         return fail(PKV_ERR_HIP, "decode_step: launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float* v_in,
+                              float* q_out, void* k_pool, void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* cu_seqlens, const int32_t* start_pos,
+                              const float* q_norm_w, const float* k_norm_w, float rms_eps,
+                              float rope_theta, int B, int num_tokens, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                              pkv_dtype dtype, void* stream) {
+    pkv_status st = check_common("prefill_append", B, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    st = check_rope("prefill_append", rope_theta, q_norm_w, k_norm_w, head_dim);
+    if (st != PKV_OK) return st;
+    if (num_tokens < 0)
+        return fail(PKV_ERR_INVALID_ARG, "prefill_append: num_tokens = %d < 0", num_tokens);
+    if (B == 0 || num_tokens == 0) return PKV_OK;
+    if (!q_in || !k_in || !v_in || !q_out || !k_pool || !v_pool || !block_tables ||
+        !cu_seqlens || !start_pos)
+        return fail(PKV_ERR_INVALID_ARG, "prefill_append: NULL pointer argument");
+    pkv::AppendArgs a;
+    a.q_in = q_in;
+    a.k_in = k_in;
+    a.v_in = v_in;
+    a.q_out = q_out;
+    a.k_pool = static_cast<uint16_t*>(k_pool);
+    a.v_pool = static_cast<uint16_t*>(v_pool);
+    a.tables = block_tables;
+    a.positions = start_pos;
+    a.cu_seqlens = cu_seqlens;
+    a.rows = num_tokens;
+    a.q_norm_w = q_norm_w;
+    a.k_norm_w = k_norm_w;
+    a.max_blocks = max_blocks_per_seq;
+    a.eps = rms_eps;
+    a.theta = rope_theta;
+    a.B = B;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.D = head_dim;
+    a.bs = block_size;
+    a.num_blocks = num_blocks;
+    a.bf16 = dtype == PKV_BF16;
+    const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, "prefill_append: launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+size_t pkv_prefill_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int max_chunk, int max_context_len) {
+    if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_chunk <= 0 || max_context_len <= 0 || num_q_heads % num_kv_heads)
+        return 0;
+    return prefill_plan(B, num_q_heads, num_kv_heads, head_dim, block_size, max_chunk,
+                        max_context_len, device_cus())
+        .total;
+}
+
+pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* cu_seqlens, const int32_t* start_pos,
+                                  int max_chunk, int max_context_len, float scale, float* out,
+                                  void* workspace, size_t workspace_bytes, int B, int num_tokens,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                  int64_t num_blocks, pkv_dtype dtype, void* stream) {
+    pkv_status st = check_common("prefill", B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    st = check_decode_shape("prefill", B, num_q_heads, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if (num_tokens < 0 || max_chunk < 0 || max_context_len < 0)
+        return fail(PKV_ERR_INVALID_ARG,
+                    "prefill: num_tokens=%d, max_chunk=%d, max_context_len=%d must be >= 0",
+                    num_tokens, max_chunk, max_context_len);
+    if (B == 0 || num_tokens == 0 || max_chunk == 0 || max_context_len == 0) return PKV_OK;
+    if (!q || !k_pool || !v_pool || !block_tables || !cu_seqlens || !start_pos || !out)
+        return fail(PKV_ERR_INVALID_ARG, "prefill: NULL pointer argument");
+    const PrefillPlan plan = prefill_plan(B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                          max_chunk, max_context_len, device_cus());
+    if ((int64_t)B * plan.QTmax > kMaxGridDim || (int64_t)plan.S > kMaxGridDim)
+        return fail(PKV_ERR_UNSUPPORTED, "prefill: %d sequences of up to %d tokens: grid too large",
+                    B, max_chunk);
+    if (plan.total > 0 && (workspace == nullptr || workspace_bytes < plan.total))
+        return fail(PKV_ERR_WORKSPACE, "prefill: workspace %zu bytes, need %zu", workspace_bytes,
+                    plan.total);
+    char* ws = static_cast<char*>(workspace);
+    pkv::PrefillArgs a{};
+    a.q = q;
+    a.k_pool = static_cast<const uint16_t*>(k_pool);
+    a.v_pool = static_cast<const uint16_t*>(v_pool);
+    a.tables = block_tables;
+    a.cu_seqlens = cu_seqlens;
+    a.start_pos = start_pos;
+    a.out = out;
+    a.part_acc = plan.total ? reinterpret_cast<float*>(ws + plan.acc_off) : nullptr;
+    a.part_ml = plan.total ? reinterpret_cast<float*>(ws + plan.ml_off) : nullptr;
+    a.counters = plan.total ? reinterpret_cast<int*>(ws + plan.cnt_off) : nullptr;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.scale = scale;
+    a.split_tokens = plan.P;
+    a.S = plan.S;
+    a.QTmax = plan.QTmax;
+    a.B = B;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.D = head_dim;
+    a.bs = block_size;
+    a.num_blocks = num_blocks;
+    a.bf16 = dtype == PKV_BF16;
+    const hipError_t e = pkv::launch_prefill_attn(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, "prefill: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
 

@@ -7,14 +7,18 @@
 namespace pkv {
 
 struct AppendArgs {
-    const float* q_in;
-    const float* k_in;
+    const float* q_in;      // [rows, Hq, D]
+    const float* k_in;      // [rows, Hkv, D]
     const float* v_in;
     float* q_out;
     uint16_t* k_pool;
     uint16_t* v_pool;
     const int32_t* tables;
+    // one token per sequence (cu_seqlens == nullptr): row b is sequence b at positions[b];
+    // chunks: rows cu_seqlens[b] .. cu_seqlens[b+1]-1 are sequence b at positions[b] + i
     const int32_t* positions;
+    const int32_t* cu_seqlens;
+    int rows;
     const float* q_norm_w;  // nullptr: no QK-norm
     const float* k_norm_w;
     int max_blocks;
@@ -26,6 +30,33 @@ struct AppendArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
+// Causal paged attention of chunks of query tokens (prefill_attn.hip).
+struct PrefillArgs {
+    const float* q;            // [N, Hq, D] rotated queries, token-major
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* tables;
+    const int32_t* cu_seqlens;  // [B + 1]
+    const int32_t* start_pos;   // [B]
+    float* out;                 // [N, Hq, D]
+    float* part_acc;            // [B * QTmax * Hkv, S, 16, D]
+    float* part_ml;             // [B * QTmax * Hkv, S, 16, 2]
+    int* counters;              // [B * QTmax * Hkv], zero between calls
+    int max_blocks;
+    int max_context_len;        // keys beyond it are not attended
+    float scale;
+    int split_tokens;           // keys per partition
+    int S;                      // partitions per query tile
+    int QTmax;                  // query tiles per sequence = ceil(max_chunk / QT)
+    int B, Hq, Hkv, D, bs;
+    int64_t num_blocks;
+    bool bf16;
+};
+
+// Query tokens per tile (16 MFMA rows of G heads each).
+int prefill_tile_tokens(int G);
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
     const float* q;

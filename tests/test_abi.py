@@ -76,6 +76,43 @@ def test_decode_argument_checks(lib, kw, status):
     assert _decode(lib, **kw) == status
 
 
+def _prefill_append(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qo=FAKE, kp=FAKE, vp=FAKE, t=FAKE, mb=4, cu=FAKE, st=FAKE,
+             qn=None, kn=None, eps=1e-6, theta=1e4, B=2, N=5, Hq=4, Hkv=2, D=64, bs=16, nb=16,
+             dt=1, s=None)
+    a.update(kw)
+    return lib.pkv_prefill_append(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), 1), (dict(B=-1), 1), (dict(Hq=5), 1), (dict(theta=0.0), 1),
+    (dict(qn=FAKE), 1), (dict(D=63), 2), (dict(cu=None), 1), (dict(st=None), 1),
+    (dict(N=0, q=None), 0), (dict(B=0, q=None), 0),
+])
+def test_prefill_append_argument_checks(lib, kw, status):
+    assert _prefill_append(lib, **kw) == status
+
+
+def _prefill(lib, **kw):
+    # few query tiles over long contexts: the keys are split, so a case that passed every other
+    # check would stop at the workspace check instead of launching on fake pointers
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, t=FAKE, mb=300, cu=FAKE, st=FAKE, mc=4, mcl=4096,
+             scale=0.125, out=FAKE, ws=None, wsb=0, B=2, N=8, Hq=4, Hkv=2, D=64, bs=16, nb=600,
+             dt=1, s=None)
+    a.update(kw)
+    return lib.pkv_paged_attn_prefill(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), 1), (dict(mc=-1), 1), (dict(mcl=-1), 1), (dict(D=96), 2),
+    (dict(Hq=32, Hkv=2), 2), (dict(cu=None), 1), (dict(out=None), 1), (dict(ws=None), 3),
+    (dict(ws=FAKE, wsb=16), 3), (dict(B=0), 0), (dict(N=0), 0), (dict(mc=0), 0),
+    (dict(B=70000, mc=64), 2),
+])
+def test_prefill_argument_checks(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+
+
 def test_workspace_formula(lib):
     # S = ceil(51 / 64) = 1 -> no partials
     assert lib.pkv_decode_workspace_bytes(2, 4, 2, 64, 16, 51, 64) == 0
