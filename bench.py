@@ -80,6 +80,10 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="pool copies (0: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--workload", choices=["decode", "prefill", "spec"], default="decode",
+                    help="decode: the decode step (default); prefill / spec: chunked prefill "
+                         "(4 x 512-token chunks) / 4 draft tokens per sequence, append + "
+                         "causal paged attention")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -106,6 +110,8 @@ def main() -> int:
                           "bytes_written_per_copy": 1 << 30, "copies": 5}))
         return 0
     pkv._lib.load()  # fail loudly before any work if the HIP library is missing
+    if args.workload != "decode":
+        return run_prefill(args, torch, pkv, W)
 
     wl = W.config(args.config)
     nbytes = algorithmic_bytes(wl)
@@ -222,6 +228,129 @@ def main() -> int:
         },
         "decode_only": {"kernel": "pkv_paged_attn_decode", "avg_launch_us": round(decode_ms * 1e3, 3),
                         "gb_per_s": round(nbytes["decode"] / (decode_ms * 1e-3) / 1e9, 2)},
+        "cpu_baseline": cpu,
+        "wall_ms_timed_steps": round(wall_ms, 2),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def run_prefill(args, torch, pkv, W) -> int:
+    """Chunked-prefill step (pkv_prefill_append + pkv_paged_attn_prefill) on one of the prefill
+    workloads; roofline of the attention kernel: matrix cores for long chunks (prefill), HBM
+    for a few tokens per sequence (spec)."""
+    wl = W.prefill_config(2 if args.workload == "prefill" else 3)
+    dev = torch.device("cuda:0")
+
+    def t(a, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.view(dt))).to(dev)
+
+    q, k_new, v_new = t(wl["q"]), t(wl["k_new"]), t(wl["v_new"])
+    tables, cu, start = t(wl["tables"]), t(wl["cu_seqlens"]), t(wl["start_pos"])
+    pool_bytes = 2 * wl["k_pool"].nbytes
+    copies = args.copies or max(2, int(np.ceil(1.0e9 / pool_bytes)))
+    k0, v0 = t(wl["k_pool"], np.int16), t(wl["v_pool"], np.int16)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    B, N, Hq, Hkv, D, bs = wl["B"], wl["N"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"]
+    need = pkv.prefill_workspace_bytes(B, Hq, Hkv, D, bs, wl["max_chunk"], wl["max_context_len"])
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    q_out = torch.empty_like(q)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def append(i):
+        kp, vp = pools[i % copies]
+        pkv.prefill_append(q, k_new, v_new, kp, vp, tables, cu, start, theta=wl["theta"],
+                           q_out=q_out, dtype=wl["dtype"], stream=stream)
+
+    def attend(i):
+        kp, vp = pools[i % copies]
+        pkv.paged_attn_prefill(q_out, kp, vp, tables, cu, start, wl["max_chunk"],
+                               wl["max_context_len"], wl["scale"], out=out, workspace=ws,
+                               dtype=wl["dtype"], stream=stream)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t0 = time.perf_counter()
+    step_ms = timed(lambda i: (append(i), attend(i)))
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    attn_ms = timed(attend)
+    append_ms = timed(append)
+
+    tok_len = wl["tok_len"].astype(np.int64)
+    flops = 4 * D * Hq * int(tok_len.sum())            # QK^T and PV, 2 flops per MAC
+    uniq = W.prefill_unique_kv_bytes(wl)
+    io = N * Hq * D * 4 * 2 + int(((wl["start_pos"] + wl["chunk"] + bs - 1) // bs).sum()) * 4
+    attn_bytes = uniq + io
+    if args.workload == "prefill":
+        achieved = flops / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "prefill_attn_kernel (pkv_paged_attn_prefill)",
+                "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "flops_per_launch": flops,
+                "avg_launch_us": round(attn_ms * 1e3, 3)}
+        metric = "chunked-prefill causal paged attention TFLOP/s (4 x 512-token chunks)"
+        value, unit = achieved, "TFLOP/s"
+    else:
+        achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "prefill_attn_kernel (pkv_paged_attn_prefill)",
+                "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": attn_bytes, "avg_launch_us": round(attn_ms * 1e3, 3)}
+        metric = "draft-verification paged attention GB/s (32 sequences x 4 tokens)"
+        value, unit = achieved, "GB/s"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.load()
+        kp = wl["k_pool"].copy()
+        vp = wl["v_pool"].copy()
+        q_ref = oracle.prefill_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"],
+                                      wl["cu_seqlens"], wl["start_pos"], None, None, wl["eps"],
+                                      wl["theta"], wl["dtype"])
+        stride = 16 if args.workload == "prefill" else 1
+        mask = np.zeros(N, dtype=np.uint8)
+        mask[::stride] = 1
+        c0 = time.perf_counter()
+        oracle.paged_attn_prefill(q_ref, kp, vp, wl["tables"], wl["cu_seqlens"],
+                                  wl["start_pos"], wl["scale"], wl["dtype"], row_mask=mask)
+        cpu_s = time.perf_counter() - c0
+        sel = mask.astype(bool)
+        if args.workload == "prefill":
+            cpu_val = 4 * D * Hq * int(tok_len[sel].sum()) / cpu_s / 1e12
+        else:
+            cpu_val = attn_bytes / cpu_s / 1e9
+        cpu = {"value": round(cpu_val, 6), "unit": unit, "cores": 1, "kind": "oracle",
+               "sample": f"causal attention of {int(sel.sum())} of the {N} query tokens "
+                         f"(every {stride}th), {cpu_s:.2f} s single-threaded"}
+
+    line = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl["dtype"], "data": "synthetic",
+        "config": {"workload": wl["name"], "batch": B, "query_tokens": N, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "kv_dtype": wl["dtype"], "max_chunk": wl["max_chunk"],
+                   "max_context_len": wl["max_context_len"], "pool_copies": copies,
+                   "attended_keys": int(tok_len.sum()), "unique_kv_bytes": uniq},
+        "roofline": roof,
+        "append": {"kernel": "pkv_prefill_append", "avg_launch_us": round(append_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "wall_ms_timed_steps": round(wall_ms, 2),
     }
