@@ -298,7 +298,7 @@ def run_prefill(args, torch, pkv, W) -> int:
     attn_bytes = uniq + io
     if args.workload == "prefill":
         achieved = flops / (attn_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "prefill_attn_kernel (pkv_paged_attn_prefill)",
+        roof = {"bound": "mfma", "kernel": "prefill_attn_shared_kernel (pkv_paged_attn_prefill)",
                 "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": None, "flops_per_launch": flops,

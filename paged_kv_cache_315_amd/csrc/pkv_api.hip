@@ -151,6 +151,7 @@ pkv_status check_decode_shape(const char* who, int B, int Hq, int Hkv, int D) {
 // Chunked prefill attention: query tiles per sequence, keys per partition and partitions.
 struct PrefillPlan {
     int QTmax, P, S;
+    bool shared;   // 4 query tiles per workgroup sharing each K/V tile (no key split)
     size_t cnt_off, acc_off, ml_off, total;
 };
 
@@ -160,6 +161,14 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int D, int bs, int max_chunk, i
     const int QT = pkv::prefill_tile_tokens(Hq / Hkv);
     p.QTmax = (max_chunk + QT - 1) / QT;
     const int64_t items = (int64_t)B * p.QTmax * Hkv;
+    // long chunks: workgroups of 4 query tiles sharing the K/V tiles, when there are enough of
+    // them to fill the device twice over
+    if (p.QTmax >= 4 && (int64_t)B * ((p.QTmax + 3) / 4) * Hkv >= 2LL * cus) {
+        p.shared = true;
+        p.S = 1;
+        p.P = 0;
+        return p;
+    }
     // split the keys only as far as needed to give every compute unit a few workgroups
     const int64_t target = 4LL * cus;
     int64_t S = items >= target ? 1 : (target + items - 1) / items;
@@ -570,6 +579,7 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
     a.bs = block_size;
     a.num_blocks = num_blocks;
     a.bf16 = dtype == PKV_BF16;
+    a.shared_tiles = plan.shared;
     const hipError_t e = pkv::launch_prefill_attn(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(PKV_ERR_HIP, "prefill: launch failed: %s", hipGetErrorString(e));

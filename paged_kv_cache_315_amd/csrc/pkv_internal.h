@@ -52,6 +52,7 @@ struct PrefillArgs {
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
     bool bf16;
+    bool shared_tiles;          // 4 query tiles per workgroup sharing each K/V tile (S == 1)
 };
 
 // Query tokens per tile (16 MFMA rows of G heads each).

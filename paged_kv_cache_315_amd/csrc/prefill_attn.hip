@@ -421,10 +421,289 @@ void prefill_attn_kernel(PrefillArgs a) {
     if (threadIdx.x == 0) store_shared(counter, 0);  // ready for the next call
 }
 
+// Long chunks: a workgroup takes 4 consecutive query tiles of one sequence and KV head (wave w
+// owns tile 4k + w and all of its keys), and the K/V rows of 64 keys at a time are loaded once
+// into LDS (double-buffered: the next 64 keys' loads are in flight while these are used) for
+// the 4 waves; V is stored transposed ([dim][key]) so a PV operand is one 8-byte read, and a
+// 16-key group holding an Inf / NaN V code is flagged while it is stored. Each wave keeps its
+// own rows' running max / sum / output and writes them at the end; a wave whose tokens all lie
+// before a 16-key group skips its arithmetic. Grid (Hkv, ceil(QTmax / 4), B).
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void prefill_attn_shared_kernel(PrefillArgs a) {
+    using M = Mma<BF16>;
+    using M16 = Mma16<BF16>;
+    constexpr int NK = D / 32;
+    constexpr int NT = D / 16;
+    constexpr int QT = 16 / G;
+    constexpr int KT = 64;              // keys per LDS stage
+    constexpr int NSUB = KT / kTile;    // 16-key groups per stage
+    constexpr int KS = D + 8;           // LDS row stride of K ([key][dim]), in codes
+    constexpr int VS = KT + 4;          // LDS row stride of V^T ([dim][key]), in codes
+    constexpr int PS = 20;
+    constexpr int CH = KT * D / 8;      // 16-byte chunks of one stage of K (or V)
+    constexpr int PER = (2 * CH + kThreads - 1) / kThreads;   // chunks of K and V per thread
+    static_assert(D % 32 == 0, "tile shape");
+    static_assert(G >= 1 && G <= 8, "GQA group");
+
+    __shared__ __align__(16) uint16_t s_k[2][KT][KS];
+    __shared__ __align__(16) uint16_t s_vt[2][D][VS];
+    __shared__ __align__(16) float s_p[kWaves][16][PS];
+    __shared__ int32_t s_tbl[kTblCap];
+    __shared__ int s_vbad[2][NSUB];     // stage base whose group holds a non-finite V code
+
+    const int g = blockIdx.x;
+    const int b = blockIdx.z;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int Hq = a.Hkv * G;
+
+    const int c0 = a.cu_seqlens[b];
+    const int T = max(0, a.cu_seqlens[b + 1] - c0);
+    const int tok_wg = blockIdx.y * kWaves * QT;          // first token of the workgroup
+    if (tok_wg >= T) return;
+    const int st = a.start_pos[b];
+    const int64_t cap = min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
+    auto limit_of = [&](int tok) -> int {                 // keys token tok may see
+        return (int)max((int64_t)0, min((int64_t)st + tok + 1, cap));
+    };
+    const int tok0 = tok_wg + wave * QT;                  // this wave's first token
+    const int ntok = max(0, min(QT, T - tok0));           // 0: the wave has no tokens
+    const int L_wg = limit_of(min(T, tok_wg + kWaves * QT) - 1);
+    const int L_w = ntok > 0 ? limit_of(tok0 + ntok - 1) : 0;
+    if (threadIdx.x < 2 * NSUB) s_vbad[threadIdx.x / NSUB][threadIdx.x % NSUB] = -1;
+
+    // ---- Q operand of this wave's tile
+    typename M::vec qhi[NK], qlo[NK];
+    float score_fix = 1.f;
+    {
+        const int tq = l16 / G;
+        const bool qok = l16 < QT * G && tq < ntok;
+        const int trow = c0 + min(tok0 + min(tq, max(ntok - 1, 0)), T - 1);
+        const float* qrow = a.q + ((int64_t)trow * Hq + g * G + l16 % G) * D + 8 * q4;
+        const float qs = a.scale * kLog2e;
+        float qv[NK][8];
+        float qmax = 0.f;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * i);
+            const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * i + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                qv[i][j] = qok ? xs[j] * qs : 0.f;
+                qmax = fmaxf(qmax, fabsf(qv[i][j]));
+            }
+        }
+        float qscale = 1.f;
+        if constexpr (!BF16) {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+            if (qmax >= 16384.f && qmax <= 3.0e38f) {
+                const int e = ilogbf(qmax) - 13;
+                qscale = ldexpf(1.f, -e);
+                score_fix = ldexpf(1.f, e);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = qv[i][j] * qscale;
+                const typename M::elem hi = (typename M::elem)x;
+                qhi[i][j] = hi;
+                qlo[i][j] = (typename M::elem)(x - (float)hi);
+            }
+    }
+    int lim[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q4 + r;
+        const int t = row / G;
+        lim[r] = (row < QT * G && t < ntok) ? limit_of(tok0 + t) : 0;
+    }
+
+    float m[4], lsum[4];
+    f32x4 acc[NT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m[r] = -INFINITY;
+        lsum[r] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const BlockDiv bdiv = make_div((uint32_t)a.bs);
+    const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+    const int64_t nb_max = a.num_blocks - 1;
+    const int64_t tok_stride = (int64_t)a.Hkv * D;
+    const int64_t head_off = (int64_t)g * D;
+    const int chunk_keys = (kTblCap - 2) * a.bs / KT * KT;
+
+    for (int c_lo = 0; c_lo < L_wg; c_lo += chunk_keys) {
+        const int c_hi = min(L_wg, c_lo + chunk_keys);
+        const int first_blk = (int)bdiv.div((uint32_t)c_lo);
+        const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
+        __syncthreads();  // previous readers of s_tbl / s_k / s_vt are done
+        for (int i = threadIdx.x; i < n_blk; i += kThreads) {
+            const int64_t id = trow[first_blk + i];
+            s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+        }
+        __syncthreads();
+        auto row_off = [&](int t) -> int64_t {
+            const int j = (int)bdiv.div((uint32_t)t);
+            const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
+            return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
+        };
+        // the K and V rows of one stage, 16 bytes per chunk (chunk c < CH: K, else V); keys
+        // past the chunk of ids clamp to its last key (zeroed when stored)
+        auto load_kv = [&](int base, uint4 (&r)[PER]) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int c = min(threadIdx.x + k * kThreads, 2 * CH - 1);
+                const int cc = c < CH ? c : c - CH;
+                const int key = cc / (D / 8);
+                const int col = cc % (D / 8);
+                const uint16_t* pool = c < CH ? a.k_pool : a.v_pool;
+                r[k] = load_stream(pool + row_off(min(base + key, c_hi - 1)) + 8 * col);
+            }
+        };
+        auto store_kv = [&](int base, const uint4 (&r)[PER], int buf) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int c = threadIdx.x + k * kThreads;
+                if (c < 2 * CH) {
+                    const int cc = c < CH ? c : c - CH;
+                    const int key = cc / (D / 8);
+                    const int col = cc % (D / 8);
+                    const uint4 v = base + key < c_hi ? r[k] : make_uint4(0, 0, 0, 0);
+                    if (c < CH) {
+                        *reinterpret_cast<uint4*>(&s_k[buf][key][8 * col]) = v;
+                    } else {
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            s_vt[buf][8 * col + 2 * j][key] = (uint16_t)(w[j] & 0xFFFFu);
+                            s_vt[buf][8 * col + 2 * j + 1][key] = (uint16_t)(w[j] >> 16);
+                        }
+                        if (any_nonfinite<BF16>(v)) s_vbad[buf][key / kTile] = base;
+                    }
+                }
+            }
+        };
+
+        // one 16-key group (keys base .. base+15, LDS keys kk .. kk+15 of buffer buf)
+        auto compute_group = [&](int base, int kk, int buf, bool vbad) {
+            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                const uint4 kw =
+                    *reinterpret_cast<const uint4*>(&s_k[buf][kk + l16][32 * i + 8 * q4]);
+                const typename M::vec kv = __builtin_bit_cast(typename M::vec, kw);
+                sacc = M::mma(qhi[i], kv, sacc);
+                sacc = M::mma(qlo[i], kv, sacc);
+            }
+            const int key = base + l16;
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sc = key < lim[r] ? sacc[r] * score_fix : -INFINITY;
+                const float tmax = row16_max(sc);
+                const float m_new = fmaxf(m[r], tmax);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = exp2f(m[r] - m_use);
+                p[r] = exp2f(sc - m_use);
+                lsum[r] = fmaf(lsum[r], alpha, p[r]);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[n][r] *= alpha;
+                m[r] = m_new;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_p[wave][4 * q4 + r][l16] = p[r];
+            wave_lds_sync();
+            if (!vbad) {
+                const float4 pr = *reinterpret_cast<const float4*>(&s_p[wave][l16][4 * q4]);
+                const float pf[4] = {pr.x, pr.y, pr.z, pr.w};
+                typename M16::vec phi, plo;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const typename M16::elem h = (typename M16::elem)pf[j];
+                    phi[j] = h;
+                    plo[j] = (typename M16::elem)(pf[j] - (float)h);
+                }
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    // B = V keys kk + 4*q4 .. +3 of dim 16*n + l16: one 8-byte read of V^T
+                    const uint2 vw =
+                        *reinterpret_cast<const uint2*>(&s_vt[buf][16 * n + l16][kk + 4 * q4]);
+                    const typename M16::vec vb = __builtin_bit_cast(typename M16::vec, vw);
+                    acc[n] = M16::mma(phi, vb, acc[n]);
+                    acc[n] = M16::mma(plo, vb, acc[n]);
+                }
+            } else {
+                // exact float products for a group with Inf / NaN values
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * q4 + r;
+                    for (int k = 0; k < kTile; ++k) {
+                        if (base + k >= lim[r]) continue;
+                        const float pk = s_p[wave][row][k];
+#pragma unroll
+                        for (int n = 0; n < NT; ++n)
+                            acc[n][r] = fmaf(pk, code_to_float<BF16>(s_vt[buf][16 * n + l16][kk + k]),
+                                             acc[n][r]);
+                    }
+                }
+            }
+            wave_lds_sync();
+        };
+
+        uint4 regs[PER];
+        load_kv(c_lo, regs);
+        store_kv(c_lo, regs, 0);
+        __syncthreads();
+        int buf = 0;
+        for (int base = c_lo; base < c_hi; base += KT) {
+            const bool more = base + KT < c_hi;
+            if (more) load_kv(base + KT, regs);
+#pragma unroll
+            for (int sg = 0; sg < NSUB; ++sg) {
+                const int gb = base + sg * kTile;
+                if (gb < L_w) compute_group(gb, sg * kTile, buf, s_vbad[buf][sg] == base);
+            }
+            if (more) store_kv(base + KT, regs, buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    // ---- this wave's rows: out = acc / l
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q4 + r;
+        const int t = row / G;
+        if (row < QT * G && t < ntok) {
+            float* o = a.out + ((int64_t)(c0 + tok0 + t) * Hq + g * G + row % G) * D;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[16 * n + l16] = acc[n][r] / lsum[r];
+        }
+    }
+}
+
 template <int D, int G, bool BF16>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-    dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)((int64_t)a.B * a.QTmax));
-    hipLaunchKernelGGL((prefill_attn_kernel<D, G, BF16>), grid, dim3(kThreads), 0, stream, a);
+    if (a.shared_tiles) {
+        dim3 grid((unsigned)a.Hkv, (unsigned)((a.QTmax + kWaves - 1) / kWaves), (unsigned)a.B);
+        hipLaunchKernelGGL((prefill_attn_shared_kernel<D, G, BF16>), grid, dim3(kThreads), 0,
+                           stream, a);
+    } else {
+        dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)((int64_t)a.B * a.QTmax));
+        hipLaunchKernelGGL((prefill_attn_kernel<D, G, BF16>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -92,15 +92,26 @@ def test_prefill_shapes(shape):
     _check(wl, f"shape {shape}")
 
 
+def test_prefill_shared_tiles_long_chunks():
+    """Many query tiles (the shared-tile kernel: 4 tiles per workgroup, one K/V tile in LDS for
+    all four), chunks longer than one table-id stage at block size 1, fp16."""
+    wl = W.make_prefill_workload(223, [0, 700, 1500, 5] * 4, [400, 300, 77, 1200] * 4, 8, 2, 64,
+                                 1, "f16", 1e4, spare_blocks=1)
+    _check(wl, "shared tiles, bs 1", row_stride=7)
+
+
 def test_prefill_nonfinite_values():
     """Inf / NaN in new K/V rows: rows before them are untouched, rows after match the oracle
     (the V tile with a non-finite code takes the exact float product)."""
-    wl = W.make_prefill_workload(220, [20], [40], 8, 2, 64, 16, "f16", 1e4, spare_blocks=1)
-    wl["v_new"][25, 1, 3] = np.inf
-    wl["v_new"][31, 0, 7] = -np.inf
-    wl["k_new"][35, 1, 0] = np.nan
-    dev, out = _check(wl, "non-finite K/V", finite=False)
-    assert np.isfinite(out[:25]).all()
+    for cached, chunk, wid in (([20], [40], 220), ([20] * 64, [40] * 64, 224)):
+        # one sequence: the key-splitting kernel; 128 sequences: the shared-tile kernel
+        wl = W.make_prefill_workload(wid, cached, chunk, 8, 2, 64, 16, "f16", 1e4, spare_blocks=1)
+        wl["v_new"][25, 1, 3] = np.inf
+        wl["v_new"][31, 0, 7] = -np.inf
+        wl["k_new"][35, 1, 0] = np.nan
+        dev, out = _check(wl, f"non-finite K/V ({len(cached)} sequences)", finite=False)
+        assert np.isfinite(out[:25]).all()
+        assert np.isfinite(out[40:]).all()
 
 
 def test_prefill_one_token_matches_decode():
