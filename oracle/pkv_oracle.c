@@ -30,6 +30,9 @@
  *             - forward_layer, CPU attention path: query head h reads KV head h divided by the
  *               group size; scores are scaled dot products, exponentials are taken after
  *               subtracting the maximum, normalised by their sum, and weight the value rows.
+ *             - forward_layer, RoPE step: a per-layer rotary dimension (partial rotary);
+ *               CPU path: per-head V normalisation in float (v_norm_per_head); the KV cache as a
+ *               ring of cache_seq slots from which the last min(total, cache_seq) tokens are read.
  *
  * Readings where the pages are silent (each one is listed with its reason in the design notes):
  *   R-ROPE   rotate-half pairing (i, i + D/2), angle pos * theta^(-2i/D), all in double,
@@ -37,6 +40,10 @@
  *   R-NORM   y = x / sqrt(mean(x^2) + eps) * w per head vector, double internals.
  *   R-BF16NAN  NaN inputs to the bf16 rule keep the sign and the 7 leading payload bits,
  *            forced non-zero (the fp16 rule's NaN treatment carried to bf16 width).
+ *   R-PART   partial rotary (rope_dim < D): rotate-half pairs (i, i + rope_dim/2) inside the first
+ *            rope_dim dims, angle pos * theta^(-2i/rope_dim); dims from rope_dim on unchanged.
+ *   R-WIN    sliding window W: a query at attended length L sees positions max(0, L - W) .. L - 1
+ *            (the last W tokens, the ring's read range without its storage reuse).
  *   R-NAN    a NaN that the norm / RoPE arithmetic produces is the canonical quiet NaN
  *            0x7FC00000 (IEEE 754 leaves the sign and payload of such a NaN to the
  *            implementation); a NaN that reaches the converter untouched (V) keeps its bits.
@@ -227,11 +234,14 @@ static float canonical_nan_if_nan(float v)
     return v;
 }
 
-void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
+/* Partial rotary (R-PART): the first rope_dim dims rotate as a rope_dim-sized head; the rest
+ * are copied unchanged. rope_dim = D is the full rotation. */
+void pkvo_rope_head_partial(const float* x, int D, int rope_dim, int pos, float theta, float* y)
 {
-    const int half = D / 2;
+    const int half = rope_dim / 2;
+    const double span = MUT(12) ? (double)D : (double)rope_dim;
     for (int i = 0; i < half; ++i) {
-        const double inv_freq = pow((double)theta, -((MUT(2) ? 1.0 : 2.0) * (double)i) / (double)D);
+        const double inv_freq = pow((double)theta, -((MUT(2) ? 1.0 : 2.0) * (double)i) / span);
         const double angle = (double)(pos + (MUT(8) ? 1 : 0)) * inv_freq;
         const double c = cos(angle);
         const double s = sin(angle);
@@ -240,6 +250,36 @@ void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
         y[i] = canonical_nan_if_nan((float)(MUT(1) ? x0 * c + x1 * s : x0 * c - x1 * s));
         y[i + half] = canonical_nan_if_nan((float)(x1 * c + x0 * s));
     }
+    for (int j = 2 * half; j < D; ++j)
+        y[j] = x[j];
+}
+
+void pkvo_rope_head(const float* x, int D, int pos, float theta, float* y)
+{
+    pkvo_rope_head_partial(x, D, D, pos, theta, y);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Per-head V normalisation. [GL-FWD] forward_layer, CPU path (v_norm_per_head): for each KV
+ * head, the sum of squares is accumulated in float in index order, rms = sqrt(sum * (1/D) +
+ * eps) in float, and every element is multiplied by the float reciprocal of rms. The page fixes
+ * float arithmetic here, so the oracle keeps float (single rounding per operation, no fused
+ * multiply-add).
+ * Pinned by: the constant-vector closed form, the unit-mean-square property, and the
+ * reduction to a plain copy when the rows already have unit mean square and eps = 0.
+ * ------------------------------------------------------------------------------------------ */
+void pkvo_vnorm_head(const float* v, int D, float eps, float* y)
+{
+    float sumsq = 0.0f;
+    for (int j = 0; j < D; ++j) {
+        const float sq = v[j] * v[j];
+        sumsq = sumsq + sq;
+    }
+    const float inv_d = 1.0f / (float)D;
+    const float rms = sqrtf(sumsq * inv_d + (MUT(13) ? 0.0f : eps));
+    const float scale = 1.0f / rms;
+    for (int j = 0; j < D; ++j)
+        y[j] = v[j] * scale;
 }
 
 /* Pool element offset of (block, slot, kv head, dim) in a [num_blocks, bs, Hkv, D] pool
@@ -256,8 +296,8 @@ static int64_t pool_offset(int64_t blk, int slot, int g, int d, int bs, int Hkv,
 static int append_token(const float* q_in, const float* k_in, const float* v_in, float* q_out,
                         uint16_t* k_pool, uint16_t* v_pool, const int32_t* table_row,
                         int max_blocks, int pos, const float* q_norm_w, const float* k_norm_w,
-                        float eps, float theta, int Hq, int Hkv, int D, int bs,
-                        int64_t num_blocks, int dtype, float* tmp, float* rot)
+                        float eps, float theta, int rope_dim, int v_norm, int Hq, int Hkv, int D,
+                        int bs, int64_t num_blocks, int dtype, float* tmp, float* rot)
 {
     if (pos < 0 || pos / bs >= max_blocks)
         return PKVO_ERR_RANGE;
@@ -273,7 +313,7 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
             pkvo_rmsnorm_head(x, q_norm_w, eps, D, tmp);
             src = tmp;
         }
-        pkvo_rope_head(src, D, pos, theta, q_out + (int64_t)h * D);
+        pkvo_rope_head_partial(src, D, rope_dim, pos, theta, q_out + (int64_t)h * D);
     }
     /* K: optional norm, RoPE, convert, store. V: convert, store. */
     for (int g = 0; g < Hkv; ++g) {
@@ -283,8 +323,12 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
             pkvo_rmsnorm_head(x, k_norm_w, eps, D, tmp);
             src = tmp;
         }
-        pkvo_rope_head(src, D, pos, theta, rot);
+        pkvo_rope_head_partial(src, D, rope_dim, pos, theta, rot);
         const float* v = v_in + (int64_t)g * D;
+        if (v_norm) {
+            pkvo_vnorm_head(v, D, eps, tmp);
+            v = tmp;
+        }
         for (int d = 0; d < D; ++d) {
             const int64_t o = pool_offset(blk, slot, g, d, bs, Hkv, D);
             k_pool[o] = encode(rot[d], dtype);
@@ -307,13 +351,15 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
  * Outputs: q_out [B,Hq,D] f32 (normed, rotated), the new rows of k_pool / v_pool.
  * Returns PKVO_ERR_RANGE (and writes nothing more) if a position or block id is out of range.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                   uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
-                   const int32_t* positions, const float* q_norm_w, const float* k_norm_w,
-                   float eps, float theta, int B, int Hq, int Hkv, int D, int bs,
-                   int64_t num_blocks, int dtype)
+int pkvo_kv_append_v(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                     uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                     const int32_t* positions, const float* q_norm_w, const float* k_norm_w,
+                     float eps, float theta, int rope_dim, int v_norm, int B, int Hq, int Hkv,
+                     int D, int bs, int64_t num_blocks, int dtype)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (D & 1) || bs <= 0 || Hq % Hkv)
+        return PKVO_ERR_ARG;
+    if (rope_dim <= 0 || rope_dim > D || (rope_dim & 1))
         return PKVO_ERR_ARG;
     if ((q_norm_w == NULL) != (k_norm_w == NULL))
         return PKVO_ERR_ARG;
@@ -329,11 +375,22 @@ int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, floa
         status = append_token(q_in + (int64_t)b * Hq * D, k_in + (int64_t)b * Hkv * D,
                               v_in + (int64_t)b * Hkv * D, q_out + (int64_t)b * Hq * D, k_pool,
                               v_pool, tables + (int64_t)b * max_blocks, max_blocks, positions[b],
-                              q_norm_w, k_norm_w, eps, theta, Hq, Hkv, D, bs, num_blocks, dtype,
-                              tmp, rot);
+                              q_norm_w, k_norm_w, eps, theta, rope_dim, v_norm, Hq, Hkv, D, bs,
+                              num_blocks, dtype, tmp, rot);
     free(tmp);
     free(rot);
     return status;
+}
+
+int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                   uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                   const int32_t* positions, const float* q_norm_w, const float* k_norm_w,
+                   float eps, float theta, int B, int Hq, int Hkv, int D, int bs,
+                   int64_t num_blocks, int dtype)
+{
+    return pkvo_kv_append_v(q_in, k_in, v_in, q_out, k_pool, v_pool, tables, max_blocks,
+                            positions, q_norm_w, k_norm_w, eps, theta, D, 0, B, Hq, Hkv, D, bs,
+                            num_blocks, dtype);
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -348,13 +405,16 @@ int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, floa
  * Pinned by: equality with pkvo_kv_append when every sequence has one token, equality of one call
  * with a chunk split over two calls, and the per-token rows stored where the table says.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_prefill_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                        uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
-                        const int32_t* cu_seqlens, const int32_t* start_pos,
-                        const float* q_norm_w, const float* k_norm_w, float eps, float theta,
-                        int B, int Hq, int Hkv, int D, int bs, int64_t num_blocks, int dtype)
+int pkvo_prefill_append_v(const float* q_in, const float* k_in, const float* v_in,
+                          float* q_out, uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables,
+                          int max_blocks, const int32_t* cu_seqlens, const int32_t* start_pos,
+                          const float* q_norm_w, const float* k_norm_w, float eps, float theta,
+                          int rope_dim, int v_norm, int B, int Hq, int Hkv, int D, int bs,
+                          int64_t num_blocks, int dtype)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (D & 1) || bs <= 0 || Hq % Hkv)
+        return PKVO_ERR_ARG;
+    if (rope_dim <= 0 || rope_dim > D || (rope_dim & 1))
         return PKVO_ERR_ARG;
     if ((q_norm_w == NULL) != (k_norm_w == NULL))
         return PKVO_ERR_ARG;
@@ -375,37 +435,53 @@ int pkvo_prefill_append(const float* q_in, const float* k_in, const float* v_in,
             status = append_token(q_in + (int64_t)r * Hq * D, k_in + (int64_t)r * Hkv * D,
                                   v_in + (int64_t)r * Hkv * D, q_out + (int64_t)r * Hq * D,
                                   k_pool, v_pool, tables + (int64_t)b * max_blocks, max_blocks,
-                                  pos, q_norm_w, k_norm_w, eps, theta, Hq, Hkv, D, bs,
-                                  num_blocks, dtype, tmp, rot);
+                                  pos, q_norm_w, k_norm_w, eps, theta, rope_dim, v_norm, Hq, Hkv,
+                                  D, bs, num_blocks, dtype, tmp, rot);
         }
     free(tmp);
     free(rot);
     return status;
 }
 
+int pkvo_prefill_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                        uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                        const int32_t* cu_seqlens, const int32_t* start_pos,
+                        const float* q_norm_w, const float* k_norm_w, float eps, float theta,
+                        int B, int Hq, int Hkv, int D, int bs, int64_t num_blocks, int dtype)
+{
+    return pkvo_prefill_append_v(q_in, k_in, v_in, q_out, k_pool, v_pool, tables, max_blocks,
+                                 cu_seqlens, start_pos, q_norm_w, k_norm_w, eps, theta, D, 0, B,
+                                 Hq, Hkv, D, bs, num_blocks, dtype);
+}
+
 /* Attention of one query token (all Hq heads, q_row [Hq, D]) over the first L tokens of the
  * sequence whose block list is table_row; writes out_row [Hq, D]. kc / vc: scratch of
  * L * Hkv * D floats, e: scratch of L doubles. */
 static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t* v_pool,
-                      const int32_t* table_row, int max_blocks, int L, float scale,
+                      const int32_t* table_row, int max_blocks, int L, int window, float scale,
                       float* out_row, int Hq, int Hkv, int D, int bs, int64_t num_blocks,
                       int dtype, float* kc, float* vc, double* e)
 {
     const int G = Hq / Hkv;
     if (L < 1 || (L + bs - 1) / bs > max_blocks)
         return PKVO_ERR_RANGE;
+    /* R-WIN: the query sees positions lo .. L-1; gathered as tokens 0 .. L-lo-1 */
+    const int lo = window > 0 && L > window ? L - window - (MUT(14) ? 1 : 0) : 0;
+    const int n = L - lo;
     /* gather: token t lives in block table_row[t / bs] at slot t % bs */
-    for (int t = 0; t < L; ++t) {
+    for (int i = 0; i < n; ++i) {
+        const int t = lo + i;
         const int64_t blk = table_row[t / bs];
         if (blk < 0 || blk >= num_blocks)
             return PKVO_ERR_RANGE;
         for (int g = 0; g < Hkv; ++g)
             for (int d = 0; d < D; ++d) {
                 const int64_t o = pool_offset(blk, (t + (MUT(5) ? 1 : 0)) % bs, g, d, bs, Hkv, D);
-                kc[((int64_t)t * Hkv + g) * D + d] = decode(k_pool[o], dtype);
-                vc[((int64_t)t * Hkv + g) * D + d] = decode(v_pool[o], dtype);
+                kc[((int64_t)i * Hkv + g) * D + d] = decode(k_pool[o], dtype);
+                vc[((int64_t)i * Hkv + g) * D + d] = decode(v_pool[o], dtype);
             }
     }
+    L = n;
     for (int h = 0; h < Hq; ++h) {
         const int g = MUT(4) ? h % Hkv : h / G;
         const float* qh = q_row + (int64_t)h * D;
@@ -438,7 +514,7 @@ static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t
  * L = lens[r] tokens, writes out + r*Hq*D (rows with row_mask[r] == 0 are skipped). */
 static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
                        const int32_t* tables, int max_blocks, const int* seq, const int* lens,
-                       float scale, float* out, int n, int Hq, int Hkv, int D, int bs,
+                       int window, float scale, float* out, int n, int Hq, int Hkv, int D, int bs,
                        int64_t num_blocks, int dtype, const uint8_t* row_mask)
 {
     int Lmax = 1;
@@ -453,7 +529,8 @@ static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v
         if (row_mask && !row_mask[r])
             continue;
         status = attend_row(q + (int64_t)r * Hq * D, k_pool, v_pool,
-                            tables + (int64_t)seq[r] * max_blocks, max_blocks, lens[r], scale,
+                            tables + (int64_t)seq[r] * max_blocks, max_blocks, lens[r], window,
+                            scale,
                             out + (int64_t)r * Hq * D, Hq, Hkv, D, bs, num_blocks, dtype, kc, vc,
                             e);
     }
@@ -477,12 +554,12 @@ static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v
  * Pinned by: brute force against an independent numpy formulation, closed forms (L = 1,
  * K = 0, V[t] = t), block-permutation invariance, GQA = MHA with duplicated heads.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                           const int32_t* tables, int max_blocks, const int32_t* context_lens,
-                           float scale, float* out, int B, int Hq, int Hkv, int D, int bs,
-                           int64_t num_blocks, int dtype, const uint8_t* row_mask)
+int pkvo_paged_attn_decode_v(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* tables, int max_blocks, const int32_t* context_lens,
+                             int window, float scale, float* out, int B, int Hq, int Hkv, int D,
+                             int bs, int64_t num_blocks, int dtype, const uint8_t* row_mask)
 {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv)
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv || window < 0)
         return PKVO_ERR_ARG;
     int* seq = (int*)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
     int* lens = (int*)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
@@ -495,11 +572,20 @@ int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_
         seq[b] = b;
         lens[b] = context_lens[b] - (MUT(9) && context_lens[b] > 1 ? 1 : 0);
     }
-    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, scale, out,
-                                   B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
+    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, window,
+                                   scale, out, B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
     free(seq);
     free(lens);
     return status;
+}
+
+int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                           const int32_t* tables, int max_blocks, const int32_t* context_lens,
+                           float scale, float* out, int B, int Hq, int Hkv, int D, int bs,
+                           int64_t num_blocks, int dtype, const uint8_t* row_mask)
+{
+    return pkvo_paged_attn_decode_v(q, k_pool, v_pool, tables, max_blocks, context_lens, 0,
+                                    scale, out, B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -515,13 +601,13 @@ int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_
  * numpy formulation with an explicit causal mask, insensitivity of each row to the K/V of later
  * positions, and equality of one call with a chunk split over two calls.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_paged_attn_prefill(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                            const int32_t* tables, int max_blocks, const int32_t* cu_seqlens,
-                            const int32_t* start_pos, float scale, float* out, int B, int Hq,
-                            int Hkv, int D, int bs, int64_t num_blocks, int dtype,
-                            const uint8_t* row_mask)
+int pkvo_paged_attn_prefill_v(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* tables, int max_blocks, const int32_t* cu_seqlens,
+                              const int32_t* start_pos, int window, float scale, float* out,
+                              int B, int Hq, int Hkv, int D, int bs, int64_t num_blocks,
+                              int dtype, const uint8_t* row_mask)
 {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv)
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv || window < 0)
         return PKVO_ERR_ARG;
     const int n = B > 0 ? cu_seqlens[B] : 0;
     for (int b = 0; b < B; ++b)
@@ -540,9 +626,20 @@ int pkvo_paged_attn_prefill(const float* q, const uint16_t* k_pool, const uint16
             /* query token i of the chunk attends positions 0 .. start_pos[b] + i */
             lens[r] = start_pos[b] + (r - cu_seqlens[b]) + (MUT(11) ? 0 : 1);
         }
-    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, scale, out,
-                                   n, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
+    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, window,
+                                   scale, out, n, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
     free(seq);
     free(lens);
     return status;
+}
+
+int pkvo_paged_attn_prefill(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* tables, int max_blocks, const int32_t* cu_seqlens,
+                            const int32_t* start_pos, float scale, float* out, int B, int Hq,
+                            int Hkv, int D, int bs, int64_t num_blocks, int dtype,
+                            const uint8_t* row_mask)
+{
+    return pkvo_paged_attn_prefill_v(q, k_pool, v_pool, tables, max_blocks, cu_seqlens,
+                                     start_pos, 0, scale, out, B, Hq, Hkv, D, bs, num_blocks,
+                                     dtype, row_mask);
 }

@@ -465,4 +465,115 @@ def pin_prefill_chunk_split(lib):
     assert np.array_equal(out1[rows_b].view(np.uint32), ob.view(np.uint32))
 
 
+# ------------------------------------------------------------------ variants: partial rotary,
+# per-head V norm, sliding window
+def pin_partial_rope(lib):
+    """rope_dim = D is the full rotation bit for bit; with rope_dim < D the first rope_dim dims
+    are the complex-form rotation of a rope_dim-sized head and the rest are untouched."""
+    rng = np.random.default_rng(31)
+    for D, rd in ((64, 64), (64, 32), (128, 96), (32, 2)):
+        x = rng.standard_normal(D).astype(np.float32)
+        for pos in (0, 7, 4095):
+            full = oracle.rope_head(x, pos, 1e4, lib)
+            part = oracle.rope_head(x, pos, 1e4, lib, rope_dim=rd)
+            if rd == D:
+                assert np.array_equal(full.view(np.uint32), part.view(np.uint32))
+            assert np.array_equal(part[rd:].view(np.uint32), x[rd:].view(np.uint32))
+            ref = _rope_complex(x[:rd], pos, 1e4)
+            assert _ulps(part[:rd], ref).max() <= 1, (D, rd, pos)
+
+
+def pin_vnorm_closed_forms(lib):
+    """Per-head V norm: a constant row c gives c / sqrt(c^2 + eps) (exactly +-1 for eps = 0
+    and a power-of-two c); the output's mean square is m / (m + eps)."""
+    for c in (0.25, -4.0, 1.0):
+        y = oracle.vnorm_head(np.full(64, c, np.float32), 0.0, lib)
+        assert np.all(y == np.float32(np.sign(c)))
+    for c, eps in ((0.01, 1e-4), (3.0, 1e-6), (-0.5, 0.25)):
+        y = oracle.vnorm_head(np.full(48, c, np.float32), eps, lib)
+        ref = c / np.sqrt(np.float64(c) ** 2 + eps)
+        assert np.allclose(y, ref, rtol=4e-7, atol=0), (c, eps, y[0], ref)
+    v = np.random.default_rng(32).standard_normal(128).astype(np.float32)
+    eps = 0.3
+    y = oracle.vnorm_head(v, eps, lib).astype(np.float64)
+    m = np.mean(v.astype(np.float64) ** 2)
+    assert abs(np.mean(y ** 2) - m / (m + eps)) < 1e-5
+
+
+def pin_vnorm_append_stores_normed_rows(lib):
+    """Append with the V norm stores the codes of the normed rows (constant rows: +-1)."""
+    wl = W.make_workload(116, [3, 40], 4, 2, 32, 16, "bf16", 1e4, spare_blocks=1)
+    wl["v_new"][:] = np.float32(0.5)
+    wl["v_new"][1, 1] = np.float32(-2.0)
+    kp = wl["k_pool"].copy()
+    vp = wl["v_pool"].copy()
+    oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"], wl["positions"],
+                     None, None, 0.0, wl["theta"], "bf16", lib=lib, v_norm=True)
+    for b, p in enumerate(wl["positions"]):
+        row = vp[wl["tables"][b, p // 16], p % 16]
+        for g in range(2):
+            want = np.sign(wl["v_new"][b, g, 0])
+            assert np.all(row[g] == _codes(np.full(32, want, np.float32), "bf16")), (b, g)
+
+
+def _drop_prefix(kp, vp, tables, L, drop, bs, NB):
+    """A one-sequence pool/table holding tokens drop .. L-1 of sequence 0 at positions
+    0 .. L-drop-1 (rows copied, fresh blocks)."""
+    n = L - drop
+    nb = (n + bs - 1) // bs
+    k2 = np.full((nb,) + kp.shape[1:], W.POISON["bf16"], np.uint16)
+    v2 = k2.copy()
+    for i in range(n):
+        t = drop + i
+        k2[i // bs, i % bs] = kp[tables[0, t // bs], t % bs]
+        v2[i // bs, i % bs] = vp[tables[0, t // bs], t % bs]
+    return k2, v2, np.arange(nb, dtype=np.int32)[None, :]
+
+
+def pin_window_is_dropped_prefix(lib):
+    """Sliding window W over L tokens equals plain attention over the last W tokens moved to a
+    sequence of their own; a window of at least L changes nothing."""
+    wl = W.make_workload(117, [70], 4, 2, 32, 8, "bf16", 1e4, spare_blocks=1)
+    q, kp, vp = _appended(wl, lib)
+    L = int(wl["context_lens"][0])
+    full = oracle.paged_attn_decode(q, kp, vp, wl["tables"], wl["context_lens"], wl["scale"],
+                                    "bf16", lib=lib)
+    big = oracle.paged_attn_decode(q, kp, vp, wl["tables"], wl["context_lens"], wl["scale"],
+                                   "bf16", lib=lib, window=L)
+    assert np.array_equal(full.view(np.uint32), big.view(np.uint32))
+    for Wn in (1, 9, 33):
+        win = oracle.paged_attn_decode(q, kp, vp, wl["tables"], wl["context_lens"], wl["scale"],
+                                       "bf16", lib=lib, window=Wn)
+        k2, v2, t2 = _drop_prefix(kp, vp, wl["tables"], L, L - Wn, 8, wl["num_blocks"])
+        ref = oracle.paged_attn_decode(q, k2, v2, t2, np.array([Wn], np.int32), wl["scale"],
+                                       "bf16", lib=lib)
+        assert np.array_equal(win.view(np.uint32), ref.view(np.uint32)), Wn
+
+
+def pin_prefill_window_numpy(lib):
+    """Chunked prefill with a sliding window against an independent numpy band mask."""
+    wl = W.make_prefill_workload(118, [30, 3], [25, 40], 4, 2, 32, 8, "f16", 1e4,
+                                 spare_blocks=1)
+    Wn = 17
+    q_out, _, kp, vp = oracle.prefill_step(wl, lib=lib)
+    out = oracle.paged_attn_prefill(q_out, kp, vp, wl["tables"], wl["cu_seqlens"],
+                                    wl["start_pos"], wl["scale"], "f16", lib=lib, window=Wn)
+    N, Hq, D = q_out.shape
+    G = Hq // 2
+    kf = _decode_np(kp, "f16")
+    vf = _decode_np(vp, "f16")
+    for r in range(N):
+        b = int(wl["tok_seq"][r])
+        L = int(wl["tok_len"][r])
+        t = np.arange(max(0, L - Wn), L)
+        blk = wl["tables"][b, t // 8]
+        for h in range(Hq):
+            K = kf[blk, t % 8, h // G]
+            V = vf[blk, t % 8, h // G]
+            sc = (K @ q_out[r, h].astype(np.float64)) * wl["scale"]
+            e = np.exp(sc - sc.max())
+            ref = (e @ V) / e.sum()
+            np.testing.assert_allclose(out[r, h], ref, rtol=2.5e-7, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -17,6 +17,9 @@ MUTANTS = {
     9: "attention: one token short",
     10: "prefill append: positions off by one",
     11: "prefill attention: a query token does not see itself",
+    12: "partial rotary: frequencies over head_dim instead of rope_dim",
+    13: "V norm: eps dropped",
+    14: "sliding window: one token too many",
 }
 
 
