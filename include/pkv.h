@@ -68,6 +68,35 @@ typedef enum {
 } pkv_dtype;
 
 /*
+ * pkv_variant — layer options of the glia decoder family (page
+ * "soft3/glia/run/arch/decoder/forward.rs", forward_layer), taken by the append, decode and
+ * prefill calls. Passing NULL is the same as {0, 0, 0}: full rotary, no V normalisation, no
+ * window (the Llama-style layer every call describes below).
+ *
+ * rope_dim  rotary dimension: 0 means head_dim; otherwise an even number in [2, head_dim].
+ *           The pairs (i, i + rope_dim/2), i < rope_dim/2, are rotated by the angle
+ *           p * rope_theta^(-2i/rope_dim) (partial rotary: a rope_dim-sized head inside the
+ *           first rope_dim dims); dims rope_dim .. head_dim-1 pass through (after the optional
+ *           QK-norm) unrotated. Used by the append calls (and pkv_decode_step).
+ * v_norm    non-zero: every new V head vector v is stored as v * (1 / sqrt(sum(v^2) / D +
+ *           rms_eps)) with float arithmetic: the sum of squares accumulated in index order, one
+ *           rounding per operation (no fused multiply-add), no weight. Used by the append calls.
+ * window    0 for full attention, else W > 0: a query at position p (attended length L = p + 1)
+ *           sees the positions max(0, L - W) .. L - 1 only — the last W tokens, the range the
+ *           page's ring cache of W slots reads (here the pool keeps every token; only the
+ *           attended range shrinks). Used by the attention calls (and pkv_decode_step).
+ * A NaN that the norm, V-norm or RoPE arithmetic produces is stored as 0x7FC00000 (the
+ * canonical quiet NaN) before conversion; a NaN that reaches the converter untouched keeps its
+ * bits as described under pkv_kv_append.
+ * Errors (INVALID_ARG): rope_dim odd, negative or above head_dim; window < 0.
+ */
+typedef struct {
+    int rope_dim;
+    int v_norm;
+    int window;
+} pkv_variant;
+
+/*
  * pkv_kv_append — write the new token of each of B sequences into the cache.
  *
  * For each sequence b, with p = positions[b] (the number of tokens already cached, which is
@@ -93,8 +122,11 @@ typedef enum {
  * q_norm_w, k_norm_w (device) float [head_dim] each, or both NULL for no QK-norm
  * rms_eps      used only with the norm weights
  * rope_theta   RoPE base, > 0
+ * variant      (host) NULL, or rope_dim / v_norm as described under pkv_variant (window is not
+ *              used here)
  * Errors: INVALID_ARG for a NULL required pointer, B < 0, a non-positive size, Hq % Hkv != 0,
- *   rope_theta <= 0 or not finite, exactly one norm weight NULL, an unknown dtype;
+ *   rope_theta <= 0 or not finite, exactly one norm weight NULL, an unknown dtype, an invalid
+ *   variant;
  *   UNSUPPORTED for an odd head_dim or head_dim > 256 (the limits of the fused RoPE path).
  *   B == 0 is a no-op.
  */
@@ -103,7 +135,8 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
                          int max_blocks_per_seq, const int32_t* positions, const float* q_norm_w,
                          const float* k_norm_w, float rms_eps, float rope_theta, int B,
                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                         int64_t num_blocks, pkv_dtype dtype, void* stream);
+                         int64_t num_blocks, pkv_dtype dtype, const pkv_variant* variant,
+                         void* stream);
 
 /*
  * pkv_paged_attn_decode — one query token per sequence against its paged K/V.
@@ -137,6 +170,9 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *              different streams) need separate workspaces.
  * split_tokens 0 for the balanced schedule, or tokens per partition: a positive multiple of
  *              64 of at most 1022 * block_size (a partition stages its block ids in LDS)
+ * variant      (host) NULL, or a window as described under pkv_variant: then only the keys
+ *              max(0, L - window) .. L - 1 are attended (the partitions and tiles start at the
+ *              16-token tile that holds the first of them; the rest of the context is not read)
  * Errors: INVALID_ARG as for pkv_kv_append, plus max_context_len < 0, split_tokens not 0 or a
  *   positive multiple of 64 up to 1022 * block_size; UNSUPPORTED for head_dim not in {32, 64, 128, 256} or a GQA group
  *   num_q_heads / num_kv_heads above 8; WORKSPACE when the workspace is too small.
@@ -148,7 +184,7 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                                  float* out, void* workspace, size_t workspace_bytes,
                                  int split_tokens, int B, int num_q_heads, int num_kv_heads,
                                  int head_dim, int block_size, int64_t num_blocks,
-                                 pkv_dtype dtype, void* stream);
+                                 pkv_dtype dtype, const pkv_variant* variant, void* stream);
 
 /*
  * pkv_decode_step — pkv_kv_append followed by pkv_paged_attn_decode, in one kernel launch.
@@ -163,7 +199,8 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
  * holds a sequence's last tile writes that KV head's new row before streaming it. Batches above
  * 2048 sequences run the append kernel and the partitioned decode instead.
  *
- * Arguments as for pkv_kv_append and pkv_paged_attn_decode; q_out must not alias q_in.
+ * Arguments as for pkv_kv_append and pkv_paged_attn_decode (variant: all three fields apply);
+ * q_out must not alias q_in.
  * workspace: at least pkv_decode_step_workspace_bytes(...) bytes, zero-filled before first use
  * (counters the call leaves zero again). A sequence whose position is outside
  * [0, max_blocks_per_seq * block_size) is skipped (its q_out and out rows are not written).
@@ -177,7 +214,7 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
                            float rope_theta, float scale, float* out, void* workspace,
                            size_t workspace_bytes, int B, int num_q_heads, int num_kv_heads,
                            int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
-                           void* stream);
+                           const pkv_variant* variant, void* stream);
 
 /* Workspace bytes pkv_decode_step needs. Host only. */
 size_t pkv_decode_step_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
@@ -215,10 +252,10 @@ size_t pkv_decode_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int 
  * cu_seqlens   (device) int32 [B + 1], non-decreasing, cu_seqlens[0] = 0,
  *              cu_seqlens[B] = num_tokens
  * start_pos    (device) int32 [B]: tokens already cached = position of the chunk's first token
- * Other arguments as for pkv_kv_append. A token whose position or block id is out of range is
- * not stored (its q_out row is still written). Chunks of different sequences must not share a
- * pool slot. Errors: as pkv_kv_append, plus num_tokens < 0. B == 0 or num_tokens == 0 is a
- * no-op.
+ * Other arguments (variant: rope_dim, v_norm) as for pkv_kv_append. A token whose position or
+ * block id is out of range is not stored (its q_out row is still written). Chunks of different
+ * sequences must not share a pool slot. Errors: as pkv_kv_append, plus num_tokens < 0. B == 0
+ * or num_tokens == 0 is a no-op.
  */
 pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float* v_in,
                               float* q_out, void* k_pool, void* v_pool,
@@ -227,7 +264,7 @@ pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float*
                               const float* q_norm_w, const float* k_norm_w, float rms_eps,
                               float rope_theta, int B, int num_tokens, int num_q_heads,
                               int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-                              pkv_dtype dtype, void* stream);
+                              pkv_dtype dtype, const pkv_variant* variant, void* stream);
 
 /*
  * pkv_paged_attn_prefill — causal paged attention of a chunk of query tokens per sequence.
@@ -249,6 +286,7 @@ pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float*
  * workspace    (device) at least pkv_prefill_workspace_bytes(...) bytes (NULL when that is 0),
  *              ZERO-FILLED before its first use: its first ints are counters every call leaves
  *              zero. Concurrent calls need separate workspaces.
+ * With a window W (variant) the row at position p attends max(0, p + 1 - W) .. p only.
  * Other arguments as for pkv_paged_attn_decode. Errors: as pkv_paged_attn_decode, plus
  *   num_tokens, max_chunk or max_context_len < 0; UNSUPPORTED when B * ceil(max_chunk / (16 /
  *   G)) exceeds 65535. A zero size is a no-op.
@@ -259,7 +297,8 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
                                   int max_chunk, int max_context_len, float scale, float* out,
                                   void* workspace, size_t workspace_bytes, int B, int num_tokens,
                                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                                  int64_t num_blocks, pkv_dtype dtype, void* stream);
+                                  int64_t num_blocks, pkv_dtype dtype, const pkv_variant* variant,
+                                  void* stream);
 
 /* Workspace bytes pkv_paged_attn_prefill needs: 0 when one partition covers every query
  * tile's keys, otherwise counters and partial results of the partitions. Host only; depends on

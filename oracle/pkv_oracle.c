@@ -44,7 +44,7 @@
  *            rope_dim dims, angle pos * theta^(-2i/rope_dim); dims from rope_dim on unchanged.
  *   R-WIN    sliding window W: a query at attended length L sees positions max(0, L - W) .. L - 1
  *            (the last W tokens, the ring's read range without its storage reuse).
- *   R-NAN    a NaN that the norm / RoPE arithmetic produces is the canonical quiet NaN
+ *   R-NAN    a NaN that the norm / V-norm / RoPE arithmetic produces is the canonical quiet NaN
  *            0x7FC00000 (IEEE 754 leaves the sign and payload of such a NaN to the
  *            implementation); a NaN that reaches the converter untouched (V) keeps its bits.
  *
@@ -206,6 +206,15 @@ void pkvo_decode_array(const uint16_t* c, float* out, int64_t n, int dtype)
  * Pinned by: constant-vector closed form, mean(y^2) identity with unit weight, scale invariance,
  * an independent numpy formula (tests/test_oracle_norm_rope.py).
  * ------------------------------------------------------------------------------------------ */
+static float canonical_nan_if_nan(float v)
+{
+    if (isnan(v)) {
+        const uint32_t qnan = 0x7FC00000u;
+        memcpy(&v, &qnan, 4);
+    }
+    return v;
+}
+
 void pkvo_rmsnorm_head(const float* x, const float* w, float eps, int D, float* y)
 {
     double ss = 0.0;
@@ -213,7 +222,7 @@ void pkvo_rmsnorm_head(const float* x, const float* w, float eps, int D, float* 
         ss += (double)x[j] * (double)x[j];
     const double r = 1.0 / sqrt(ss / (double)D + (MUT(3) ? 0.0 : (double)eps));
     for (int j = 0; j < D; ++j)
-        y[j] = (float)(((double)x[j] * r) * (double)w[j]);
+        y[j] = canonical_nan_if_nan((float)(((double)x[j] * r) * (double)w[j]));
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -225,15 +234,6 @@ void pkvo_rmsnorm_head(const float* x, const float* w, float eps, int D, float* 
  * Pinned by: position 0 is the identity bit for bit, norm preservation, the relative-position
  * property, an independent complex-exponential formulation in numpy.
  * ------------------------------------------------------------------------------------------ */
-static float canonical_nan_if_nan(float v)
-{
-    if (isnan(v)) {
-        const uint32_t qnan = 0x7FC00000u;
-        memcpy(&v, &qnan, 4);
-    }
-    return v;
-}
-
 /* Partial rotary (R-PART): the first rope_dim dims rotate as a rope_dim-sized head; the rest
  * are copied unchanged. rope_dim = D is the full rotation. */
 void pkvo_rope_head_partial(const float* x, int D, int rope_dim, int pos, float theta, float* y)
@@ -279,7 +279,7 @@ void pkvo_vnorm_head(const float* v, int D, float eps, float* y)
     const float rms = sqrtf(sumsq * inv_d + (MUT(13) ? 0.0f : eps));
     const float scale = 1.0f / rms;
     for (int j = 0; j < D; ++j)
-        y[j] = v[j] * scale;
+        y[j] = canonical_nan_if_nan(v[j] * scale);
 }
 
 /* Pool element offset of (block, slot, kv head, dim) in a [num_blocks, bs, Hkv, D] pool

@@ -69,11 +69,13 @@ def _stream(stream):
 
 def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, theta: float,
               q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None, dtype=None,
-              stream=None):
+              rope_dim: int = 0, v_norm: bool = False, stream=None):
     """Append one token per sequence; returns q_out ([B, Hq, D] float32, normed + rotated).
 
     q_in [B,Hq,D], k_in / v_in [B,Hkv,D] float32; k_pool / v_pool [NB,bs,Hkv,D] 16-bit;
     block_tables [B,max_blocks] int32; positions [B] int32 (write slot = RoPE position).
+    rope_dim: rotary dims (0 = D; partial rotary below D); v_norm: RMS-normalise each new V
+    head vector before it is stored.
     """
     torch = _torch()
     B, Hq, D = q_in.shape
@@ -90,7 +92,7 @@ def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, thet
         _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
         _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
         float(eps), float(theta), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
-        _stream(stream))
+        _lib.variant(rope_dim, v_norm), _stream(stream))
     _lib.check(_lib.load().pkv_kv_append(*args), "pkv_kv_append")
     return q_out
 
@@ -107,9 +109,10 @@ def decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_context_len,
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
                       scale: float, *, out=None, workspace=None, split_tokens: int = 0,
-                      dtype=None, stream=None):
+                      dtype=None, window: int = 0, stream=None):
     """Decode attention for one query token per sequence; returns out [B, Hq, D] float32.
 
+    window: 0, or W > 0 to attend only the last W of each sequence's context_lens tokens.
     workspace: uint8 GPU tensor of >= decode_workspace_bytes(...) bytes, zero-filled before its
     first use (the library keeps its counters zero); allocated here (zeroed) if None.
     """
@@ -130,7 +133,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
         _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
         _dev_ptr(context_lens, "context_lens", dtype=torch.int32, ndim=1), int(max_context_len),
         float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3), ws_ptr, ws_bytes,
-        int(split_tokens), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype), _stream(stream))
+        int(split_tokens), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
+        _lib.variant(window=window), _stream(stream))
     _lib.check(_lib.load().pkv_paged_attn_decode(*args), "pkv_paged_attn_decode")
     return out
 
@@ -142,9 +146,11 @@ def decode_step_workspace_bytes(B, Hq, Hkv, D, block_size, max_blocks_per_seq) -
 
 def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, theta: float,
                 scale: float, q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None,
-                out=None, workspace=None, dtype=None, stream=None):
+                out=None, workspace=None, dtype=None, rope_dim: int = 0, v_norm: bool = False,
+                window: int = 0, stream=None):
     """One layer's decode step in one launch: append the new token of every sequence, then
     attend over positions + 1 tokens. Returns (q_out, out), both [B, Hq, D] float32.
+    rope_dim / v_norm as for kv_append, window as for paged_attn_decode.
 
     workspace: uint8 GPU tensor of >= decode_step_workspace_bytes(...) bytes, zero-filled before
     its first use; allocated here (zeroed) if None.
@@ -171,7 +177,8 @@ def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, th
         _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
         _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
         float(eps), float(theta), float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3),
-        ws_ptr, ws_bytes, B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype), _stream(stream))
+        ws_ptr, ws_bytes, B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
+        _lib.variant(rope_dim, v_norm, window), _stream(stream))
     _lib.check(_lib.load().pkv_decode_step(*args), "pkv_decode_step")
     return q_out, out
 
@@ -179,14 +186,15 @@ def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, th
 def append_then_decode(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, context_lens,
                        max_context_len: int, *, theta: float, scale: float, q_norm_w=None,
                        k_norm_w=None, eps: float = 1e-6, q_out=None, out=None, workspace=None,
-                       split_tokens: int = 0, dtype=None, stream=None):
+                       split_tokens: int = 0, dtype=None, rope_dim: int = 0,
+                       v_norm: bool = False, window: int = 0, stream=None):
     """The same step as two calls (kv_append, then paged_attn_decode). Returns (q_out, out)."""
     q_out = kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, theta=theta,
                       q_norm_w=q_norm_w, k_norm_w=k_norm_w, eps=eps, q_out=q_out, dtype=dtype,
-                      stream=stream)
+                      rope_dim=rope_dim, v_norm=v_norm, stream=stream)
     out = paged_attn_decode(q_out, k_pool, v_pool, block_tables, context_lens, max_context_len,
                             scale, out=out, workspace=workspace, split_tokens=split_tokens,
-                            dtype=dtype, stream=stream)
+                            dtype=dtype, window=window, stream=stream)
     return q_out, out
 
 
@@ -209,12 +217,12 @@ def validate_tables(block_tables, positions, context_lens, block_size: int, num_
 
 def prefill_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens, start_pos, *,
                    theta: float, q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None,
-                   dtype=None, stream=None):
+                   dtype=None, rope_dim: int = 0, v_norm: bool = False, stream=None):
     """Append a chunk of tokens per sequence; returns q_out ([N, Hq, D] float32).
 
     q_in [N,Hq,D], k_in / v_in [N,Hkv,D] float32 token-major; cu_seqlens [B+1] int32 (rows of
     sequence b are cu_seqlens[b] .. cu_seqlens[b+1]-1); start_pos [B] int32 (position of the
-    chunk's first token).
+    chunk's first token). rope_dim / v_norm as for kv_append.
     """
     torch = _torch()
     N, Hq, D = q_in.shape
@@ -234,7 +242,7 @@ def prefill_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens, s
         _dev_ptr(start_pos, "start_pos", dtype=torch.int32, ndim=1),
         _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
         float(eps), float(theta), B, N, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
-        _stream(stream))
+        _lib.variant(rope_dim, v_norm), _stream(stream))
     _lib.check(_lib.load().pkv_prefill_append(*args), "pkv_prefill_append")
     return q_out
 
@@ -246,8 +254,9 @@ def prefill_workspace_bytes(B, Hq, Hkv, D, block_size, max_chunk, max_context_le
 
 def paged_attn_prefill(q, k_pool, v_pool, block_tables, cu_seqlens, start_pos, max_chunk: int,
                        max_context_len: int, scale: float, *, out=None, workspace=None,
-                       dtype=None, stream=None):
+                       dtype=None, window: int = 0, stream=None):
     """Causal attention of a chunk of query tokens per sequence; returns out [N, Hq, D].
+    window: 0, or W > 0 so that the row at position p attends positions p - W + 1 .. p only.
 
     workspace: uint8 GPU tensor of >= prefill_workspace_bytes(...) bytes, zero-filled before
     its first use; allocated here (zeroed) if None and needed.
@@ -272,7 +281,8 @@ def paged_attn_prefill(q, k_pool, v_pool, block_tables, cu_seqlens, start_pos, m
         _dev_ptr(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1),
         _dev_ptr(start_pos, "start_pos", dtype=torch.int32, ndim=1), int(max_chunk),
         int(max_context_len), float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3), ws_ptr,
-        ws_bytes, B, N, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype), _stream(stream))
+        ws_bytes, B, N, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
+        _lib.variant(window=window), _stream(stream))
     _lib.check(_lib.load().pkv_paged_attn_prefill(*args), "pkv_paged_attn_prefill")
     return out
 
@@ -280,13 +290,15 @@ def paged_attn_prefill(q, k_pool, v_pool, block_tables, cu_seqlens, start_pos, m
 def prefill_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens, start_pos,
                  max_chunk: int, max_context_len: int, *, theta: float, scale: float,
                  q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None, out=None,
-                 workspace=None, dtype=None, stream=None):
+                 workspace=None, dtype=None, rope_dim: int = 0, v_norm: bool = False,
+                 window: int = 0, stream=None):
     """pkv_prefill_append then pkv_paged_attn_prefill on the same stream; returns
     (q_out, out)."""
     q_out = prefill_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens,
                            start_pos, theta=theta, q_norm_w=q_norm_w, k_norm_w=k_norm_w,
-                           eps=eps, q_out=q_out, dtype=dtype, stream=stream)
+                           eps=eps, q_out=q_out, dtype=dtype, rope_dim=rope_dim, v_norm=v_norm,
+                           stream=stream)
     out = paged_attn_prefill(q_out, k_pool, v_pool, block_tables, cu_seqlens, start_pos,
                              max_chunk, max_context_len, scale, out=out, workspace=workspace,
-                             dtype=dtype, stream=stream)
+                             dtype=dtype, window=window, stream=stream)
     return q_out, out

@@ -20,7 +20,15 @@ PKV_ERR_HIP = 4
 PKV_F16 = 1
 PKV_BF16 = 2
 
+
+
+class Variant(ctypes.Structure):
+    """pkv_variant: rope_dim (0 = head_dim), v_norm (0/1), window (0 = full attention)."""
+    _fields_ = [("rope_dim", ctypes.c_int), ("v_norm", ctypes.c_int), ("window", ctypes.c_int)]
+
+
 # every function include/pkv.h declares, with (restype, argtypes)
+_V = ctypes.POINTER(Variant)
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _I64 = ctypes.c_int64
@@ -28,18 +36,18 @@ _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 SIGNATURES = {
     "pkv_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _F, _F,
-                           _I, _I, _I, _I, _I, _I64, _I, _P]),
+                           _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_paged_attn_decode": (_I, [_P, _P, _P, _P, _I, _P, _I, _F, _P, _P, _SZ, _I,
-                                   _I, _I, _I, _I, _I, _I64, _I, _P]),
+                                   _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _F, _F, _F, _P, _P, _SZ,
-                             _I, _I, _I, _I, _I, _I64, _I, _P]),
+                             _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_decode_step_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "pkv_decode_split_tokens": (_I, [_I, _I, _I, _I, _I, _I]),
     "pkv_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "pkv_prefill_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _F, _F,
-                                _I, _I, _I, _I, _I, _I, _I64, _I, _P]),
+                                _I, _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_paged_attn_prefill": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _F, _P, _P, _SZ,
-                                    _I, _I, _I, _I, _I, _I, _I64, _I, _P]),
+                                    _I, _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_prefill_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "pkv_validate_tables": (_I, [_P, _I, _P, _P, _I, _I, _I64, _I]),
     "pkv_status_string": (ctypes.c_char_p, [_I]),
@@ -80,3 +88,10 @@ def check(status: int, what: str):
         lib = load()
         msg = lib.pkv_last_error().decode()
         raise PkvError(status, f"{what}: {lib.pkv_status_string(status).decode()}: {msg}")
+
+
+def variant(rope_dim: int = 0, v_norm: bool = False, window: int = 0):
+    """A pkv_variant argument: None (the defaults) or a pointer to the filled struct."""
+    if not rope_dim and not v_norm and not window:
+        return None
+    return ctypes.pointer(Variant(int(rope_dim), int(bool(v_norm)), int(window)))

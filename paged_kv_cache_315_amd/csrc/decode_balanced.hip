@@ -47,69 +47,88 @@ constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 
 // Query rotation of one unit and, for the unit holding a segment's last tile, the new token's
-// K/V row (norm + RoPE in double, round-to-nearest-even codes; see kv_append.hip), stored into
-// the pool before the unit streams its tiles. Expects s_q to hold the raw query heads and s_kx
-// the new K row (written by this thread block, not yet synchronised) and s_inv the angles per
-// position of the rotary pairs; ends with a barrier, after which this workgroup's own loads of
-// the new row see the stored codes.
+// K/V row (norm + RoPE in double over the first rope_dim dims, optional V norm in float,
+// round-to-nearest-even codes; see kv_append.hip), stored into the pool before the unit streams
+// its tiles. Expects s_q to hold the raw query heads and s_kx / s_vx the new K / V rows (written
+// by this thread block, not yet synchronised) and s_inv the angles per position of the rotary
+// pairs; ends with a barrier, after which this workgroup's own loads of the new row see the
+// stored codes.
 template <int D, int G, bool BF16>
 __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, int g, int pnew,
                                                bool owns_new, bool seg_first, float* s_q,
-                                               float* s_kx, const double* s_inv, double* s_cs,
-                                               double* s_r) {
-    constexpr int HALF = D / 2;
+                                               const float* s_kx, const float* s_vx,
+                                               const double* s_inv, double* s_cs, double* s_r,
+                                               float* s_vsc) {
     const int tid = threadIdx.x;
     const int Hkv = a.Hkv;
     const int Hq = Hkv * G;
+    const int rhalf = a.rope_dim >> 1;     // rotary pairs (i, i + rhalf), i < rhalf
     const int64_t tok_stride = (int64_t)Hkv * D;
-    for (int i = tid; i < HALF; i += kThreads)
+    for (int i = tid; i < rhalf; i += kThreads)
         rope_cs_from(pnew, s_inv[i], s_cs[2 * i], s_cs[2 * i + 1]);
-    __syncthreads();
     const bool norm = a.q_norm_w != nullptr;
+    const bool vnorm = a.v_norm && owns_new;
     if (norm) {
         if (tid < G) s_r[tid] = rms_inv(s_q + tid * D, D, a.eps);
         if (tid == G && owns_new) s_r[G] = rms_inv(s_kx, D, a.eps);
-        __syncthreads();
     }
+    if (vnorm && tid == G + 1) *s_vsc = vnorm_scale(s_vx, D, a.eps);
+    __syncthreads();
     float* qo = a.q_out + ((int64_t)b * Hq + g * G) * D;
-    for (int idx = tid; idx < G * HALF; idx += kThreads) {
-        const int h = idx / HALF;
-        const int i = idx % HALF;
-        float x0 = s_q[h * D + i], x1 = s_q[h * D + i + HALF];
+    for (int idx = tid; idx < G * rhalf; idx += kThreads) {
+        const int h = idx / rhalf;
+        const int i = idx - h * rhalf;
+        float x0 = s_q[h * D + i], x1 = s_q[h * D + i + rhalf];
         if (norm) {
             x0 = norm_elem(x0, s_r[h], a.q_norm_w[i]);
-            x1 = norm_elem(x1, s_r[h], a.q_norm_w[i + HALF]);
+            x1 = norm_elem(x1, s_r[h], a.q_norm_w[i + rhalf]);
         }
         float y0, y1;
         rope_rotate(x0, x1, s_cs[2 * i], s_cs[2 * i + 1], y0, y1);
         s_q[h * D + i] = y0;
-        s_q[h * D + i + HALF] = y1;
+        s_q[h * D + i + rhalf] = y1;
         if (seg_first) {
             qo[h * D + i] = y0;
-            qo[h * D + i + HALF] = y1;
+            qo[h * D + i + rhalf] = y1;
         }
     }
+    // partial rotary: the dims from rope_dim on are only normed
+    const int rest = D - a.rope_dim;
+    if (rest > 0)
+        for (int idx = tid; idx < G * rest; idx += kThreads) {
+            const int h = idx / rest;
+            const int j = a.rope_dim + (idx - h * rest);
+            const float y = norm ? norm_elem(s_q[h * D + j], s_r[h], a.q_norm_w[j]) : s_q[h * D + j];
+            s_q[h * D + j] = y;
+            if (seg_first) qo[h * D + j] = y;
+        }
     if (owns_new) {
         int64_t row = -1;
         const int64_t blk = a.tables[(int64_t)b * a.max_blocks + pnew / a.bs];
         if (blk >= 0 && blk < a.num_blocks)
             row = (blk * a.bs + pnew % a.bs) * tok_stride + (int64_t)g * D;
-        for (int i = tid; i < HALF; i += kThreads) {
-            float x0 = s_kx[i], x1 = s_kx[i + HALF];
+        for (int i = tid; i < rhalf; i += kThreads) {
+            float x0 = s_kx[i], x1 = s_kx[i + rhalf];
             if (norm) {
                 x0 = norm_elem(x0, s_r[G], a.k_norm_w[i]);
-                x1 = norm_elem(x1, s_r[G], a.k_norm_w[i + HALF]);
+                x1 = norm_elem(x1, s_r[G], a.k_norm_w[i + rhalf]);
             }
             float y0, y1;
             rope_rotate(x0, x1, s_cs[2 * i], s_cs[2 * i + 1], y0, y1);
             if (row >= 0) {
                 a.k_pool[row + i] = encode16(y0, BF16);
-                a.k_pool[row + i + HALF] = encode16(y1, BF16);
+                a.k_pool[row + i + rhalf] = encode16(y1, BF16);
             }
         }
-        const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
-        if (row >= 0)
-            for (int i = tid; i < D; i += kThreads) a.v_pool[row + i] = encode16(vsrc[i], BF16);
+        if (row >= 0) {
+            for (int j = a.rope_dim + tid; j < D; j += kThreads) {
+                const float y = norm ? norm_elem(s_kx[j], s_r[G], a.k_norm_w[j]) : s_kx[j];
+                a.k_pool[row + j] = encode16(y, BF16);
+            }
+            const float vsc = vnorm ? *s_vsc : 1.f;
+            for (int i = tid; i < D; i += kThreads)
+                a.v_pool[row + i] = encode16(vnorm ? vnorm_elem(s_vx[i], vsc) : s_vx[i], BF16);
+        }
     }
     __syncthreads();
 }
@@ -132,7 +151,9 @@ void decode_balanced_kernel(BalancedArgs a) {
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ __align__(16) float s_q[G][D];
     __shared__ float s_kx[APPEND ? D : 1];
-    __shared__ double s_inv[APPEND ? HALF : 1];  // theta^(-2i/D) of rotary pair i
+    __shared__ float s_vx[APPEND ? D : 1];
+    __shared__ float s_vsc;
+    __shared__ double s_inv[APPEND ? HALF : 1];  // theta^(-2i/rope_dim) of rotary pair i
     __shared__ double s_cs[APPEND ? HALF : 1][2];
     __shared__ double s_r[G + 1];
     __shared__ __align__(16) float s_p[kWaves][kTile][16];
@@ -152,6 +173,9 @@ void decode_balanced_kernel(BalancedArgs a) {
     const int B = a.B;
     const int Hkv = a.Hkv;
     const int Hq = Hkv * G;
+    const int W = a.window;
+    // tiles of a sequence of L tokens: from the one holding its first visible key to the last
+    auto ntiles = [W](int L) { return (L + kTile - 1) / kTile - window_lo(L, W) / kTile; };
 
     // ---- 1. lengths and the tile prefix of every sequence (all heads) -> LDS
     const int64_t cap64 = (int64_t)a.max_blocks * a.bs;
@@ -169,11 +193,12 @@ void decode_balanced_kernel(BalancedArgs a) {
                 L = max(0, min(a.lens[b], cap));
             }
             s_len[b] = L;
-            cnt += (L + kTile - 1) / kTile;
+            cnt += ntiles(L);
         }
     }
     if constexpr (APPEND) {  // while the lengths arrive
-        for (int i = tid; i < HALF; i += kThreads) s_inv[i] = rope_inv_freq(a.theta, i, D);
+        for (int i = tid; i < (a.rope_dim >> 1); i += kThreads)
+            s_inv[i] = rope_inv_freq(a.theta, i, a.rope_dim);
     }
     s_scan[tid] = cnt;
     __syncthreads();
@@ -190,7 +215,7 @@ void decode_balanced_kernel(BalancedArgs a) {
             const int b = tid * kPerThread + k;
             if (b < B) {
                 s_pre[b] = run;
-                run += Hkv * ((s_len[b] + kTile - 1) / kTile);
+                run += Hkv * ntiles(s_len[b]);
             }
         }
         if (tid == kThreads - 1) s_pre[B] = s_scan[tid] * Hkv;
@@ -213,7 +238,7 @@ void decode_balanced_kernel(BalancedArgs a) {
         }
         b = lo;
     }
-    int g = (r0 - s_pre[b]) / ((s_len[b] + kTile - 1) / kTile);
+    int g = (r0 - s_pre[b]) / ntiles(s_len[b]);
 
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
     const int64_t nb_max = a.num_blocks - 1;
@@ -225,12 +250,14 @@ void decode_balanced_kernel(BalancedArgs a) {
     for (int x = r0; x < r1;) {
         // ---- one unit: tiles [x, u_end) of segment (b, g)
         const int L = s_len[b];
-        const int nb = (L + kTile - 1) / kTile;
+        const int vis_lo = window_lo(L, W);          // first key the query sees
+        const int t0 = vis_lo / kTile * kTile;        // first token of the segment's first tile
+        const int nb = ntiles(L);
         const int seg_start = s_pre[b] + g * nb;
         const int seg_end = seg_start + nb;
         const int u_end = min(seg_end, r1);
-        const int tok_lo = (x - seg_start) * kTile;
-        const int tok_hi = min((u_end - seg_start) * kTile, L);
+        const int tok_lo = t0 + (x - seg_start) * kTile;
+        const int tok_hi = min(t0 + (u_end - seg_start) * kTile, L);
         const bool seg_first = x == seg_start;
         const bool owns_new = APPEND && u_end == seg_end;
         const int pnew = L - 1;
@@ -260,10 +287,14 @@ void decode_balanced_kernel(BalancedArgs a) {
             if constexpr (APPEND) {
                 if (owns_new) {
                     const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
-                    for (int i = tid; i < D; i += kThreads) s_kx[i] = ksrc[i];
+                    const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
+                    for (int i = tid; i < D; i += kThreads) {
+                        s_kx[i] = ksrc[i];
+                        s_vx[i] = vsrc[i];
+                    }
                 }
                 rotate_and_append<D, G, BF16>(a, b, g, pnew, owns_new, seg_first, &s_q[0][0],
-                                              s_kx, s_inv, &s_cs[0][0], s_r);
+                                              s_kx, s_vx, s_inv, &s_cs[0][0], s_r, &s_vsc);
             } else {
                 __syncthreads();
             }
@@ -344,7 +375,7 @@ void decode_balanced_kernel(BalancedArgs a) {
                     sacc = M::mma(qhi[i], kv, sacc);
                     sacc = M::mma(qlo[i], kv, sacc);
                 }
-                const bool tok_ok = base + l16 < c_hi;
+                const bool tok_ok = base + l16 < c_hi && base + l16 >= vis_lo;
                 float p[4], alpha[4];
                 bool grew = false;
 #pragma unroll
@@ -381,7 +412,8 @@ void decode_balanced_kernel(BalancedArgs a) {
                     float pv[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) pv[h] = s_p[wave][tt][h];
-                    const uint4 raw = base + tt < c_hi ? vc[u] : make_uint4(0, 0, 0, 0);
+                    const uint4 raw =
+                        base + tt < c_hi && base + tt >= vis_lo ? vc[u] : make_uint4(0, 0, 0, 0);
                     float vf[8];
                     decode8<BF16>(raw, vf);
 #pragma unroll

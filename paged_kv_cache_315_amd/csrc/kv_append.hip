@@ -8,9 +8,12 @@
 //   optional RMS normalisation  y = x / sqrt(mean(x^2) + eps) * w
 //     (page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock: QNorm/KNorm
 //      before RoPE; page "soft3/glia/run/arch/decoder/forward.rs", forward_layer: per-head norm)
-//   RoPE, rotate-half pairs (i, i + D/2) by pos * theta^(-2i/D)
+//   RoPE, rotate-half pairs (i, i + R/2) by pos * theta^(-2i/R) over the first R = rope_dim dims
 //     (hybrid_decoder.go, runHybridAttentionBlock: the RoPE op takes positions, head dim and
-//      base; forward.rs, forward_layer: the full head dimension rotates for LlamaStyle layers)
+//      base; forward.rs, forward_layer: the full head dimension rotates for LlamaStyle layers,
+//      and a per-layer rotary dimension R < D gives partial rotary), the other dims only normed
+//   optional per-head V normalisation in float (forward.rs, forward_layer CPU path,
+//     v_norm_per_head): v * (1 / sqrt(sum(v^2) / D + eps)), one rounding per operation
 //   f32 -> 16-bit code, round to nearest even, and the store into row
 //   (tables[b][pos / bs], pos % bs) of the [num_blocks, bs, Hkv, D] pool
 //     (page "makarna/pkg/kvcache/paged_cache.go": float32ToFloat16Bits, float32ToBFloat16Bits,
@@ -45,7 +48,6 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x;
     const int D = a.D;
-    const int half = D >> 1;
 
     int b, pos;
     if (a.cu_seqlens != nullptr) {
@@ -61,8 +63,9 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
         b = row;
         pos = a.positions[b];
     }
-    for (int i = threadIdx.x; i < half; i += kWaves * 64)
-        rope_cs(pos, a.theta, i, D, s_cs[i][0], s_cs[i][1]);
+    const int rhalf = a.rope_dim >> 1;   // rotary pairs (i, i + rhalf), i < rhalf
+    for (int i = threadIdx.x; i < rhalf; i += kWaves * 64)
+        rope_cs(pos, a.theta, i, a.rope_dim, s_cs[i][0], s_cs[i][1]);
     // destination pool row of the token (per KV head: + head * D); an out-of-range position or
     // block id skips the pool stores
     int64_t prow0 = -1;
@@ -83,27 +86,42 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
         const float* w = is_q ? a.q_norm_w : a.k_norm_w;
         const double r = w != nullptr ? rms_inv(x, D, a.eps) : 1.0;
         const int64_t prow = is_q || prow0 < 0 ? -1 : prow0 + (int64_t)head * D;
-        for (int i = lane; i < half; i += 64) {
+        float* qo = a.q_out + ((int64_t)row * a.Hq + head) * D;
+        for (int i = lane; i < rhalf; i += 64) {
             float x0 = x[i];
-            float x1 = x[i + half];
+            float x1 = x[i + rhalf];
             if (w != nullptr) {
                 x0 = norm_elem(x0, r, w[i]);
-                x1 = norm_elem(x1, r, w[i + half]);
+                x1 = norm_elem(x1, r, w[i + rhalf]);
             }
             float y0, y1;
             rope_rotate(x0, x1, s_cs[i][0], s_cs[i][1], y0, y1);
             if (is_q) {
-                float* qo = a.q_out + ((int64_t)row * a.Hq + head) * D;
                 qo[i] = y0;
-                qo[i + half] = y1;
+                qo[i + rhalf] = y1;
             } else if (prow >= 0) {
                 a.k_pool[prow + i] = encode16(y0, a.bf16);
-                a.k_pool[prow + i + half] = encode16(y1, a.bf16);
+                a.k_pool[prow + i + rhalf] = encode16(y1, a.bf16);
             }
+        }
+        // partial rotary: the dims from rope_dim on are only normed
+        for (int j = a.rope_dim + lane; j < D; j += 64) {
+            const float y = w != nullptr ? norm_elem(x[j], r, w[j]) : x[j];
+            if (is_q) qo[j] = y;
+            else if (prow >= 0) a.k_pool[prow + j] = encode16(y, a.bf16);
         }
         if (prow >= 0) {
             const float* vsrc = a.v_in + ((int64_t)row * a.Hkv + head) * D;
-            for (int d = lane; d < D; d += 64) a.v_pool[prow + d] = encode16(vsrc[d], a.bf16);
+            if (a.v_norm) {
+                wave_lds_sync();
+                for (int d = lane; d < D; d += 64) x[d] = vsrc[d];
+                wave_lds_sync();
+                const float sc = vnorm_scale(x, D, a.eps);
+                for (int d = lane; d < D; d += 64)
+                    a.v_pool[prow + d] = encode16(vnorm_elem(x[d], sc), a.bf16);
+            } else {
+                for (int d = lane; d < D; d += 64) a.v_pool[prow + d] = encode16(vsrc[d], a.bf16);
+            }
         }
         wave_lds_sync();  // x is reused by the wave's next vector
     }

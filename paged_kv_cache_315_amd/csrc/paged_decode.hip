@@ -92,10 +92,12 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
 
     const int L = clamp_len(a.context_lens[b], a);
     const int P = a.split_tokens;
-    const int t_begin = s * P;
+    const int vis_lo = window_lo(L, a.window);        // first key the query sees
+    const int t_first = vis_lo / kTile * kTile;       // partitions start at its tile
+    const int t_begin = t_first + s * P;
     if (t_begin >= L) return;           // whole workgroup exits together
     const int t_end = min(L, t_begin + P);
-    const int nsplit = (L + P - 1) / P;
+    const int nsplit = (L - t_first + P - 1) / P;
     const int Hq = a.Hkv * G;
 
     // ---- block ids of this partition -> LDS (the host keeps split_tokens within kTblCap ids)
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
             sacc = M::mma(qhi[i], kv, sacc);
             sacc = M::mma(qlo[i], kv, sacc);
         }
-        const bool tok_ok = base + l16 < t_end;
+        const bool tok_ok = base + l16 < t_end && base + l16 >= vis_lo;
         float p[4], alpha[4];
         bool grew = false;
 #pragma unroll
@@ -235,7 +237,8 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeArgs a)
             float pv[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) pv[h] = s_p[wave][tt][h];
-            const bool v_ok = base + tt < t_end;   // rows past the end were clamped: drop them
+            // rows past the end were clamped, rows before the window are not seen: drop them
+            const bool v_ok = base + tt < t_end && base + tt >= vis_lo;
             const uint4 raw = v_ok ? vc[u] : make_uint4(0, 0, 0, 0);
             float vf[8];
             decode8<BF16>(raw, vf);

@@ -136,6 +136,26 @@ pkv_status check_rope(const char* who, float theta, const float* qn, const float
     return PKV_OK;
 }
 
+// Layer options with the defaults filled in (rope_dim = D, no V norm, no window).
+struct Variant {
+    int rope_dim;
+    bool v_norm;
+    int window;
+};
+
+pkv_status resolve_variant(const char* who, const pkv_variant* v, int D, Variant& out) {
+    out = Variant{D, false, 0};
+    if (v == nullptr) return PKV_OK;
+    if (v->rope_dim < 0 || v->rope_dim > D || (v->rope_dim & 1))
+        return fail(PKV_ERR_INVALID_ARG, "%s: rope_dim=%d must be 0 or even in [2, head_dim=%d]",
+                    who, v->rope_dim, D);
+    if (v->window < 0) return fail(PKV_ERR_INVALID_ARG, "%s: window=%d < 0", who, v->window);
+    out.rope_dim = v->rope_dim ? v->rope_dim : D;
+    out.v_norm = v->v_norm != 0;
+    out.window = v->window;
+    return PKV_OK;
+}
+
 pkv_status check_decode_shape(const char* who, int B, int Hq, int Hkv, int D) {
     if (!decode_shape_supported(Hq, Hkv, D))
         return fail(PKV_ERR_UNSUPPORTED,
@@ -210,11 +230,15 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
                          int max_blocks_per_seq, const int32_t* positions, const float* q_norm_w,
                          const float* k_norm_w, float rms_eps, float rope_theta, int B,
                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                         int64_t num_blocks, pkv_dtype dtype, void* stream) {
+                         int64_t num_blocks, pkv_dtype dtype, const pkv_variant* variant,
+                         void* stream) {
     pkv_status st = check_common("kv_append", B, num_q_heads, num_kv_heads, head_dim, block_size,
                                  num_blocks, max_blocks_per_seq, dtype);
     if (st != PKV_OK) return st;
     st = check_rope("kv_append", rope_theta, q_norm_w, k_norm_w, head_dim);
+    if (st != PKV_OK) return st;
+    Variant var;
+    st = resolve_variant("kv_append", variant, head_dim, var);
     if (st != PKV_OK) return st;
     if (B == 0) return PKV_OK;
     if (!q_in || !k_in || !v_in || !q_out || !k_pool || !v_pool || !block_tables || !positions)
@@ -242,6 +266,8 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
     a.D = head_dim;
     a.bs = block_size;
     a.num_blocks = num_blocks;
+    a.rope_dim = var.rope_dim;
+    a.v_norm = var.v_norm;
     a.bf16 = dtype == PKV_BF16;
     const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append: launch failed: %s", hipGetErrorString(e));
@@ -287,7 +313,7 @@ pkv_status run_decode(const float* q, const void* k_pool, const void* v_pool,
                       const int32_t* tables, int max_blocks, const int32_t* context_lens,
                       int max_context_len, float scale, float* out, void* workspace,
                       const WorkspaceLayout& wl, int P, int B, int Hq, int Hkv, int D, int bs,
-                      int64_t nb, pkv_dtype dtype, hipStream_t stream,
+                      int64_t nb, pkv_dtype dtype, int window, hipStream_t stream,
                       bool lens_are_positions = false) {
     char* ws = static_cast<char*>(workspace);
     const bool has_ws = wl.total > 0;
@@ -313,6 +339,8 @@ pkv_status run_decode(const float* q, const void* k_pool, const void* v_pool,
         a.bs = bs;
         a.num_blocks = nb;
         a.num_cus = device_cus();
+        a.rope_dim = D;
+        a.window = window;
         a.bf16 = dtype == PKV_BF16;
         a.append = false;
         e = pkv::launch_decode_balanced(a, stream);
@@ -338,6 +366,7 @@ pkv_status run_decode(const float* q, const void* k_pool, const void* v_pool,
         a.D = D;
         a.bs = bs;
         a.num_blocks = nb;
+        a.window = window;
         a.bf16 = dtype == PKV_BF16;
         a.lens_are_positions = lens_are_positions;
         e = pkv::launch_paged_decode(a, stream);
@@ -354,9 +383,12 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                                  float* out, void* workspace, size_t workspace_bytes,
                                  int split_tokens, int B, int num_q_heads, int num_kv_heads,
                                  int head_dim, int block_size, int64_t num_blocks,
-                                 pkv_dtype dtype, void* stream) {
+                                 pkv_dtype dtype, const pkv_variant* variant, void* stream) {
     pkv_status st = check_common("decode", B, num_q_heads, num_kv_heads, head_dim, block_size,
                                  num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    Variant var;
+    st = resolve_variant("decode", variant, head_dim, var);
     if (st != PKV_OK) return st;
     if (max_context_len < 0)
         return fail(PKV_ERR_INVALID_ARG, "decode: max_context_len=%d must be >= 0", max_context_len);
@@ -385,7 +417,8 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                     wl.total);
     return run_decode(q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                       max_context_len, scale, out, workspace, wl, P, B, num_q_heads, num_kv_heads,
-                      head_dim, block_size, num_blocks, dtype, static_cast<hipStream_t>(stream));
+                      head_dim, block_size, num_blocks, dtype, var.window,
+                      static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_in, float* q_out,
@@ -395,11 +428,14 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
                            float rope_theta, float scale, float* out, void* workspace,
                            size_t workspace_bytes, int B, int num_q_heads, int num_kv_heads,
                            int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
-                           void* stream) {
+                           const pkv_variant* variant, void* stream) {
     pkv_status st = check_common("decode_step", B, num_q_heads, num_kv_heads, head_dim,
                                  block_size, num_blocks, max_blocks_per_seq, dtype);
     if (st != PKV_OK) return st;
     st = check_rope("decode_step", rope_theta, q_norm_w, k_norm_w, head_dim);
+    if (st != PKV_OK) return st;
+    Variant var;
+    st = resolve_variant("decode_step", variant, head_dim, var);
     if (st != PKV_OK) return st;
     st = check_decode_shape("decode_step", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
@@ -427,11 +463,11 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
         st = pkv_kv_append(q_in, k_in, v_in, q_out, k_pool, v_pool, block_tables,
                            max_blocks_per_seq, positions, q_norm_w, k_norm_w, rms_eps, rope_theta,
                            B, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype,
-                           stream);
+                           variant, stream);
         if (st != PKV_OK) return st;
         return run_decode(q_out, k_pool, v_pool, block_tables, max_blocks_per_seq, positions,
                           max_ctx, scale, out, workspace, wl, P, B, num_q_heads, num_kv_heads,
-                          head_dim, block_size, num_blocks, dtype, s, true);
+                          head_dim, block_size, num_blocks, dtype, var.window, s, true);
     }
     char* ws = static_cast<char*>(workspace);
     pkv::BalancedArgs a{};
@@ -461,6 +497,9 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
     a.bs = block_size;
     a.num_blocks = num_blocks;
     a.num_cus = device_cus();
+    a.rope_dim = var.rope_dim;
+    a.v_norm = var.v_norm;
+    a.window = var.window;
     a.bf16 = dtype == PKV_BF16;
     a.append = true;
     const hipError_t e = pkv::launch_decode_balanced(a, s);
@@ -476,11 +515,14 @@ pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float*
                               const float* q_norm_w, const float* k_norm_w, float rms_eps,
                               float rope_theta, int B, int num_tokens, int num_q_heads,
                               int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-                              pkv_dtype dtype, void* stream) {
+                              pkv_dtype dtype, const pkv_variant* variant, void* stream) {
     pkv_status st = check_common("prefill_append", B, num_q_heads, num_kv_heads, head_dim,
                                  block_size, num_blocks, max_blocks_per_seq, dtype);
     if (st != PKV_OK) return st;
     st = check_rope("prefill_append", rope_theta, q_norm_w, k_norm_w, head_dim);
+    if (st != PKV_OK) return st;
+    Variant var;
+    st = resolve_variant("prefill_append", variant, head_dim, var);
     if (st != PKV_OK) return st;
     if (num_tokens < 0)
         return fail(PKV_ERR_INVALID_ARG, "prefill_append: num_tokens = %d < 0", num_tokens);
@@ -510,6 +552,8 @@ pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float*
     a.D = head_dim;
     a.bs = block_size;
     a.num_blocks = num_blocks;
+    a.rope_dim = var.rope_dim;
+    a.v_norm = var.v_norm;
     a.bf16 = dtype == PKV_BF16;
     const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -533,9 +577,13 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
                                   int max_chunk, int max_context_len, float scale, float* out,
                                   void* workspace, size_t workspace_bytes, int B, int num_tokens,
                                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                                  int64_t num_blocks, pkv_dtype dtype, void* stream) {
+                                  int64_t num_blocks, pkv_dtype dtype,
+                                  const pkv_variant* variant, void* stream) {
     pkv_status st = check_common("prefill", B, num_q_heads, num_kv_heads, head_dim, block_size,
                                  num_blocks, max_blocks_per_seq, dtype);
+    if (st != PKV_OK) return st;
+    Variant var;
+    st = resolve_variant("prefill", variant, head_dim, var);
     if (st != PKV_OK) return st;
     st = check_decode_shape("prefill", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
@@ -578,6 +626,7 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
     a.D = head_dim;
     a.bs = block_size;
     a.num_blocks = num_blocks;
+    a.window = var.window;
     a.bf16 = dtype == PKV_BF16;
     a.shared_tiles = plan.shared;
     const hipError_t e = pkv::launch_prefill_attn(a, static_cast<hipStream_t>(stream));

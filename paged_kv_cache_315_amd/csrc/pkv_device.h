@@ -82,10 +82,32 @@ __device__ __forceinline__ double rms_inv(const float* x, int D, float eps) {
 
 __device__ __forceinline__ float norm_elem(float x, double r, float w) {
 #pragma clang fp contract(off)
-    return (float)(((double)x * r) * (double)w);
+    return canonical_if_nan((float)(((double)x * r) * (double)w));
 }
 
-// theta^(-2i/D), the angle per position of rotary pair i.
+// Per-head V normalisation factor in float, in the order of page "soft3/glia/run/arch/decoder/
+// forward.rs" forward_layer CPU path (v_norm_per_head): the squares summed in index order,
+// rms = sqrt(sum * (1/D) + eps), factor = 1 / rms; every operation rounded once (no fused
+// multiply-add; division and square root correctly rounded).
+__device__ __forceinline__ float vnorm_scale(const float* v, int D, float eps) {
+#pragma clang fp contract(off)
+    float sumsq = 0.0f;
+    for (int j = 0; j < D; ++j) {
+        const float sq = v[j] * v[j];
+        sumsq = sumsq + sq;
+    }
+    const float inv_d = 1.0f / (float)D;
+    const float rms = __builtin_sqrtf(sumsq * inv_d + eps);
+    return 1.0f / rms;
+}
+
+__device__ __forceinline__ float vnorm_elem(float v, float scale) {
+#pragma clang fp contract(off)
+    return canonical_if_nan(v * scale);
+}
+
+// theta^(-2i/D), the angle per position of rotary pair i (D = the rotated span: head_dim, or
+// rope_dim for partial rotary).
 __device__ __forceinline__ double rope_inv_freq(float theta, int i, int D) {
 #pragma clang fp contract(off)
     return pow((double)theta, -(2.0 * (double)i) / (double)D);
@@ -172,6 +194,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// First position a query at attended length L sees under a sliding window of W positions
+// (0: no window).
+__device__ __forceinline__ int window_lo(int L, int W) { return (W > 0 && L > W) ? L - W : 0; }
 
 // ---- K/V codes ----------------------------------------------------------------------------
 template <bool BF16>

@@ -26,6 +26,8 @@ struct AppendArgs {
     float theta;
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
+    int rope_dim;           // rotated dims (even, <= D)
+    bool v_norm;            // V rows normalised per KV head before they are stored
     bool bf16;
 };
 
@@ -51,6 +53,7 @@ struct PrefillArgs {
     int QTmax;                  // query tiles per sequence = ceil(max_chunk / QT)
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
+    int window;                 // sliding window (0: every token)
     bool bf16;
     bool shared_tiles;          // 4 query tiles per workgroup sharing each K/V tile (S == 1)
 };
@@ -76,6 +79,7 @@ struct DecodeArgs {
     int S;            // partitions per sequence = ceil(max_context_len / split_tokens)
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
+    int window;               // sliding window (0: every token)
     bool bf16;
     bool lens_are_positions;  // context_lens holds positions: L = p + 1 (fused-step fallback)
 };
@@ -110,6 +114,9 @@ struct BalancedArgs {
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
     int num_cus;
+    int rope_dim;           // append only: rotated dims (even, <= D)
+    int window;             // sliding window (0: every token)
+    bool v_norm;            // append only: V rows normalised per KV head
     bool bf16;
     bool append;
 };

@@ -132,12 +132,15 @@ void prefill_attn_kernel(PrefillArgs a) {
     auto row_limit = [&](int t) -> int {
         return (int)max((int64_t)0, min((int64_t)st + tok0 + t + 1, cap));
     };
+    // ... and the first of them (a sliding window hides the keys before it)
+    auto row_lo = [&](int t) -> int { return window_lo(row_limit(t), a.window); };
     const int L_tile = row_limit(ntok - 1);
+    const int t_first = row_lo(0) / kTile * kTile;   // partitions start at the tile holding it
     const int P = a.split_tokens;
-    const int t_begin = s * P;
+    const int t_begin = t_first + s * P;
     if (t_begin >= L_tile) return;
     const int t_end = min(L_tile, t_begin + P);
-    const int nsplit = (L_tile + P - 1) / P;
+    const int nsplit = (L_tile - t_first + P - 1) / P;
 
     // ---- block ids of this partition -> LDS
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
@@ -194,7 +197,7 @@ void prefill_attn_kernel(PrefillArgs a) {
             }
     }
     // the rows of the score / output layout this lane holds: 4 * q4 + r
-    int lim[4];
+    int lim[4], lo[4];   // the row sees keys lo .. lim-1
     bool rvalid[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -202,6 +205,7 @@ void prefill_attn_kernel(PrefillArgs a) {
         const int t = row / G;
         rvalid[r] = row < QT * G && t < ntok;
         lim[r] = rvalid[r] ? min(row_limit(t), t_end) : 0;
+        lo[r] = rvalid[r] ? row_lo(t) : 0;
     }
     __syncthreads();  // s_tbl ready
 
@@ -247,7 +251,7 @@ void prefill_attn_kernel(PrefillArgs a) {
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float sc = key < lim[r] ? sacc[r] * score_fix : -INFINITY;
+            const float sc = key < lim[r] && key >= lo[r] ? sacc[r] * score_fix : -INFINITY;
             const float tmax = row16_max(sc);
             const float m_new = fmaxf(m[r], tmax);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -297,7 +301,7 @@ void prefill_attn_kernel(PrefillArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * q4 + r;
                 for (int k = 0; k < kTile; ++k) {
-                    if (base + k >= lim[r]) continue;
+                    if (base + k >= lim[r] || base + k < lo[r]) continue;
                     const float pk = s_p[wave][row][k];
 #pragma unroll
                     for (int n = 0; n < NT; ++n)
@@ -473,6 +477,9 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
     const int ntok = max(0, min(QT, T - tok0));           // 0: the wave has no tokens
     const int L_wg = limit_of(min(T, tok_wg + kWaves * QT) - 1);
     const int L_w = ntok > 0 ? limit_of(tok0 + ntok - 1) : 0;
+    // first keys seen (a sliding window hides the ones before): workgroup (tile aligned), wave
+    const int lo_wg = window_lo(limit_of(tok_wg), a.window) / kTile * kTile;
+    const int lo_w = ntok > 0 ? window_lo(limit_of(tok0), a.window) : 0;
     if (threadIdx.x < 2 * NSUB) s_vbad[threadIdx.x / NSUB][threadIdx.x % NSUB] = -1;
 
     // ---- Q operand of this wave's tile
@@ -517,12 +524,14 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
                 qlo[i][j] = (typename M::elem)(x - (float)hi);
             }
     }
-    int lim[4];
+    int lim[4], lo[4];   // the row sees keys lo .. lim-1
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = 4 * q4 + r;
         const int t = row / G;
-        lim[r] = (row < QT * G && t < ntok) ? limit_of(tok0 + t) : 0;
+        const bool ok = row < QT * G && t < ntok;
+        lim[r] = ok ? limit_of(tok0 + t) : 0;
+        lo[r] = ok ? window_lo(lim[r], a.window) : 0;
     }
 
     float m[4], lsum[4];
@@ -542,7 +551,7 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
     const int64_t head_off = (int64_t)g * D;
     const int chunk_keys = (kTblCap - 2) * a.bs / KT * KT;
 
-    for (int c_lo = 0; c_lo < L_wg; c_lo += chunk_keys) {
+    for (int c_lo = lo_wg; c_lo < L_wg; c_lo += chunk_keys) {
         const int c_hi = min(L_wg, c_lo + chunk_keys);
         const int first_blk = (int)bdiv.div((uint32_t)c_lo);
         const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
@@ -609,7 +618,7 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
             float p[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float sc = key < lim[r] ? sacc[r] * score_fix : -INFINITY;
+                const float sc = key < lim[r] && key >= lo[r] ? sacc[r] * score_fix : -INFINITY;
                 const float tmax = row16_max(sc);
                 const float m_new = fmaxf(m[r], tmax);
                 const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -648,7 +657,7 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * q4 + r;
                     for (int k = 0; k < kTile; ++k) {
-                        if (base + k >= lim[r]) continue;
+                        if (base + k >= lim[r] || base + k < lo[r]) continue;
                         const float pk = s_p[wave][row][k];
 #pragma unroll
                         for (int n = 0; n < NT; ++n)
@@ -671,7 +680,8 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
 #pragma unroll
             for (int sg = 0; sg < NSUB; ++sg) {
                 const int gb = base + sg * kTile;
-                if (gb < L_w) compute_group(gb, sg * kTile, buf, s_vbad[buf][sg] == base);
+                if (gb < L_w && gb + kTile > lo_w)
+                    compute_group(gb, sg * kTile, buf, s_vbad[buf][sg] == base);
             }
             if (more) store_kv(base + KT, regs, buf ^ 1);
             __syncthreads();

@@ -40,7 +40,8 @@ def test_status_strings_and_version(lib):
 
 def _append(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qo=FAKE, kp=FAKE, vp=FAKE, t=FAKE, mb=4, p=FAKE, qn=None,
-             kn=None, eps=1e-6, theta=1e4, B=2, Hq=4, Hkv=2, D=64, bs=16, nb=16, dt=1, s=None)
+             kn=None, eps=1e-6, theta=1e4, B=2, Hq=4, Hkv=2, D=64, bs=16, nb=16, dt=1, var=None,
+             s=None)
     a.update(kw)
     return lib.pkv_kv_append(*a.values())
 
@@ -49,7 +50,8 @@ def _decode(lib, **kw):
     # mcl = 200 with 64-token partitions needs a workspace, so a case that passed every other
     # check would still stop at the workspace check instead of launching on fake pointers
     a = dict(q=FAKE, kp=FAKE, vp=FAKE, t=FAKE, mb=4, cl=FAKE, mcl=200, scale=0.125, out=FAKE,
-             ws=None, wsb=0, split=64, B=2, Hq=4, Hkv=2, D=64, bs=16, nb=16, dt=1, s=None)
+             ws=None, wsb=0, split=64, B=2, Hq=4, Hkv=2, D=64, bs=16, nb=16, dt=1, var=None,
+             s=None)
     a.update(kw)
     return lib.pkv_paged_attn_decode(*a.values())
 
@@ -58,6 +60,9 @@ def _decode(lib, **kw):
     (dict(B=-1), 1), (dict(Hq=5), 1), (dict(Hkv=0), 1), (dict(bs=0), 1), (dict(nb=0), 1),
     (dict(theta=0.0), 1), (dict(theta=float("inf")), 1), (dict(qn=FAKE), 1), (dict(dt=3), 1),
     (dict(D=63), 2), (dict(D=258), 2), (dict(q=None), 1), (dict(B=0, q=None), 0),
+    (dict(var=_lib.variant(rope_dim=3)), 1), (dict(var=_lib.variant(rope_dim=66)), 1),
+    (dict(var=_lib.variant(rope_dim=-2)), 1), (dict(var=_lib.variant(window=-1)), 1),
+    (dict(B=0, q=None, var=_lib.variant(rope_dim=32, v_norm=True)), 0),
 ])
 def test_append_argument_checks(lib, kw, status):
     assert _append(lib, **kw) == status
@@ -71,6 +76,8 @@ def test_append_argument_checks(lib, kw, status):
     (dict(out=None), 1), (dict(ws=None, wsb=0), 3), (dict(ws=FAKE, wsb=10), 3),
     (dict(B=0), 0), (dict(mcl=0), 0), (dict(B=70000), 2),
     (dict(split=1024, bs=1), 1),                      # 1024 > 1022 * block_size
+    (dict(var=_lib.variant(window=-5)), 1), (dict(var=_lib.variant(rope_dim=7)), 1),
+    (dict(var=_lib.variant(window=100)), 3),          # a valid window reaches the workspace check
 ])
 def test_decode_argument_checks(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -79,7 +86,7 @@ def test_decode_argument_checks(lib, kw, status):
 def _prefill_append(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qo=FAKE, kp=FAKE, vp=FAKE, t=FAKE, mb=4, cu=FAKE, st=FAKE,
              qn=None, kn=None, eps=1e-6, theta=1e4, B=2, N=5, Hq=4, Hkv=2, D=64, bs=16, nb=16,
-             dt=1, s=None)
+             dt=1, var=None, s=None)
     a.update(kw)
     return lib.pkv_prefill_append(*a.values())
 
@@ -98,7 +105,7 @@ def _prefill(lib, **kw):
     # check would stop at the workspace check instead of launching on fake pointers
     a = dict(q=FAKE, kp=FAKE, vp=FAKE, t=FAKE, mb=300, cu=FAKE, st=FAKE, mc=4, mcl=4096,
              scale=0.125, out=FAKE, ws=None, wsb=0, B=2, N=8, Hq=4, Hkv=2, D=64, bs=16, nb=600,
-             dt=1, s=None)
+             dt=1, var=None, s=None)
     a.update(kw)
     return lib.pkv_paged_attn_prefill(*a.values())
 
@@ -107,7 +114,8 @@ def _prefill(lib, **kw):
     (dict(N=-1), 1), (dict(mc=-1), 1), (dict(mcl=-1), 1), (dict(D=96), 2),
     (dict(Hq=32, Hkv=2), 2), (dict(cu=None), 1), (dict(out=None), 1), (dict(ws=None), 3),
     (dict(ws=FAKE, wsb=16), 3), (dict(B=0), 0), (dict(N=0), 0), (dict(mc=0), 0),
-    (dict(B=70000, mc=64), 2),
+    (dict(B=70000, mc=64), 2), (dict(var=_lib.variant(window=-1)), 1),
+    (dict(var=_lib.variant(window=64)), 3),
 ])
 def test_prefill_argument_checks(lib, kw, status):
     assert _prefill(lib, **kw) == status
