@@ -50,6 +50,23 @@ SIGNATURES = {
                                     _I, _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_prefill_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "pkv_validate_tables": (_I, [_P, _I, _P, _P, _I, _I, _I64, _I]),
+    # host block manager (include/pkv_blocks.h)
+    "pkv_pool_create": (_I, [_I64, _I, _P]),
+    "pkv_pool_destroy": (_I, [_P]),
+    "pkv_pool_stats": (_I, [_P, _P]),
+    "pkv_pool_block_state": (_I, [_P, _P, _P, _P, _P]),
+    "pkv_block_hash": (ctypes.c_uint64, [_P, _I, _P]),
+    "pkv_seq_create": (_I, [_P, _I, _P]),
+    "pkv_seq_destroy": (None, [_P]),
+    "pkv_seq_allocate_for_tokens": (_I, [_P, _P, _I, _P]),
+    "pkv_seq_reserve": (_I, [_P, _I, _P]),
+    "pkv_seq_append_token": (_I, [_P, ctypes.c_int32]),
+    "pkv_seq_commit": (_I, [_P, _I]),
+    "pkv_seq_truncate": (_I, [_P, _I]),
+    "pkv_seq_free": (_I, [_P]),
+    "pkv_seq_info": (_I, [_P, _P]),
+    "pkv_seq_blocks": (_I, [_P, _P, _P, _P, _I]),
+    "pkv_fill_block_tables": (_I, [_P, _I, _I, ctypes.c_int32, _P, _P]),
     "pkv_status_string": (ctypes.c_char_p, [_I]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),

@@ -4,7 +4,8 @@
 
 Every HIP source is compiled with packed-fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops): the compiler otherwise forms
-v_pk_{add,mul,fma}_f32 from ordinary float code.
+v_pk_{add,mul,fma}_f32 from ordinary float code. Host-only sources (csrc/*.cpp: the block
+manager) are plain C++ built with g++ and linked into the same library.
 """
 from __future__ import annotations
 
@@ -34,8 +35,15 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def host_sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(out_path: str = LIB_PATH, extra_flags: tuple[str, ...] = (), verbose: bool = False) -> str:
@@ -46,6 +54,14 @@ def build(out_path: str = LIB_PATH, extra_flags: tuple[str, ...] = (), verbose: 
         for src in sources():
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                           text=True), src))
+            objs.append(obj)
+        for src in host_sources():
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = ["g++", *CXX_FLAGS, "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

@@ -24,6 +24,21 @@ pkv_status fail(pkv_status st, const char* fmt, ...) {
     return st;
 }
 
+}  // namespace
+
+// The same thread-local message for the host block manager (block_manager.cpp).
+namespace pkv {
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+}  // namespace pkv
+
+namespace {
+
 bool valid_dtype(pkv_dtype d) { return d == PKV_F16 || d == PKV_BF16; }
 
 constexpr int kMaxGridDim = 65535;  // y / z grid limit used for Hkv and B

@@ -1,4 +1,4 @@
-"""The C ABI library without a GPU: it loads, exports every symbol include/pkv.h declares, and
+"""The C ABI library without a GPU: it loads, exports every symbol include/*.h declares, and
 its host-side argument checks and helpers behave as documented (no kernel is launched)."""
 import ctypes
 import os
@@ -15,9 +15,13 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails it
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "pkv.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(pkv_\w+)\s*\(", src))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(pkv_\w+)\s*\(", src))
+    return names
 
 
 @pytest.fixture(scope="module")
