@@ -44,6 +44,9 @@
  *            rope_dim dims, angle pos * theta^(-2i/rope_dim); dims from rope_dim on unchanged.
  *   R-WIN    sliding window W: a query at attended length L sees positions max(0, L - W) .. L - 1
  *            (the last W tokens, the ring's read range without its storage reuse).
+ *   R-READ   RoPE applied at read: the append with rope_dim = 0 rotates nothing (the pool holds the
+ *            un-rotated, normed keys, q_out is the normed query); attention then rotates the
+ *            query to position L - 1 and key t to position t, in double.
  *   R-NAN    a NaN that the norm / V-norm / RoPE arithmetic produces is the canonical quiet NaN
  *            0x7FC00000 (IEEE 754 leaves the sign and payload of such a NaN to the
  *            implementation); a NaN that reaches the converter untouched (V) keeps its bits.
@@ -359,7 +362,7 @@ int pkvo_kv_append_v(const float* q_in, const float* k_in, const float* v_in, fl
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (D & 1) || bs <= 0 || Hq % Hkv)
         return PKVO_ERR_ARG;
-    if (rope_dim <= 0 || rope_dim > D || (rope_dim & 1))
+    if (rope_dim < 0 || rope_dim > D || (rope_dim & 1))
         return PKVO_ERR_ARG;
     if ((q_norm_w == NULL) != (k_norm_w == NULL))
         return PKVO_ERR_ARG;
@@ -414,7 +417,7 @@ int pkvo_prefill_append_v(const float* q_in, const float* k_in, const float* v_i
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (D & 1) || bs <= 0 || Hq % Hkv)
         return PKVO_ERR_ARG;
-    if (rope_dim <= 0 || rope_dim > D || (rope_dim & 1))
+    if (rope_dim < 0 || rope_dim > D || (rope_dim & 1))
         return PKVO_ERR_ARG;
     if ((q_norm_w == NULL) != (k_norm_w == NULL))
         return PKVO_ERR_ARG;
@@ -454,13 +457,32 @@ int pkvo_prefill_append(const float* q_in, const float* k_in, const float* v_in,
                                  Hq, Hkv, D, bs, num_blocks, dtype);
 }
 
+/* RoPE of one head vector in double, not rounded (R-ROPE angles, R-PART pairing): used when
+ * the pool holds un-rotated keys and attention rotates query and keys itself (R-READ). */
+static void rope_double(const double* x, int D, int rope_dim, int pos, double theta, double* y)
+{
+    const int half = rope_dim / 2;
+    for (int i = 0; i < half; ++i) {
+        const double inv_freq = pow(theta, -(2.0 * (double)i) / (double)rope_dim);
+        const double angle = (double)pos * inv_freq;
+        const double c = cos(angle);
+        const double s = sin(angle);
+        y[i] = x[i] * c - x[i + half] * s;
+        y[i + half] = x[i + half] * c + x[i] * s;
+    }
+    for (int j = 2 * half; j < D; ++j)
+        y[j] = x[j];
+}
+
 /* Attention of one query token (all Hq heads, q_row [Hq, D]) over the first L tokens of the
  * sequence whose block list is table_row; writes out_row [Hq, D]. kc / vc: scratch of
- * L * Hkv * D floats, e: scratch of L doubles. */
+ * L * Hkv * D floats, e: scratch of L doubles. read_theta > 0 (R-READ): the query is rotated to
+ * position L - 1 and key t to position t (first rope_dim dims, double) before the dot product. */
 static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t* v_pool,
                       const int32_t* table_row, int max_blocks, int L, int window, float scale,
                       float* out_row, int Hq, int Hkv, int D, int bs, int64_t num_blocks,
-                      int dtype, float* kc, float* vc, double* e)
+                      int dtype, float* kc, float* vc, double* e, double read_theta,
+                      int rope_dim)
 {
     const int G = Hq / Hkv;
     if (L < 1 || (L + bs - 1) / bs > max_blocks)
@@ -481,16 +503,33 @@ static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t
                 vc[((int64_t)i * Hkv + g) * D + d] = decode(v_pool[o], dtype);
             }
     }
+    const int qpos = L - 1;
     L = n;
+    double qd[256], qr[256], kd[256], kr[256];
+    if (read_theta > 0.0 && (D > 256 || rope_dim < 2 || rope_dim > D))
+        return PKVO_ERR_ARG;
     for (int h = 0; h < Hq; ++h) {
         const int g = MUT(4) ? h % Hkv : h / G;
         const float* qh = q_row + (int64_t)h * D;
+        if (read_theta > 0.0) {
+            for (int d = 0; d < D; ++d)
+                qd[d] = (double)qh[d];
+            rope_double(qd, D, rope_dim, qpos, read_theta, qr);
+        }
         double m = -INFINITY;
         for (int t = 0; t < L; ++t) {
             const float* kt = kc + ((int64_t)t * Hkv + g) * D;
             double dot = 0.0;
-            for (int d = 0; d < D; ++d)
-                dot += (double)qh[d] * (double)kt[d];
+            if (read_theta > 0.0) {
+                for (int d = 0; d < D; ++d)
+                    kd[d] = (double)kt[d];
+                rope_double(kd, D, rope_dim, lo + t + (MUT(15) ? 1 : 0), read_theta, kr);
+                for (int d = 0; d < D; ++d)
+                    dot += qr[d] * kr[d];
+            } else {
+                for (int d = 0; d < D; ++d)
+                    dot += (double)qh[d] * (double)kt[d];
+            }
             e[t] = (MUT(6) ? 1.0 : (double)scale) * dot;
             if (e[t] > m) /* NaN never compares greater: ignored by the max */
                 m = e[t];
@@ -515,7 +554,8 @@ static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t
 static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
                        const int32_t* tables, int max_blocks, const int* seq, const int* lens,
                        int window, float scale, float* out, int n, int Hq, int Hkv, int D, int bs,
-                       int64_t num_blocks, int dtype, const uint8_t* row_mask)
+                       int64_t num_blocks, int dtype, const uint8_t* row_mask, double read_theta,
+                       int rope_dim)
 {
     int Lmax = 1;
     for (int r = 0; r < n; ++r)
@@ -532,7 +572,7 @@ static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v
                             tables + (int64_t)seq[r] * max_blocks, max_blocks, lens[r], window,
                             scale,
                             out + (int64_t)r * Hq * D, Hq, Hkv, D, bs, num_blocks, dtype, kc, vc,
-                            e);
+                            e, read_theta, rope_dim);
     }
     free(kc);
     free(vc);
@@ -573,7 +613,49 @@ int pkvo_paged_attn_decode_v(const float* q, const uint16_t* k_pool, const uint1
         lens[b] = context_lens[b] - (MUT(9) && context_lens[b] > 1 ? 1 : 0);
     }
     const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, window,
-                                   scale, out, B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
+                                   scale, out, B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask,
+                                   0.0, D);
+    free(seq);
+    free(lens);
+    return status;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Decode over a pool of un-rotated keys, rotating at read (R-READ).
+ * [MK-DEC] runHybridAttentionBlock / runHybridAttentionBlockBatch: when RoPE is fused into the
+ * paged kernel the standalone RoPE of Q and K is skipped, the cache receives the un-rotated K,
+ * and the kernel (given the RoPE base) applies RoPE itself. What it computes is therefore the
+ * decode above with q rotated to its position (L - 1) and every key t rotated to position t:
+ * s_t = scale * (R_{L-1} q) . (R_t k_t), the rotations of R-ROPE / R-PART in double.
+ * Pinned by: agreement with the stored-rotated path on float-exact pools (a pool of rotated keys
+ * that the codes hold exactly), the relative-position property (shifting every position leaves
+ * the output unchanged), an independent numpy complex-exponential formulation, and a planted
+ * off-by-one key position that those catch.
+ * ------------------------------------------------------------------------------------------ */
+int pkvo_paged_attn_decode_rope(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                                const int32_t* tables, int max_blocks,
+                                const int32_t* context_lens, int window, float theta,
+                                int rope_dim, float scale, float* out, int B, int Hq, int Hkv,
+                                int D, int bs, int64_t num_blocks, int dtype,
+                                const uint8_t* row_mask)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 256 || bs <= 0 || Hq % Hkv ||
+        window < 0 || !(theta > 0.0f) || rope_dim < 2 || rope_dim > D || (rope_dim & 1))
+        return PKVO_ERR_ARG;
+    int* seq = (int*)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
+    int* lens = (int*)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
+    if (!seq || !lens) {
+        free(seq);
+        free(lens);
+        return PKVO_ERR_ARG;
+    }
+    for (int b = 0; b < B; ++b) {
+        seq[b] = b;
+        lens[b] = context_lens[b];
+    }
+    const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, window,
+                                   scale, out, B, Hq, Hkv, D, bs, num_blocks, dtype, row_mask,
+                                   (double)theta, rope_dim);
     free(seq);
     free(lens);
     return status;
@@ -627,7 +709,8 @@ int pkvo_paged_attn_prefill_v(const float* q, const uint16_t* k_pool, const uint
             lens[r] = start_pos[b] + (r - cu_seqlens[b]) + (MUT(11) ? 0 : 1);
         }
     const int status = attend_rows(q, k_pool, v_pool, tables, max_blocks, seq, lens, window,
-                                   scale, out, n, Hq, Hkv, D, bs, num_blocks, dtype, row_mask);
+                                   scale, out, n, Hq, Hkv, D, bs, num_blocks, dtype, row_mask,
+                                   0.0, D);
     free(seq);
     free(lens);
     return status;

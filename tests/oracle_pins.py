@@ -576,4 +576,84 @@ def pin_prefill_window_numpy(lib):
             np.testing.assert_allclose(out[r, h], ref, rtol=2.5e-7, atol=1e-12)
 
 
+# ------------------------------------------------------------------ RoPE applied at read
+def _rope_complex_f64(x: np.ndarray, pos: int, theta: float, rope_dim: int) -> np.ndarray:
+    """Rotate-half pairs as complex numbers: (x[i] + 1j x[i + R/2]) * exp(1j pos theta^(-2i/R))
+    on the first R = rope_dim dims, float64, nothing rounded; the tail is kept."""
+    half = rope_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    z = (x[..., :half].astype(np.float64) + 1j * x[..., half:rope_dim].astype(np.float64))
+    z = z * np.exp(1j * pos * theta ** (-2.0 * i / rope_dim))
+    return np.concatenate([z.real, z.imag, x[..., rope_dim:].astype(np.float64)], axis=-1)
+
+
+def pin_rope_read_complex(lib):
+    """Attention over un-rotated keys with the rotation applied at read (the page's fused-RoPE
+    paged kernel): the numpy complex formulation rotates q to position L-1 and key t to t."""
+    for wl, rope_dim in ((W.make_workload(111, [1, 6, 33], 4, 2, 32, 4, "f16", 1e4,
+                                          spare_blocks=2), 32),
+                         (W.make_workload(112, [19, 70], 6, 3, 64, 16, "bf16", 5e5,
+                                          spare_blocks=1), 32)):
+        L = wl["context_lens"]
+        out = oracle.paged_attn_decode_rope(wl["q"], wl["k_pool"], wl["v_pool"], wl["tables"],
+                                            L - 1, wl["theta"], wl["scale"], wl["dtype"],
+                                            rope_dim=rope_dim, lib=lib)
+        kf = _decode_np(wl["k_pool"], wl["dtype"])
+        vf = _decode_np(wl["v_pool"], wl["dtype"])
+        B, Hq, D = wl["q"].shape
+        bs, Hkv = wl["k_pool"].shape[1], wl["k_pool"].shape[2]
+        G = Hq // Hkv
+        for b in range(B):
+            n = int(L[b]) - 1                       # the cached tokens (no append here)
+            t = np.arange(n)
+            K = kf[wl["tables"][b, t // bs], t % bs]
+            V = vf[wl["tables"][b, t // bs], t % bs]
+            Kr = np.stack([_rope_complex_f64(K[j], int(j), wl["theta"], rope_dim) for j in range(n)])
+            for h in range(Hq):
+                qr = _rope_complex_f64(wl["q"][b, h], n - 1, wl["theta"], rope_dim)
+                sc = (Kr[:, h // G, :] @ qr) * float(wl["scale"])
+                e = np.exp(sc - sc.max())
+                ref = (e @ V[:, h // G, :]) / e.sum()
+                np.testing.assert_allclose(out[b, h], ref, rtol=2.5e-7, atol=1e-12)
+
+
+def pin_rope_read_relative_position(lib):
+    """Scores depend on key position minus query position only: a sequence whose last L tokens
+    are another sequence's L tokens, seen through a window of L, gives the same output."""
+    rng = np.random.default_rng(9)
+    D, Hkv, Hq, bs, L, c = 32, 1, 2, 4, 9, 7
+    kc = oracle.encode(rng.standard_normal((L, Hkv, D), dtype=np.float32), "f16", lib)
+    vc = oracle.encode(rng.standard_normal((L, Hkv, D), dtype=np.float32), "f16", lib)
+    q = rng.standard_normal((2, Hq, D), dtype=np.float32)
+    q[1] = q[0]
+    nb = (L + c + bs - 1) // bs
+    kp = np.zeros((2 * nb, bs, Hkv, D), np.uint16)
+    vp = np.zeros_like(kp)
+    tables = np.arange(2 * nb, dtype=np.int32).reshape(2, nb)
+    for j in range(L):
+        for b, pos in ((0, j), (1, j + c)):
+            blk = tables[b, pos // bs]
+            kp[blk, pos % bs], vp[blk, pos % bs] = kc[j], vc[j]
+    lens = np.array([L, L + c], np.int32)
+    out = oracle.paged_attn_decode_rope(q, kp, vp, tables, lens, 1e4, 0.25, "f16", lib=lib,
+                                        window=L)
+    np.testing.assert_allclose(out[1], out[0], rtol=1e-6, atol=1e-7)
+
+
+def pin_rope_read_append_stores_unrotated(lib):
+    """With the rotation left to the read, the append rotates nothing: q_out is q and the stored
+    K / V are the library casts of the inputs."""
+    wl = W.make_workload(113, [5, 12], 4, 2, 64, 8, "f16", 1e4, spare_blocks=1)
+    kp, vp = wl["k_pool"].copy(), wl["v_pool"].copy()
+    q_out = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"],
+                             wl["positions"], None, None, 1e-6, wl["theta"], "f16", lib=lib,
+                             rope_on_read=True)
+    assert np.array_equal(q_out, wl["q"])
+    bs = kp.shape[1]
+    for b, p in enumerate(wl["positions"]):
+        blk = wl["tables"][b, p // bs]
+        assert np.array_equal(kp[blk, p % bs], wl["k_new"][b].astype(np.float16).view(np.uint16))
+        assert np.array_equal(vp[blk, p % bs], wl["v_new"][b].astype(np.float16).view(np.uint16))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -20,6 +20,7 @@ MUTANTS = {
     12: "partial rotary: frequencies over head_dim instead of rope_dim",
     13: "V norm: eps dropped",
     14: "sliding window: one token too many",
+    15: "RoPE at read: key positions off by one",
 }
 
 
