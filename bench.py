@@ -80,10 +80,12 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="pool copies (0: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--workload", choices=["decode", "prefill", "spec"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "spec", "rope"],
+                    default="decode",
                     help="decode: the decode step (default); prefill / spec: chunked prefill "
                          "(4 x 512-token chunks) / 4 draft tokens per sequence, append + "
-                         "causal paged attention")
+                         "causal paged attention; rope: the decode step with RoPE applied at "
+                         "read (un-rotated pool), append + decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -110,6 +112,8 @@ def main() -> int:
                           "bytes_written_per_copy": 1 << 30, "copies": 5}))
         return 0
     pkv._lib.load()  # fail loudly before any work if the HIP library is missing
+    if args.workload == "rope":
+        return run_rope(args, torch, pkv, W)
     if args.workload != "decode":
         return run_prefill(args, torch, pkv, W)
 
@@ -228,6 +232,113 @@ def main() -> int:
         },
         "decode_only": {"kernel": "pkv_paged_attn_decode", "avg_launch_us": round(decode_ms * 1e3, 3),
                         "gb_per_s": round(nbytes["decode"] / (decode_ms * 1e-3) / 1e9, 2)},
+        "cpu_baseline": cpu,
+        "wall_ms_timed_steps": round(wall_ms, 2),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_rope(args, torch, pkv, W) -> int:
+    """Decode step with RoPE applied at read on a decode workload: pkv_kv_append storing
+    un-rotated keys, then pkv_paged_attn_decode rotating query and keys in the kernel
+    (decode_rope_kernel, HBM-bound like the plain decode)."""
+    wl = W.config(args.config)
+    nbytes = algorithmic_bytes(wl)
+    dev = torch.device("cuda:0")
+
+    def t(a, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.view(dt))).to(dev)
+
+    q, k_new, v_new = t(wl["q"]), t(wl["k_new"]), t(wl["v_new"])
+    tables, positions, ctx = t(wl["tables"]), t(wl["positions"]), t(wl["context_lens"])
+    qn = None if wl["q_norm_w"] is None else t(wl["q_norm_w"])
+    kn = None if wl["k_norm_w"] is None else t(wl["k_norm_w"])
+    pool_bytes = 2 * wl["k_pool"].nbytes
+    copies = args.copies or max(2, int(np.ceil(1.0e9 / pool_bytes)))
+    k0, v0 = t(wl["k_pool"], np.int16), t(wl["v_pool"], np.int16)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    B, Hq, Hkv, D, bs = wl["B"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"]
+    split = args.split_tokens or pkv.decode_split_tokens(B, Hq, Hkv, D, bs, wl["max_context_len"])
+    ws = torch.zeros(max(pkv.decode_workspace_bytes(B, Hq, Hkv, D, bs, wl["max_context_len"],
+                                                    split), 1), dtype=torch.uint8, device=dev)
+    q_out = torch.empty_like(q)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def append(i):
+        kp, vp = pools[i % copies]
+        pkv.kv_append(q, k_new, v_new, kp, vp, tables, positions, theta=wl["theta"],
+                      q_norm_w=qn, k_norm_w=kn, eps=wl["eps"], q_out=q_out, dtype=wl["dtype"],
+                      rope_on_read=True, stream=stream)
+
+    def attend(i):
+        kp, vp = pools[i % copies]
+        pkv.paged_attn_decode(q_out, kp, vp, tables, ctx, wl["max_context_len"], wl["scale"],
+                              out=out, workspace=ws, split_tokens=split, dtype=wl["dtype"],
+                              rope_on_read=True, read_theta=wl["theta"], stream=stream)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t0 = time.perf_counter()
+    step_ms = timed(lambda i: (append(i), attend(i)))
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    attn_ms = timed(attend)
+    append_ms = timed(append)
+    step_gbs = nbytes["step"] / (step_ms * 1e-3) / 1e9
+    attn_gbs = nbytes["decode"] / (attn_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.load()
+        kp, vp = wl["k_pool"].copy(), wl["v_pool"].copy()
+        q_ref = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"],
+                                 wl["positions"], wl["q_norm_w"], wl["k_norm_w"], wl["eps"],
+                                 wl["theta"], wl["dtype"], rope_on_read=True)
+        mask = np.zeros(B, dtype=np.uint8)
+        mask[::4] = 1
+        c0 = time.perf_counter()
+        oracle.paged_attn_decode_rope(q_ref, kp, vp, wl["tables"], wl["context_lens"],
+                                      wl["theta"], wl["scale"], wl["dtype"], row_mask=mask)
+        cpu_s = time.perf_counter() - c0
+        L = wl["context_lens"].astype(np.int64)
+        kv_sample = int(L[mask.astype(bool)].sum()) * 2 * Hkv * D * 2
+        cpu = {"value": round(kv_sample / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"attention with rotation at read of {int(mask.sum())} of the {B} "
+                         f"sequences (every 4th), {cpu_s:.2f} s single-threaded"}
+
+    line = {
+        "metric": "paged-attn decode with RoPE applied at read, achieved HBM GB/s",
+        "value": round(step_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"], "data": "synthetic",
+        "tokens_per_s": round(B / (step_ms * 1e-3), 1),
+        "config": {"workload": wl["name"] + "-rope-at-read", "batch": B, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "kv_dtype": wl["dtype"], "context_tokens": int(wl["context_lens"].sum()),
+                   "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
+                   "pool_copies": copies, "split_tokens": split,
+                   "bytes_per_step": nbytes["step"]},
+        "roofline": {"bound": "hbm", "kernel": "decode_rope_kernel (pkv_paged_attn_decode)",
+                     "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": nbytes["decode"],
+                     "avg_launch_us": round(attn_ms * 1e3, 3)},
+        "append": {"kernel": "pkv_kv_append (no rotation)",
+                   "avg_launch_us": round(append_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "wall_ms_timed_steps": round(wall_ms, 2),
     }

@@ -69,15 +69,18 @@ typedef enum {
 
 /*
  * pkv_variant — layer options of the glia decoder family (page
- * "soft3/glia/run/arch/decoder/forward.rs", forward_layer), taken by the append, decode and
- * prefill calls. Passing NULL is the same as {0, 0, 0}: full rotary, no V normalisation, no
- * window (the Llama-style layer every call describes below).
+ * "soft3/glia/run/arch/decoder/forward.rs", forward_layer) and makarna's RoPE-in-attention
+ * kernels (page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock), taken by
+ * the append, decode and prefill calls. Passing NULL is the same as all fields zero: full
+ * rotary applied by the append, no V normalisation, no window (the Llama-style layer every call
+ * describes below).
  *
  * rope_dim  rotary dimension: 0 means head_dim; otherwise an even number in [2, head_dim].
  *           The pairs (i, i + rope_dim/2), i < rope_dim/2, are rotated by the angle
  *           p * rope_theta^(-2i/rope_dim) (partial rotary: a rope_dim-sized head inside the
  *           first rope_dim dims); dims rope_dim .. head_dim-1 pass through (after the optional
- *           QK-norm) unrotated. Used by the append calls (and pkv_decode_step).
+ *           QK-norm) unrotated. Used by the append calls (and pkv_decode_step), and by
+ *           pkv_paged_attn_decode when rope_on_read is set.
  * v_norm    non-zero: every new V head vector v is stored as v * (1 / sqrt(sum(v^2) / D +
  *           rms_eps)) with float arithmetic: the sum of squares accumulated in index order, one
  *           rounding per operation (no fused multiply-add), no weight. Used by the append calls.
@@ -85,15 +88,28 @@ typedef enum {
  *           sees the positions max(0, L - W) .. L - 1 only — the last W tokens, the range the
  *           page's ring cache of W slots reads (here the pool keeps every token; only the
  *           attended range shrinks). Used by the attention calls (and pkv_decode_step).
+ * rope_on_read  non-zero: RoPE moves from the append to the attention, as in makarna's fused
+ *           RoPE paged kernels. The append calls then rotate nothing (q_out is the normed query,
+ *           the pool keeps normed, un-rotated keys); pkv_paged_attn_decode rotates the query to
+ *           position L - 1 and key t to position t (the pairing and angles above, base
+ *           read_theta) before the dot products, in float with cos / sin evaluated in double.
+ *           Needs rope_dim (after the default) a multiple of 16 for the decode (UNSUPPORTED
+ *           otherwise); pkv_decode_step and pkv_paged_attn_prefill return UNSUPPORTED with it.
+ *           Keys holding +-Inf are outside what the rotated-at-read decode reproduces.
+ * read_theta  RoPE base of the rotation at read (finite, > 0); used by pkv_paged_attn_decode
+ *           when rope_on_read is set (the append calls take rope_theta as an argument).
  * A NaN that the norm, V-norm or RoPE arithmetic produces is stored as 0x7FC00000 (the
  * canonical quiet NaN) before conversion; a NaN that reaches the converter untouched keeps its
  * bits as described under pkv_kv_append.
- * Errors (INVALID_ARG): rope_dim odd, negative or above head_dim; window < 0.
+ * Errors (INVALID_ARG): rope_dim odd, negative or above head_dim; window < 0; read_theta not
+ * finite and > 0 when the decode rotates at read.
  */
 typedef struct {
     int rope_dim;
     int v_norm;
     int window;
+    int rope_on_read;
+    float read_theta;
 } pkv_variant;
 
 /*
@@ -169,7 +185,9 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *              again (the rest needs no initialisation). Calls that run concurrently (on
  *              different streams) need separate workspaces.
  * split_tokens 0 for the balanced schedule, or tokens per partition: a positive multiple of
- *              64 of at most 1022 * block_size (a partition stages its block ids in LDS)
+ *              64 of at most 1022 * block_size (a partition stages its block ids in LDS).
+ *              With rope_on_read (variant) the partitioned schedule always runs, and 0 means
+ *              pkv_decode_split_tokens(...)'s choice (size the workspace with that value).
  * variant      (host) NULL, or a window as described under pkv_variant: then only the keys
  *              max(0, L - window) .. L - 1 are attended (the partitions and tiles start at the
  *              16-token tile that holds the first of them; the rest of the context is not read)

@@ -69,13 +69,14 @@ def _stream(stream):
 
 def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, theta: float,
               q_norm_w=None, k_norm_w=None, eps: float = 1e-6, q_out=None, dtype=None,
-              rope_dim: int = 0, v_norm: bool = False, stream=None):
+              rope_dim: int = 0, v_norm: bool = False, rope_on_read: bool = False,
+              stream=None):
     """Append one token per sequence; returns q_out ([B, Hq, D] float32, normed + rotated).
 
     q_in [B,Hq,D], k_in / v_in [B,Hkv,D] float32; k_pool / v_pool [NB,bs,Hkv,D] 16-bit;
     block_tables [B,max_blocks] int32; positions [B] int32 (write slot = RoPE position).
     rope_dim: rotary dims (0 = D; partial rotary below D); v_norm: RMS-normalise each new V
-    head vector before it is stored.
+    head vector before it is stored; rope_on_read: rotate nothing (the decode rotates at read).
     """
     torch = _torch()
     B, Hq, D = q_in.shape
@@ -92,7 +93,7 @@ def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, thet
         _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
         _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
         float(eps), float(theta), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
-        _lib.variant(rope_dim, v_norm), _stream(stream))
+        _lib.variant(rope_dim, v_norm, rope_on_read=rope_on_read), _stream(stream))
     _lib.check(_lib.load().pkv_kv_append(*args), "pkv_kv_append")
     return q_out
 
@@ -109,10 +110,13 @@ def decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_context_len,
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
                       scale: float, *, out=None, workspace=None, split_tokens: int = 0,
-                      dtype=None, window: int = 0, stream=None):
+                      dtype=None, window: int = 0, rope_on_read: bool = False,
+                      read_theta: float = 0.0, rope_dim: int = 0, stream=None):
     """Decode attention for one query token per sequence; returns out [B, Hq, D] float32.
 
     window: 0, or W > 0 to attend only the last W of each sequence's context_lens tokens.
+    rope_on_read: the pool holds un-rotated keys; the query is rotated to position L - 1 and
+    key t to position t (base read_theta, rotary dims rope_dim, 0 = D) inside the kernel.
     workspace: uint8 GPU tensor of >= decode_workspace_bytes(...) bytes, zero-filled before its
     first use (the library keeps its counters zero); allocated here (zeroed) if None.
     """
@@ -121,6 +125,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
     NB, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if out is None:
         out = torch.empty_like(q)
+    if rope_on_read and not split_tokens and B and max_context_len:
+        split_tokens = decode_split_tokens(B, Hq, Hkv, D, bs, max_context_len)
     need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, split_tokens) if B else 0
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -134,7 +140,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
         _dev_ptr(context_lens, "context_lens", dtype=torch.int32, ndim=1), int(max_context_len),
         float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3), ws_ptr, ws_bytes,
         int(split_tokens), B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
-        _lib.variant(window=window), _stream(stream))
+        _lib.variant(rope_dim=rope_dim, window=window, rope_on_read=rope_on_read,
+                     read_theta=read_theta), _stream(stream))
     _lib.check(_lib.load().pkv_paged_attn_decode(*args), "pkv_paged_attn_decode")
     return out
 

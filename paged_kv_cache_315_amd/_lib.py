@@ -23,8 +23,10 @@ PKV_BF16 = 2
 
 
 class Variant(ctypes.Structure):
-    """pkv_variant: rope_dim (0 = head_dim), v_norm (0/1), window (0 = full attention)."""
-    _fields_ = [("rope_dim", ctypes.c_int), ("v_norm", ctypes.c_int), ("window", ctypes.c_int)]
+    """pkv_variant: rope_dim (0 = head_dim), v_norm (0/1), window (0 = full attention),
+    rope_on_read (0/1), read_theta (RoPE base of the rotation at read)."""
+    _fields_ = [("rope_dim", ctypes.c_int), ("v_norm", ctypes.c_int), ("window", ctypes.c_int),
+                ("rope_on_read", ctypes.c_int), ("read_theta", ctypes.c_float)]
 
 
 # every function include/pkv.h declares, with (restype, argtypes)
@@ -107,8 +109,10 @@ def check(status: int, what: str):
         raise PkvError(status, f"{what}: {lib.pkv_status_string(status).decode()}: {msg}")
 
 
-def variant(rope_dim: int = 0, v_norm: bool = False, window: int = 0):
+def variant(rope_dim: int = 0, v_norm: bool = False, window: int = 0,
+            rope_on_read: bool = False, read_theta: float = 0.0):
     """A pkv_variant argument: None (the defaults) or a pointer to the filled struct."""
-    if not rope_dim and not v_norm and not window:
+    if not rope_dim and not v_norm and not window and not rope_on_read:
         return None
-    return ctypes.pointer(Variant(int(rope_dim), int(bool(v_norm)), int(window)))
+    return ctypes.pointer(Variant(int(rope_dim), int(bool(v_norm)), int(window),
+                                  int(bool(rope_on_read)), float(read_theta)))

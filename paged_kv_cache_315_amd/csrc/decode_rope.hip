@@ -1,0 +1,346 @@
+// decode_rope.hip — paged-attention decode over a pool of un-rotated keys, with RoPE applied at
+// read (gfx950).
+//
+// What it computes (page "makarna/pkg/model/arch/hybrid_decoder.go", runHybridAttentionBlock and
+// runHybridAttentionBlockBatch: when RoPE is fused into the paged kernel, the standalone rotation
+// of Q and K is skipped, the cache receives un-rotated K and the kernel, given the RoPE base,
+// rotates them itself):
+//   out[b][h] = softmax_t(scale * (R_p q[b][h]) . (R_t K[t][g])) . V[t][g],  p = L_b - 1,
+// with R_x the rotate-half RoPE of the first rope_dim dims at position x (angle
+// x * theta^(-2i/rope_dim) for the pair (i, i + rope_dim/2)). Rotations are orthogonal and
+// commute, so (R_p q) . (R_t k) = q . (R_{t-p} k): the query is used as it is and each key is
+// turned back by delta = p - t, which only needs cos / sin of delta * f_i.
+//
+// Work decomposition: the partitioned schedule of paged_decode.hip — grid (Hkv, S, B), workgroup
+// (g, s, b) owns P = split_tokens tokens of sequence b and the G query heads of KV head g, with
+// the same workspace (partials + counters, last partition merges). Inside a workgroup every row
+// of 8-dim columns is one token: lane column c holds dims 8c .. 8c+7 of the K and V rows
+// (16-byte loads), 64 / (D/8) rows per wave, waves interleaved, the next row's K/V in flight
+// while one is computed.
+//
+// Rotation at read. rope_dim is a multiple of 16, so a column lies entirely in the first half of
+// the rotated dims, entirely in the second half, or past rope_dim. A first-half lane gets its
+// partner column (the dims rope_dim/2 further on) from the lane rope_dim/16 to its right with
+// one cross-lane permute of the raw codes, a second-half lane from the lane as far to its left:
+//   first half:  k'_i = k_i cos(delta f_i) + k_{i+h} sin(delta f_i)
+//   second half: k'_{i+h} = k_{i+h} cos(delta f_i) - k_i sin(delta f_i).
+// cos / sin of each lane's 8 pairs are evaluated in double at its first token and then advanced
+// by the fixed step of the row stride with the angle-difference formulas in float (error about
+// one ulp per step, a few hundred steps at most per partition); the rest is float arithmetic:
+// dot products reduced over the row's lanes, online softmax in exp2 units, PV on the vector ALU.
+// Keys holding +-Inf are outside what this path reproduces (Inf times a zero sine is NaN here at
+// other tokens than in a rotation by absolute positions).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+using namespace dev;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTblCap = 1024;   // block ids staged in LDS per workgroup (bounds split_tokens)
+
+__device__ __forceinline__ int clamp_len(int L, const DecodeArgs& a) {
+    const int64_t cap = min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
+    return (int)min((int64_t)L, cap);
+}
+
+__device__ __forceinline__ uint4 permute_u4(uint4 x, int src_lane) {
+    uint4 y;
+    y.x = (uint32_t)__shfl((int)x.x, src_lane);
+    y.y = (uint32_t)__shfl((int)x.y, src_lane);
+    y.z = (uint32_t)__shfl((int)x.z, src_lane);
+    y.w = (uint32_t)__shfl((int)x.w, src_lane);
+    return y;
+}
+
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
+    constexpr int R = D / 8;            // lanes per K/V row
+    constexpr int RPW = 64 / R;         // rows per wave per step
+    constexpr int STR = kWaves * RPW;   // tokens per step of the workgroup
+    static_assert(D % 32 == 0 && G >= 1 && G <= 8, "shape");
+
+    __shared__ int32_t s_tbl[kTblCap];
+    __shared__ float s_acc[kWaves][G][D];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    __shared__ int s_last;
+
+    const int g = blockIdx.x;
+    const int s = blockIdx.y;
+    const int b = blockIdx.z;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int rg = lane / R;            // row of this lane within the wave's step
+    const int d0 = 8 * (lane % R);      // first dim of this lane's column
+
+    const int L = clamp_len(a.context_lens[b], a);
+    const int P = a.split_tokens;
+    const int vis_lo = window_lo(L, a.window);
+    const int t_first = vis_lo / 16 * 16;
+    const int t_begin = t_first + s * P;
+    if (t_begin >= L) return;           // whole workgroup exits together
+    const int t_end = min(L, t_begin + P);
+    const int nsplit = (L - t_first + P - 1) / P;
+    const int Hq = a.Hkv * G;
+    const int pq = L - 1;               // position of the query
+
+    // ---- block ids of this partition -> LDS (the host keeps split_tokens within kTblCap ids)
+    const BlockDiv bdiv = make_div((uint32_t)a.bs);
+    const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+    const int first_blk = (int)bdiv.div((uint32_t)t_begin);
+    const int n_blk = min((int)bdiv.div((uint32_t)(t_end - 1)) - first_blk + 1, kTblCap);
+    const int64_t nb_max = a.num_blocks - 1;
+    for (int i = threadIdx.x; i < n_blk; i += kThreads) {
+        const int64_t id = trow[first_blk + i];
+        s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+    }
+
+    // ---- this lane's query dims, in exp2 units
+    const float qs = a.scale * kLog2e;
+    float qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float4* qp =
+            reinterpret_cast<const float4*>(a.q + ((int64_t)b * Hq + g * G + h) * D + d0);
+        const float4 x0 = qp[0], x1 = qp[1];
+        qv[h][0] = x0.x * qs; qv[h][1] = x0.y * qs; qv[h][2] = x0.z * qs; qv[h][3] = x0.w * qs;
+        qv[h][4] = x1.x * qs; qv[h][5] = x1.y * qs; qv[h][6] = x1.z * qs; qv[h][7] = x1.w * qs;
+    }
+
+    // ---- rotation role of the column, cos / sin at the first token and per step
+    const int rhalf = a.rope_dim >> 1;
+    const bool first_half = d0 < rhalf;
+    const bool rotated = d0 < a.rope_dim;
+    const int src = first_half ? lane + rhalf / 8 : (rotated ? lane - rhalf / 8 : lane);
+    const int pair0 = first_half ? d0 : d0 - rhalf;
+    const float sgn = first_half ? 1.f : -1.f;
+    const int t0 = t_begin + wave * RPW + rg;   // this lane's first token
+    float cc[8], ss[8], stc[8], sts[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        cc[j] = 1.f;
+        ss[j] = 0.f;
+        stc[j] = 1.f;
+        sts[j] = 0.f;
+    }
+    if (rotated) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const double inv = pow((double)a.rope_theta, -2.0 * (double)(pair0 + j) / a.rope_dim);
+            double sn, cs;
+            sincos((double)(pq - t0) * inv, &sn, &cs);
+            cc[j] = (float)cs;
+            ss[j] = (float)sn;
+            sincos((double)STR * inv, &sn, &cs);
+            stc[j] = (float)cs;
+            sts[j] = (float)sn;
+        }
+    }
+    __syncthreads();  // s_tbl
+
+    float m[G], lsum[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        lsum[h] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    }
+
+    const int64_t tok_stride = (int64_t)a.Hkv * D;
+    const int64_t col_off = (int64_t)g * D + d0;
+    auto row_off = [&](int t) -> int64_t {
+        const int j = (int)bdiv.div((uint32_t)t);
+        const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
+        return (blk * a.bs + (t - j * a.bs)) * tok_stride + col_off;
+    };
+
+    // every lane runs the same number of steps (rows past the partition clamp to its last row
+    // and are masked), so the cross-lane permutes and reductions see a converged wave
+    const int n_steps = (t_end - t_begin + STR - 1) / STR;
+    int t = t0;
+    uint4 kc, vc;
+    {
+        const int64_t o = row_off(min(t, t_end - 1));
+        kc = load_stream(a.k_pool + o);
+        vc = load_stream(a.v_pool + o);
+    }
+    for (int step = 0; step < n_steps; ++step) {
+        const int64_t on = row_off(min(t + STR, t_end - 1));
+        const uint4 kn = load_stream(a.k_pool + on);
+        const uint4 vn = load_stream(a.v_pool + on);
+
+        const bool valid = t < t_end && t >= vis_lo;
+        const uint4 kp = permute_u4(kc, src);
+        float kf[8], kpf[8], vf[8];
+        decode8<BF16>(kc, kf);
+        decode8<BF16>(kp, kpf);
+        decode8<BF16>(valid ? vc : make_uint4(0, 0, 0, 0), vf);
+        float kr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            kr[j] = rotated ? fmaf(kf[j], cc[j], sgn * kpf[j] * ss[j]) : kf[j];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dot = fmaf(qv[h][j], kr[j], dot);
+#pragma unroll
+            for (int off = 1; off < R; off <<= 1) dot += __shfl_xor(dot, off);
+            const float sc = valid ? dot : -INFINITY;
+            const float mn = fmaxf(m[h], sc);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float al = exp2f(m[h] - mu);
+            const float pe = exp2f(sc - mu);
+            lsum[h] = fmaf(lsum[h], al, pe);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pe, vf[j], acc[h][j] * al);
+            m[h] = mn;
+        }
+        // delta -> delta - STR: cos(a - b) = cos a cos b + sin a sin b,
+        //                       sin(a - b) = sin a cos b - cos a sin b
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float nc = fmaf(cc[j], stc[j], ss[j] * sts[j]);
+            const float ns = fmaf(ss[j], stc[j], -(cc[j] * sts[j]));
+            cc[j] = nc;
+            ss[j] = ns;
+        }
+        kc = kn;
+        vc = vn;
+        t += STR;
+    }
+
+    // ---- combine the rows of the wave (lanes of one column), then the waves through LDS
+#pragma unroll
+    for (int off = R; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(m[h], off);
+            const float lo = __shfl_xor(lsum[h], off);
+            const float mx = fmaxf(m[h], mo);
+            const float mu = mx == -INFINITY ? 0.f : mx;
+            const float e = exp2f(m[h] - mu);
+            const float eo = exp2f(mo - mu);
+            lsum[h] = fmaf(lsum[h], e, lo * eo);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float ao = __shfl_xor(acc[h][j], off);
+                acc[h][j] = fmaf(acc[h][j], e, ao * eo);
+            }
+            m[h] = mx;
+        }
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s_acc[wave][h][d0 + j] = acc[h][j];
+            if (lane == 0) {
+                s_m[wave][h] = m[h];
+                s_l[wave][h] = lsum[h];
+            }
+        }
+    }
+    __syncthreads();
+
+    float* part_acc = a.part_acc;
+    float* part_ml = a.part_ml;
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+        const int h = i / D;
+        const int d = i % D;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+        const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float e = exp2f(s_m[w][h] - M_use);
+            num = fmaf(e, s_acc[w][h][d], num);
+            den = fmaf(e, s_l[w][h], den);
+        }
+        const int hq = g * G + h;
+        if (nsplit == 1) {
+            a.out[((int64_t)b * Hq + hq) * D + d] = num / den;
+        } else {
+            const int64_t pi = ((int64_t)b * Hq + hq) * a.S + s;
+            store_shared(part_acc + pi * D + d, num);
+            if (d == 0) {
+                store_shared(part_ml + pi * 2, Mx);
+                store_shared(part_ml + pi * 2 + 1, den);
+            }
+        }
+    }
+    if (nsplit == 1) return;
+
+    // ---- the last partition of (b, g) to finish merges all of them (agent-scope atomics:
+    // partials and counters are shared by workgroups on different XCDs)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* counter = a.counters + (int64_t)b * a.Hkv + g;
+    if (threadIdx.x == 0) s_last = fetch_add_shared(counter, 1) == nsplit - 1;
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+        const int h = i / D;
+        const int d = i % D;
+        const int64_t p0 = ((int64_t)b * Hq + g * G + h) * a.S;
+        float Mx = -INFINITY;
+        for (int k = 0; k < nsplit; ++k) Mx = fmaxf(Mx, load_shared(part_ml + (p0 + k) * 2));
+        const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+        float num = 0.f, den = 0.f;
+        for (int k = 0; k < nsplit; ++k) {
+            const float e = exp2f(load_shared(part_ml + (p0 + k) * 2) - M_use);
+            den = fmaf(e, load_shared(part_ml + (p0 + k) * 2 + 1), den);
+            num = fmaf(e, load_shared(part_acc + (p0 + k) * D + d), num);
+        }
+        a.out[((int64_t)b * Hq + g * G + h) * D + d] = num / den;
+    }
+    if (threadIdx.x == 0) store_shared(counter, 0);  // ready for the next call
+}
+
+template <int D, int G, bool BF16>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+    dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)a.B);
+    hipLaunchKernelGGL((decode_rope_kernel<D, G, BF16>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return launch_typed<D, 1, BF16>(a, stream);
+        case 2: return launch_typed<D, 2, BF16>(a, stream);
+        case 3: return launch_typed<D, 3, BF16>(a, stream);
+        case 4: return launch_typed<D, 4, BF16>(a, stream);
+        case 5: return launch_typed<D, 5, BF16>(a, stream);
+        case 6: return launch_typed<D, 6, BF16>(a, stream);
+        case 7: return launch_typed<D, 7, BF16>(a, stream);
+        case 8: return launch_typed<D, 8, BF16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool BF16>
+hipError_t dispatch_d(const DecodeArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 32: return dispatch_g<32, BF16>(a, stream);
+        case 64: return dispatch_g<64, BF16>(a, stream);
+        case 128: return dispatch_g<128, BF16>(a, stream);
+        case 256: return dispatch_g<256, BF16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_rope(const DecodeArgs& a, hipStream_t stream) {
+    return a.bf16 ? dispatch_d<true>(a, stream) : dispatch_d<false>(a, stream);
+}
+
+}  // namespace pkv

@@ -151,15 +151,18 @@ pkv_status check_rope(const char* who, float theta, const float* qn, const float
     return PKV_OK;
 }
 
-// Layer options with the defaults filled in (rope_dim = D, no V norm, no window).
+// Layer options with the defaults filled in (rope_dim = D, no V norm, no window, rotation
+// applied by the append).
 struct Variant {
     int rope_dim;
     bool v_norm;
     int window;
+    bool rope_read;
+    float read_theta;
 };
 
 pkv_status resolve_variant(const char* who, const pkv_variant* v, int D, Variant& out) {
-    out = Variant{D, false, 0};
+    out = Variant{D, false, 0, false, 0.f};
     if (v == nullptr) return PKV_OK;
     if (v->rope_dim < 0 || v->rope_dim > D || (v->rope_dim & 1))
         return fail(PKV_ERR_INVALID_ARG, "%s: rope_dim=%d must be 0 or even in [2, head_dim=%d]",
@@ -168,6 +171,8 @@ pkv_status resolve_variant(const char* who, const pkv_variant* v, int D, Variant
     out.rope_dim = v->rope_dim ? v->rope_dim : D;
     out.v_norm = v->v_norm != 0;
     out.window = v->window;
+    out.rope_read = v->rope_on_read != 0;
+    out.read_theta = v->read_theta;
     return PKV_OK;
 }
 
@@ -281,7 +286,7 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
     a.D = head_dim;
     a.bs = block_size;
     a.num_blocks = num_blocks;
-    a.rope_dim = var.rope_dim;
+    a.rope_dim = var.rope_read ? 0 : var.rope_dim;  // rotation at read: the pool keeps un-rotated K
     a.v_norm = var.v_norm;
     a.bf16 = dtype == PKV_BF16;
     const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
@@ -414,9 +419,63 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                     split_tokens, (long long)max_split_for(block_size), kTblCap - 2);
     st = check_decode_shape("decode", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
+    if (var.rope_read) {
+        if (!(var.read_theta > 0.f) || !isfinite(var.read_theta))
+            return fail(PKV_ERR_INVALID_ARG, "decode: read_theta=%g must be finite and > 0",
+                        (double)var.read_theta);
+        if (var.rope_dim % 16)
+            return fail(PKV_ERR_UNSUPPORTED,
+                        "decode: rope_on_read needs rope_dim a multiple of 16 (got %d)",
+                        var.rope_dim);
+    }
     if (B == 0 || max_context_len == 0) return PKV_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
         return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer argument");
+    if (var.rope_read) {
+        // rotation at read: the partitioned schedule of decode_rope.hip
+        const int P = split_tokens > 0 ? split_tokens
+                                       : choose_split(B, num_kv_heads, max_context_len,
+                                                      block_size, device_cus());
+        if (((int64_t)max_context_len + P - 1) / P > 0x7FFFFFFF)
+            return fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions");
+        const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len, P, block_size, false);
+        if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
+            return fail(PKV_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu",
+                        workspace_bytes, wl.total);
+        char* ws = static_cast<char*>(workspace);
+        const bool has_ws = wl.total > 0;
+        pkv::DecodeArgs a{};
+        a.q = q;
+        a.k_pool = static_cast<const uint16_t*>(k_pool);
+        a.v_pool = static_cast<const uint16_t*>(v_pool);
+        a.tables = block_tables;
+        a.context_lens = context_lens;
+        a.out = out;
+        a.part_acc = has_ws ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
+        a.part_ml = has_ws ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+        a.counters = has_ws ? reinterpret_cast<int*>(ws + wl.cnt_off) : nullptr;
+        a.max_blocks = max_blocks_per_seq;
+        a.max_context_len = max_context_len;
+        a.scale = scale;
+        a.split_tokens = P;
+        a.S = (int)wl.S;
+        a.B = B;
+        a.Hq = num_q_heads;
+        a.Hkv = num_kv_heads;
+        a.D = head_dim;
+        a.bs = block_size;
+        a.num_blocks = num_blocks;
+        a.window = var.window;
+        a.bf16 = dtype == PKV_BF16;
+        a.lens_are_positions = false;
+        a.rope_theta = var.read_theta;
+        a.rope_dim = var.rope_dim;
+        const hipError_t e = pkv::launch_decode_rope(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess)
+            return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
+        return PKV_OK;
+    }
 
     const bool bal = split_tokens == 0 && balanced_ok(B, num_kv_heads, max_context_len);
     const int P = bal ? 0
@@ -452,6 +511,9 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
     Variant var;
     st = resolve_variant("decode_step", variant, head_dim, var);
     if (st != PKV_OK) return st;
+    if (var.rope_read)
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "decode_step: rope_on_read is served by pkv_kv_append + pkv_paged_attn_decode");
     st = check_decode_shape("decode_step", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
     if (B == 0) return PKV_OK;
@@ -567,7 +629,7 @@ pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float*
     a.D = head_dim;
     a.bs = block_size;
     a.num_blocks = num_blocks;
-    a.rope_dim = var.rope_dim;
+    a.rope_dim = var.rope_read ? 0 : var.rope_dim;  // rotation at read: the pool keeps un-rotated K
     a.v_norm = var.v_norm;
     a.bf16 = dtype == PKV_BF16;
     const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
@@ -600,6 +662,8 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
     Variant var;
     st = resolve_variant("prefill", variant, head_dim, var);
     if (st != PKV_OK) return st;
+    if (var.rope_read)
+        return fail(PKV_ERR_UNSUPPORTED, "prefill: rope_on_read is not built for chunked prefill");
     st = check_decode_shape("prefill", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
     if (num_tokens < 0 || max_chunk < 0 || max_context_len < 0)

@@ -82,10 +82,16 @@ struct DecodeArgs {
     int window;               // sliding window (0: every token)
     bool bf16;
     bool lens_are_positions;  // context_lens holds positions: L = p + 1 (fused-step fallback)
+    float rope_theta;         // decode_rope.hip only: RoPE base of the rotation at read
+    int rope_dim;             // decode_rope.hip only: rotated dims, a multiple of 16
 };
 
 // Launches the decode kernel (partitions + in-kernel merge by the last partition).
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Decode over un-rotated keys, rotating query and keys at read (decode_rope.hip); the same
+// partitions, workspace layout and merge as launch_paged_decode.
+hipError_t launch_decode_rope(const DecodeArgs& a, hipStream_t stream);
 
 // Balanced schedule (decode_balanced.hip): one resident workgroup per slot, equal tile ranges.
 constexpr int kMaxBalancedBatch = 2048;  // sequences whose tile prefix fits in LDS

@@ -82,6 +82,13 @@ def test_append_argument_checks(lib, kw, status):
     (dict(split=1024, bs=1), 1),                      # 1024 > 1022 * block_size
     (dict(var=_lib.variant(window=-5)), 1), (dict(var=_lib.variant(rope_dim=7)), 1),
     (dict(var=_lib.variant(window=100)), 3),          # a valid window reaches the workspace check
+    # rotation at read: a base is required, rope_dim must be a multiple of 16, the partitioned
+    # schedule's workspace is checked
+    (dict(var=_lib.variant(rope_on_read=True)), 1),
+    (dict(var=_lib.variant(rope_on_read=True, read_theta=float("nan"))), 1),
+    (dict(var=_lib.variant(rope_dim=8, rope_on_read=True, read_theta=1e4)), 2),
+    (dict(var=_lib.variant(rope_on_read=True, read_theta=1e4)), 3),
+    (dict(var=_lib.variant(rope_dim=32, rope_on_read=True, read_theta=1e4, window=9)), 3),
 ])
 def test_decode_argument_checks(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -120,9 +127,18 @@ def _prefill(lib, **kw):
     (dict(ws=FAKE, wsb=16), 3), (dict(B=0), 0), (dict(N=0), 0), (dict(mc=0), 0),
     (dict(B=70000, mc=64), 2), (dict(var=_lib.variant(window=-1)), 1),
     (dict(var=_lib.variant(window=64)), 3),
+    (dict(var=_lib.variant(rope_on_read=True, read_theta=1e4)), 2),
 ])
 def test_prefill_argument_checks(lib, kw, status):
     assert _prefill(lib, **kw) == status
+
+
+def test_decode_step_rejects_rotation_at_read(lib):
+    var = _lib.variant(rope_on_read=True, read_theta=1e4)
+    st = lib.pkv_decode_step(FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000), FAKE, FAKE, FAKE, 4, FAKE,
+                             None, None, 1e-6, 1e4, 0.125, FAKE, None, 0, 2, 4, 2, 64, 16, 16, 1,
+                             var, None)
+    assert st == 2 and b"rope_on_read" in lib.pkv_last_error()
 
 
 def test_workspace_formula(lib):
