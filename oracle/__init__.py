@@ -24,7 +24,15 @@ LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
 
 F16 = 1
 BF16 = 2
-DTYPES = {"f16": F16, "fp16": F16, "bf16": BF16}
+F32 = 3
+DTYPES = {"f16": F16, "fp16": F16, "bf16": BF16, "f32": F32}
+
+
+def _check_pools(k_pool, v_pool, dtype):
+    """Pools are uint16 codes, or for f32 pools float32 / uint32 arrays (the float bits)."""
+    want = (np.float32, np.uint32) if _dtype_code(dtype) == F32 else (np.uint16,)
+    assert k_pool.dtype in want and v_pool.dtype in want, (k_pool.dtype, dtype)
+    assert k_pool.flags["C_CONTIGUOUS"] and v_pool.flags["C_CONTIGUOUS"]
 
 OK = 0
 ERR_ARG = 1
@@ -183,8 +191,7 @@ def kv_append(q_in, k_in, v_in, k_pool, v_pool, tables, positions, q_norm_w, k_n
     v_in = np.ascontiguousarray(v_in, dtype=np.float32)
     tables = np.ascontiguousarray(tables, dtype=np.int32)
     positions = np.ascontiguousarray(positions, dtype=np.int32)
-    assert k_pool.dtype == np.uint16 and v_pool.dtype == np.uint16
-    assert k_pool.flags["C_CONTIGUOUS"] and v_pool.flags["C_CONTIGUOUS"]
+    _check_pools(k_pool, v_pool, dtype)
     B, Hq, D = q_in.shape
     Hkv = k_in.shape[1]
     NB, bs = k_pool.shape[0], k_pool.shape[1]
@@ -278,8 +285,7 @@ def prefill_append(q_in, k_in, v_in, k_pool, v_pool, tables, cu_seqlens, start_p
     tables = np.ascontiguousarray(tables, dtype=np.int32)
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     start = np.ascontiguousarray(start_pos, dtype=np.int32)
-    assert k_pool.dtype == np.uint16 and v_pool.dtype == np.uint16
-    assert k_pool.flags["C_CONTIGUOUS"] and v_pool.flags["C_CONTIGUOUS"]
+    _check_pools(k_pool, v_pool, dtype)
     N, Hq, D = q_in.shape
     Hkv = k_in.shape[1]
     B = len(start)

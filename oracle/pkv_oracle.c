@@ -64,6 +64,7 @@
 
 #define PKVO_F16 1
 #define PKVO_BF16 2
+#define PKVO_F32 3  /* float32 pool elements (no conversion) */
 
 /* Planted mistakes for the tests that prove the pins bite (0 = the oracle as specified).
  * Each mutant is a plausible slip: a dropped term, a wrong sign or index, an off-by-one. */
@@ -187,6 +188,25 @@ static float decode(uint16_t c, int dtype)
     return dtype == PKVO_F16 ? pkvo_f16_to_f32(c) : pkvo_bf16_to_f32(c);
 }
 
+/* Pool elements: 16-bit codes, or (PKVO_F32) the float itself — [MK-KV] Append copies float32
+ * rows into a float32 block unchanged, and [MK-DEC] dispatches float32 KV to its plain paged
+ * kernel. A NaN from the norm / RoPE arithmetic is already canonical (R-NAN); a NaN input that
+ * reaches the pool untouched keeps its bits, as it does through the 16-bit converters. */
+static float pool_get(const void* pool, int64_t o, int dtype)
+{
+    if (dtype == PKVO_F32)
+        return ((const float*)pool)[o];
+    return decode(((const uint16_t*)pool)[o], dtype);
+}
+
+static void pool_put(void* pool, int64_t o, float x, int dtype)
+{
+    if (dtype == PKVO_F32)
+        ((float*)pool)[o] = x;
+    else
+        ((uint16_t*)pool)[o] = encode(x, dtype);
+}
+
 /* Convert n floats to codes (array form for the tests). */
 void pkvo_encode_array(const float* x, uint16_t* out, int64_t n, int dtype)
 {
@@ -297,7 +317,7 @@ static int64_t pool_offset(int64_t blk, int slot, int g, int d, int bs, int Hkv,
  * (table_row[pos / bs], pos % bs). Returns PKVO_ERR_RANGE (storing nothing) if the position or
  * its block id is out of range. tmp / rot: scratch of D floats. */
 static int append_token(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                        uint16_t* k_pool, uint16_t* v_pool, const int32_t* table_row,
+                        void* k_pool, void* v_pool, const int32_t* table_row,
                         int max_blocks, int pos, const float* q_norm_w, const float* k_norm_w,
                         float eps, float theta, int rope_dim, int v_norm, int Hq, int Hkv, int D,
                         int bs, int64_t num_blocks, int dtype, float* tmp, float* rot)
@@ -334,8 +354,8 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
         }
         for (int d = 0; d < D; ++d) {
             const int64_t o = pool_offset(blk, slot, g, d, bs, Hkv, D);
-            k_pool[o] = encode(rot[d], dtype);
-            v_pool[o] = encode(v[d], dtype);
+            pool_put(k_pool, o, rot[d], dtype);
+            pool_put(v_pool, o, v[d], dtype);
         }
     }
     return PKVO_OK;
@@ -355,7 +375,7 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
  * Returns PKVO_ERR_RANGE (and writes nothing more) if a position or block id is out of range.
  * ------------------------------------------------------------------------------------------ */
 int pkvo_kv_append_v(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                     uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                     void* k_pool, void* v_pool, const int32_t* tables, int max_blocks,
                      const int32_t* positions, const float* q_norm_w, const float* k_norm_w,
                      float eps, float theta, int rope_dim, int v_norm, int B, int Hq, int Hkv,
                      int D, int bs, int64_t num_blocks, int dtype)
@@ -386,7 +406,7 @@ int pkvo_kv_append_v(const float* q_in, const float* k_in, const float* v_in, fl
 }
 
 int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                   uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                   void* k_pool, void* v_pool, const int32_t* tables, int max_blocks,
                    const int32_t* positions, const float* q_norm_w, const float* k_norm_w,
                    float eps, float theta, int B, int Hq, int Hkv, int D, int bs,
                    int64_t num_blocks, int dtype)
@@ -409,7 +429,7 @@ int pkvo_kv_append(const float* q_in, const float* k_in, const float* v_in, floa
  * with a chunk split over two calls, and the per-token rows stored where the table says.
  * ------------------------------------------------------------------------------------------ */
 int pkvo_prefill_append_v(const float* q_in, const float* k_in, const float* v_in,
-                          float* q_out, uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables,
+                          float* q_out, void* k_pool, void* v_pool, const int32_t* tables,
                           int max_blocks, const int32_t* cu_seqlens, const int32_t* start_pos,
                           const float* q_norm_w, const float* k_norm_w, float eps, float theta,
                           int rope_dim, int v_norm, int B, int Hq, int Hkv, int D, int bs,
@@ -447,7 +467,7 @@ int pkvo_prefill_append_v(const float* q_in, const float* k_in, const float* v_i
 }
 
 int pkvo_prefill_append(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                        uint16_t* k_pool, uint16_t* v_pool, const int32_t* tables, int max_blocks,
+                        void* k_pool, void* v_pool, const int32_t* tables, int max_blocks,
                         const int32_t* cu_seqlens, const int32_t* start_pos,
                         const float* q_norm_w, const float* k_norm_w, float eps, float theta,
                         int B, int Hq, int Hkv, int D, int bs, int64_t num_blocks, int dtype)
@@ -478,7 +498,7 @@ static void rope_double(const double* x, int D, int rope_dim, int pos, double th
  * sequence whose block list is table_row; writes out_row [Hq, D]. kc / vc: scratch of
  * L * Hkv * D floats, e: scratch of L doubles. read_theta > 0 (R-READ): the query is rotated to
  * position L - 1 and key t to position t (first rope_dim dims, double) before the dot product. */
-static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t* v_pool,
+static int attend_row(const float* q_row, const void* k_pool, const void* v_pool,
                       const int32_t* table_row, int max_blocks, int L, int window, float scale,
                       float* out_row, int Hq, int Hkv, int D, int bs, int64_t num_blocks,
                       int dtype, float* kc, float* vc, double* e, double read_theta,
@@ -499,8 +519,8 @@ static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t
         for (int g = 0; g < Hkv; ++g)
             for (int d = 0; d < D; ++d) {
                 const int64_t o = pool_offset(blk, (t + (MUT(5) ? 1 : 0)) % bs, g, d, bs, Hkv, D);
-                kc[((int64_t)i * Hkv + g) * D + d] = decode(k_pool[o], dtype);
-                vc[((int64_t)i * Hkv + g) * D + d] = decode(v_pool[o], dtype);
+                kc[((int64_t)i * Hkv + g) * D + d] = pool_get(k_pool, o, dtype);
+                vc[((int64_t)i * Hkv + g) * D + d] = pool_get(v_pool, o, dtype);
             }
     }
     const int qpos = L - 1;
@@ -551,7 +571,7 @@ static int attend_row(const float* q_row, const uint16_t* k_pool, const uint16_t
 
 /* Runs attend_row over n rows: row r reads q + r*Hq*D, the block list of sequence seq[r] and
  * L = lens[r] tokens, writes out + r*Hq*D (rows with row_mask[r] == 0 are skipped). */
-static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+static int attend_rows(const float* q, const void* k_pool, const void* v_pool,
                        const int32_t* tables, int max_blocks, const int* seq, const int* lens,
                        int window, float scale, float* out, int n, int Hq, int Hkv, int D, int bs,
                        int64_t num_blocks, int dtype, const uint8_t* row_mask, double read_theta,
@@ -594,7 +614,7 @@ static int attend_rows(const float* q, const uint16_t* k_pool, const uint16_t* v
  * Pinned by: brute force against an independent numpy formulation, closed forms (L = 1,
  * K = 0, V[t] = t), block-permutation invariance, GQA = MHA with duplicated heads.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_paged_attn_decode_v(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+int pkvo_paged_attn_decode_v(const float* q, const void* k_pool, const void* v_pool,
                              const int32_t* tables, int max_blocks, const int32_t* context_lens,
                              int window, float scale, float* out, int B, int Hq, int Hkv, int D,
                              int bs, int64_t num_blocks, int dtype, const uint8_t* row_mask)
@@ -632,7 +652,7 @@ int pkvo_paged_attn_decode_v(const float* q, const uint16_t* k_pool, const uint1
  * the output unchanged), an independent numpy complex-exponential formulation, and a planted
  * off-by-one key position that those catch.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_paged_attn_decode_rope(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+int pkvo_paged_attn_decode_rope(const float* q, const void* k_pool, const void* v_pool,
                                 const int32_t* tables, int max_blocks,
                                 const int32_t* context_lens, int window, float theta,
                                 int rope_dim, float scale, float* out, int B, int Hq, int Hkv,
@@ -661,7 +681,7 @@ int pkvo_paged_attn_decode_rope(const float* q, const uint16_t* k_pool, const ui
     return status;
 }
 
-int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+int pkvo_paged_attn_decode(const float* q, const void* k_pool, const void* v_pool,
                            const int32_t* tables, int max_blocks, const int32_t* context_lens,
                            float scale, float* out, int B, int Hq, int Hkv, int D, int bs,
                            int64_t num_blocks, int dtype, const uint8_t* row_mask)
@@ -683,7 +703,7 @@ int pkvo_paged_attn_decode(const float* q, const uint16_t* k_pool, const uint16_
  * numpy formulation with an explicit causal mask, insensitivity of each row to the K/V of later
  * positions, and equality of one call with a chunk split over two calls.
  * ------------------------------------------------------------------------------------------ */
-int pkvo_paged_attn_prefill_v(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+int pkvo_paged_attn_prefill_v(const float* q, const void* k_pool, const void* v_pool,
                               const int32_t* tables, int max_blocks, const int32_t* cu_seqlens,
                               const int32_t* start_pos, int window, float scale, float* out,
                               int B, int Hq, int Hkv, int D, int bs, int64_t num_blocks,
@@ -716,7 +736,7 @@ int pkvo_paged_attn_prefill_v(const float* q, const uint16_t* k_pool, const uint
     return status;
 }
 
-int pkvo_paged_attn_prefill(const float* q, const uint16_t* k_pool, const uint16_t* v_pool,
+int pkvo_paged_attn_prefill(const float* q, const void* k_pool, const void* v_pool,
                             const int32_t* tables, int max_blocks, const int32_t* cu_seqlens,
                             const int32_t* start_pos, float scale, float* out, int B, int Hq,
                             int Hkv, int D, int bs, int64_t num_blocks, int dtype,

@@ -28,8 +28,10 @@ import numpy as np
 # stream ids
 S_CTX, S_PERM, S_KPOOL, S_VPOOL, S_Q, S_KNEW, S_VNEW, S_NORM, S_EDGE_POS, S_EDGE_VAL = range(10)
 
-# quiet-NaN codes used to poison every pool element that no valid token owns
-POISON = {"f16": 0x7E00, "bf16": 0x7FC0}
+# quiet-NaN codes used to poison every pool element that no valid token owns (f32 pools hold
+# the float bits themselves, as uint32)
+POISON = {"f16": 0x7E00, "bf16": 0x7FC0, "f32": 0x7FC00000}
+POOL_NP = {"f16": np.uint16, "bf16": np.uint16, "f32": np.uint32}
 
 EDGE_VALUES = np.array([70000.0, -70000.0, 1e-7, np.nan], dtype=np.float32)
 
@@ -39,7 +41,9 @@ def _rng(wid: int, stream: int) -> np.random.Generator:
 
 
 def _to_codes(x: np.ndarray, dtype: str) -> np.ndarray:
-    """float32 -> 16-bit codes with a library cast (inputs only)."""
+    """float32 -> pool codes: 16-bit with a library cast, or the float bits (inputs only)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     import torch
@@ -49,7 +53,7 @@ def _to_codes(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def _fill_pool(rng: np.random.Generator, shape, dtype: str, std: float) -> np.ndarray:
     """N(0, std^2) codes, drawn in chunks of blocks to bound host memory."""
-    pool = np.empty(shape, dtype=np.uint16)
+    pool = np.empty(shape, dtype=POOL_NP[dtype])
     nb = shape[0]
     per_block = int(np.prod(shape[1:]))
     chunk = max(1, (1 << 24) // per_block)

@@ -146,6 +146,9 @@ def pin_rope_norm_and_relative_position(lib):
 
 # ------------------------------------------------------------------ attention
 def _decode_np(pool: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        with np.errstate(invalid="ignore"):   # signalling-NaN bits in a pool are data
+            return pool.view(np.float32).astype(np.float64)
     if dtype == "f16":
         return pool.view(np.float16).astype(np.float64)
     return (pool.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -654,6 +657,31 @@ def pin_rope_read_append_stores_unrotated(lib):
         blk = wl["tables"][b, p // bs]
         assert np.array_equal(kp[blk, p % bs], wl["k_new"][b].astype(np.float16).view(np.uint16))
         assert np.array_equal(vp[blk, p % bs], wl["v_new"][b].astype(np.float16).view(np.uint16))
+
+
+# ------------------------------------------------------------------ float32 pools
+def pin_f32_pool_step(lib):
+    """float32 pools (the page's Append copies float32 rows unchanged): the stored K row is the
+    rotated key (complex form, within 1 ulp), the stored V row is the input's bits (a NaN
+    payload included), nothing else changes, and attention matches the numpy formulation."""
+    wl = W.make_workload(121, [3, 20, 47], 4, 2, 64, 8, "f32", 1e4, spare_blocks=1)
+    wl["v_new"][1, 0, 5] = np.array([0x7F800123], np.uint32).view(np.float32)[0]
+    q_out, out, kp, vp = oracle.decode_step(wl, lib=lib)
+    bs = kp.shape[1]
+    written = np.zeros(kp.shape[:3], bool)
+    for b, p in enumerate(wl["positions"]):
+        blk = wl["tables"][b, p // bs]
+        written[blk, p % bs] = True
+        for g in range(2):
+            ref = _rope_complex(wl["k_new"][b, g], int(p), wl["theta"])
+            assert _ulps(kp[blk, p % bs, g].view(np.float32), ref).max() <= 1
+        assert np.array_equal(vp[blk, p % bs], wl["v_new"][b].view(np.uint32))
+    assert np.array_equal(kp[~written], wl["k_pool"][~written])
+    assert np.array_equal(vp[~written], wl["v_pool"][~written])
+    ref = numpy_attention(q_out, kp, vp, wl["tables"], wl["context_lens"], wl["scale"], "f32")
+    fin = np.isfinite(ref)
+    np.testing.assert_allclose(out[fin], ref[fin], rtol=2.5e-7, atol=1e-12)
+    assert np.array_equal(np.isnan(out), np.isnan(ref))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
