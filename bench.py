@@ -63,11 +63,12 @@ def algorithmic_bytes(wl: dict) -> dict:
     """Bytes the step must move (each input read once, each output written once)."""
     B, Hq, Hkv, D, bs = wl["B"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"]
     L = wl["context_lens"].astype(np.int64)
-    kv = int(L.sum()) * 2 * Hkv * D * 2
+    E = 4 if wl["dtype"] == "f32" else 2           # bytes per pool element
+    kv = int(L.sum()) * 2 * Hkv * D * E
     tables = int(((L + bs - 1) // bs).sum()) * 4
     decode = kv + B * Hq * D * 4 * 2 + tables + B * 4
     norm = 2 * D * 4 if wl["q_norm_w"] is not None else 0
-    append = B * (Hq + 2 * Hkv) * D * 4 + B * Hq * D * 4 + 2 * B * Hkv * D * 2 + B * 4 * 2 + norm
+    append = B * (Hq + 2 * Hkv) * D * 4 + B * Hq * D * 4 + 2 * B * Hkv * D * E + B * 4 * 2 + norm
     return {"kv": kv, "decode": decode, "append": append, "step": decode + append}
 
 
@@ -80,12 +81,13 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="pool copies (0: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--workload", choices=["decode", "prefill", "spec", "rope"],
+    ap.add_argument("--workload", choices=["decode", "prefill", "spec", "rope", "f32"],
                     default="decode",
                     help="decode: the decode step (default); prefill / spec: chunked prefill "
                          "(4 x 512-token chunks) / 4 draft tokens per sequence, append + "
                          "causal paged attention; rope: the decode step with RoPE applied at "
-                         "read (un-rotated pool), append + decode")
+                         "read (un-rotated pool), append + decode; f32: the decode step over "
+                         "float32 pools, append + decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -112,7 +114,7 @@ def main() -> int:
                           "bytes_written_per_copy": 1 << 30, "copies": 5}))
         return 0
     pkv._lib.load()  # fail loudly before any work if the HIP library is missing
-    if args.workload == "rope":
+    if args.workload in ("rope", "f32"):
         return run_rope(args, torch, pkv, W)
     if args.workload != "decode":
         return run_prefill(args, torch, pkv, W)
@@ -240,10 +242,15 @@ def main() -> int:
 
 
 def run_rope(args, torch, pkv, W) -> int:
-    """Decode step with RoPE applied at read on a decode workload: pkv_kv_append storing
-    un-rotated keys, then pkv_paged_attn_decode rotating query and keys in the kernel
-    (decode_rope_kernel, HBM-bound like the plain decode)."""
+    """Decode step on the vector-ALU kernel of decode_rope.hip, append + decode: with RoPE
+    applied at read (--workload rope: pkv_kv_append storing un-rotated keys, the decode rotating
+    query and keys), or over float32 pools (--workload f32: the same lengths and shapes with
+    float32 K/V, rotation by the append). HBM-bound like the plain decode."""
+    rope = args.workload == "rope"
     wl = W.config(args.config)
+    if not rope:
+        wl = W.make_workload(wl["wid"], wl["positions"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"],
+                             "f32", wl["theta"], name=wl["name"] + "-f32")
     nbytes = algorithmic_bytes(wl)
     dev = torch.device("cuda:0")
 
@@ -256,7 +263,8 @@ def run_rope(args, torch, pkv, W) -> int:
     kn = None if wl["k_norm_w"] is None else t(wl["k_norm_w"])
     pool_bytes = 2 * wl["k_pool"].nbytes
     copies = args.copies or max(2, int(np.ceil(1.0e9 / pool_bytes)))
-    k0, v0 = t(wl["k_pool"], np.int16), t(wl["v_pool"], np.int16)
+    pool_view = np.int16 if rope else np.int32
+    k0, v0 = t(wl["k_pool"], pool_view), t(wl["v_pool"], pool_view)
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     B, Hq, Hkv, D, bs = wl["B"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"]
     split = args.split_tokens or pkv.decode_split_tokens(B, Hq, Hkv, D, bs, wl["max_context_len"])
@@ -270,13 +278,13 @@ def run_rope(args, torch, pkv, W) -> int:
         kp, vp = pools[i % copies]
         pkv.kv_append(q, k_new, v_new, kp, vp, tables, positions, theta=wl["theta"],
                       q_norm_w=qn, k_norm_w=kn, eps=wl["eps"], q_out=q_out, dtype=wl["dtype"],
-                      rope_on_read=True, stream=stream)
+                      rope_on_read=rope, stream=stream)
 
     def attend(i):
         kp, vp = pools[i % copies]
         pkv.paged_attn_decode(q_out, kp, vp, tables, ctx, wl["max_context_len"], wl["scale"],
                               out=out, workspace=ws, split_tokens=split, dtype=wl["dtype"],
-                              rope_on_read=True, read_theta=wl["theta"], stream=stream)
+                              rope_on_read=rope, read_theta=wl["theta"], stream=stream)
 
     def timed(fn):
         for i in range(args.warmup):
@@ -306,27 +314,34 @@ def run_rope(args, torch, pkv, W) -> int:
         kp, vp = wl["k_pool"].copy(), wl["v_pool"].copy()
         q_ref = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], kp, vp, wl["tables"],
                                  wl["positions"], wl["q_norm_w"], wl["k_norm_w"], wl["eps"],
-                                 wl["theta"], wl["dtype"], rope_on_read=True)
+                                 wl["theta"], wl["dtype"], rope_on_read=rope)
         mask = np.zeros(B, dtype=np.uint8)
         mask[::4] = 1
         c0 = time.perf_counter()
-        oracle.paged_attn_decode_rope(q_ref, kp, vp, wl["tables"], wl["context_lens"],
-                                      wl["theta"], wl["scale"], wl["dtype"], row_mask=mask)
+        if rope:
+            oracle.paged_attn_decode_rope(q_ref, kp, vp, wl["tables"], wl["context_lens"],
+                                          wl["theta"], wl["scale"], wl["dtype"], row_mask=mask)
+        else:
+            oracle.paged_attn_decode(q_ref, kp, vp, wl["tables"], wl["context_lens"],
+                                     wl["scale"], wl["dtype"], row_mask=mask)
         cpu_s = time.perf_counter() - c0
         L = wl["context_lens"].astype(np.int64)
-        kv_sample = int(L[mask.astype(bool)].sum()) * 2 * Hkv * D * 2
+        E = 4 if wl["dtype"] == "f32" else 2
+        kv_sample = int(L[mask.astype(bool)].sum()) * 2 * Hkv * D * E
         cpu = {"value": round(kv_sample / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
-               "sample": f"attention with rotation at read of {int(mask.sum())} of the {B} "
-                         f"sequences (every 4th), {cpu_s:.2f} s single-threaded"}
+               "sample": f"attention of {int(mask.sum())} of the {B} sequences (every 4th), "
+                         f"{cpu_s:.2f} s single-threaded"}
 
     line = {
-        "metric": "paged-attn decode with RoPE applied at read, achieved HBM GB/s",
+        "metric": ("paged-attn decode with RoPE applied at read, achieved HBM GB/s" if rope
+                   else "paged-attn decode over float32 KV pools, achieved HBM GB/s"),
         "value": round(step_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"], "data": "synthetic",
         "tokens_per_s": round(B / (step_ms * 1e-3), 1),
-        "config": {"workload": wl["name"] + "-rope-at-read", "batch": B, "num_q_heads": Hq,
+        "config": {"workload": wl["name"] + ("-rope-at-read" if rope else ""), "batch": B,
+                   "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
                    "kv_dtype": wl["dtype"], "context_tokens": int(wl["context_lens"].sum()),
                    "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
@@ -337,7 +352,7 @@ def run_rope(args, torch, pkv, W) -> int:
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": nbytes["decode"],
                      "avg_launch_us": round(attn_ms * 1e3, 3)},
-        "append": {"kernel": "pkv_kv_append (no rotation)",
+        "append": {"kernel": "pkv_kv_append" + (" (no rotation)" if rope else " (float32 rows)"),
                    "avg_launch_us": round(append_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "wall_ms_timed_steps": round(wall_ms, 2),

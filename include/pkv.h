@@ -28,8 +28,8 @@
  *   - Pointers marked (device) are HIP device pointers owned by the caller; the library never
  *     allocates, frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream) and the call returns as soon as it is enqueued.
- *   - Pools: k_pool and v_pool are two arrays of 16-bit codes shaped
- *     [num_blocks, block_size, num_kv_heads, head_dim], row-major: element (blk, slot, g, d)
+ *   - Pools: k_pool and v_pool are two arrays of 16-bit codes (or float32 values, PKV_F32)
+ *     shaped [num_blocks, block_size, num_kv_heads, head_dim], row-major: element (blk, slot, g, d)
  *     is at ((blk * block_size + slot) * num_kv_heads + g) * head_dim + d. Offsets are 64-bit.
  *   - block_tables: int32 [B, max_blocks_per_seq], row-major; row b lists the physical block
  *     ids of sequence b in logical order. Entries past a sequence's length are never read.
@@ -64,7 +64,14 @@ typedef enum {
 
 typedef enum {
     PKV_F16 = 1,  /* IEEE binary16 */
-    PKV_BF16 = 2  /* bfloat16 */
+    PKV_BF16 = 2, /* bfloat16 */
+    PKV_F32 = 3   /* float32 elements, stored unchanged (page "makarna/pkg/kvcache/paged_cache.go",
+                     Append copies float32 rows as they are; page "makarna/pkg/model/arch/
+                     hybrid_decoder.go" sends float32 KV to its plain paged kernel). Taken by
+                     pkv_kv_append, pkv_prefill_append and pkv_paged_attn_decode (which then runs
+                     the partitioned vector-ALU kernel of the rotation-at-read path, rotating
+                     only with rope_on_read); pkv_decode_step and pkv_paged_attn_prefill return
+                     UNSUPPORTED for it. */
 } pkv_dtype;
 
 /*

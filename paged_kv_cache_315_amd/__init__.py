@@ -14,9 +14,10 @@ from __future__ import annotations
 import ctypes
 
 from . import _lib
-from ._lib import PKV_BF16, PKV_F16, PkvError
+from ._lib import PKV_BF16, PKV_F16, PKV_F32, PkvError
 
-__all__ = ["kv_append", "paged_attn_decode", "decode_step", "decode_workspace_bytes",
+__all__ = ["PKV_F16", "PKV_BF16", "PKV_F32", "kv_append", "paged_attn_decode", "decode_step",
+           "decode_workspace_bytes",
            "prefill_append", "paged_attn_prefill", "prefill_workspace_bytes", "prefill_step",
            "decode_step_workspace_bytes", "append_then_decode", "decode_split_tokens", "validate_tables", "version",
            "PkvError", "pool_dtype_code"]
@@ -32,15 +33,23 @@ def version() -> str:
 
 
 def pool_dtype_code(pool, dtype=None) -> int:
-    """PKV_F16 / PKV_BF16 from an explicit name or from the pool tensor's dtype."""
+    """PKV_F16 / PKV_BF16 / PKV_F32 from an explicit name or from the pool tensor's dtype."""
     torch = _torch()
     if dtype is not None:
-        return {"f16": PKV_F16, "fp16": PKV_F16, "bf16": PKV_BF16}[dtype]
+        return {"f16": PKV_F16, "fp16": PKV_F16, "bf16": PKV_BF16, "f32": PKV_F32}[dtype]
     if pool.dtype == torch.float16:
         return PKV_F16
     if pool.dtype == torch.bfloat16:
         return PKV_BF16
-    raise ValueError("pool dtype must be float16 or bfloat16, or pass dtype='f16'|'bf16'")
+    if pool.dtype == torch.float32:
+        return PKV_F32
+    raise ValueError("pool dtype must be float16, bfloat16 or float32, or pass "
+                     "dtype='f16'|'bf16'|'f32'")
+
+
+def _pool_elem(pool, dtype) -> int:
+    """Bytes per pool element the call expects: 4 for float32 pools, else 2."""
+    return 4 if pool_dtype_code(pool, dtype) == PKV_F32 else 2
 
 
 def _dev_ptr(t, name, *, dtype=None, ndim=None, elem_size=None):
@@ -88,7 +97,8 @@ def kv_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, thet
     args = (
         _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
         _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
-        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2), _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
         _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
         _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
         _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
@@ -134,8 +144,9 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     f32 = torch.float32
     args = (
-        _dev_ptr(q, "q", dtype=f32, ndim=3), _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2),
-        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(q, "q", dtype=f32, ndim=3),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
         _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
         _dev_ptr(context_lens, "context_lens", dtype=torch.int32, ndim=1), int(max_context_len),
         float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3), ws_ptr, ws_bytes,
@@ -179,7 +190,8 @@ def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, th
     args = (
         _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
         _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
-        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2), _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
         _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
         _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
         _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
@@ -242,8 +254,8 @@ def prefill_append(q_in, k_in, v_in, k_pool, v_pool, block_tables, cu_seqlens, s
     args = (
         _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
         _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
-        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2),
-        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
         _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
         _dev_ptr(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1),
         _dev_ptr(start_pos, "start_pos", dtype=torch.int32, ndim=1),
@@ -282,8 +294,9 @@ def paged_attn_prefill(q, k_pool, v_pool, block_tables, cu_seqlens, start_pos, m
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     f32 = torch.float32
     args = (
-        _dev_ptr(q, "q", dtype=f32, ndim=3), _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=2),
-        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=2),
+        _dev_ptr(q, "q", dtype=f32, ndim=3),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
         _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
         _dev_ptr(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1),
         _dev_ptr(start_pos, "start_pos", dtype=torch.int32, ndim=1), int(max_chunk),

@@ -19,6 +19,7 @@ PKV_ERR_WORKSPACE = 3
 PKV_ERR_HIP = 4
 PKV_F16 = 1
 PKV_BF16 = 2
+PKV_F32 = 3
 
 
 

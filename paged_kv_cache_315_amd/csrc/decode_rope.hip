@@ -30,6 +30,10 @@
 // dot products reduced over the row's lanes, online softmax in exp2 units, PV on the vector ALU.
 // Keys holding +-Inf are outside what this path reproduces (Inf times a zero sine is NaN here at
 // other tokens than in a rotation by absolute positions).
+//
+// The same kernel serves float32 pools (page "makarna/pkg/model/arch/hybrid_decoder.go":
+// float32 KV goes to the plain paged kernel): a lane then loads its 8 dims as two 16-byte
+// pieces; with rope_dim = 0 no key is rotated and the kernel is a plain paged decode.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -47,6 +51,40 @@ __device__ __forceinline__ int clamp_len(int L, const DecodeArgs& a) {
     return (int)min((int64_t)L, cap);
 }
 
+enum ElemKind { kF16 = 0, kBF16 = 1, kF32 = 2 };
+
+// 8 consecutive pool elements of one row: one 16-byte piece of codes, or two of floats.
+template <int EK>
+struct Row8 {
+    static constexpr int NW = EK == kF32 ? 2 : 1;
+    uint4 w[NW];
+};
+
+template <int EK>
+__device__ __forceinline__ Row8<EK> load_row8(const uint16_t* pool, int64_t off) {
+    Row8<EK> r;
+    if constexpr (EK == kF32) {
+        const float* p = reinterpret_cast<const float*>(pool) + off;
+        r.w[0] = load_stream(reinterpret_cast<const uint16_t*>(p));
+        r.w[1] = load_stream(reinterpret_cast<const uint16_t*>(p + 4));
+    } else {
+        r.w[0] = load_stream(pool + off);
+    }
+    return r;
+}
+
+template <int EK>
+__device__ __forceinline__ void decode_row8(const Row8<EK>& r, float (&f)[8]) {
+    if constexpr (EK == kF32) {
+        f[0] = __uint_as_float(r.w[0].x); f[1] = __uint_as_float(r.w[0].y);
+        f[2] = __uint_as_float(r.w[0].z); f[3] = __uint_as_float(r.w[0].w);
+        f[4] = __uint_as_float(r.w[1].x); f[5] = __uint_as_float(r.w[1].y);
+        f[6] = __uint_as_float(r.w[1].z); f[7] = __uint_as_float(r.w[1].w);
+    } else {
+        decode8<EK == kBF16>(r.w[0], f);
+    }
+}
+
 __device__ __forceinline__ uint4 permute_u4(uint4 x, int src_lane) {
     uint4 y;
     y.x = (uint32_t)__shfl((int)x.x, src_lane);
@@ -56,7 +94,7 @@ __device__ __forceinline__ uint4 permute_u4(uint4 x, int src_lane) {
     return y;
 }
 
-template <int D, int G, bool BF16>
+template <int D, int G, int EK>
 __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
     constexpr int R = D / 8;            // lanes per K/V row
     constexpr int RPW = 64 / R;         // rows per wave per step
@@ -113,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
 
     // ---- rotation role of the column, cos / sin at the first token and per step
     const int rhalf = a.rope_dim >> 1;
+    const bool any_rot = a.rope_dim > 0;          // uniform: 0 = plain decode (no rotation)
     const bool first_half = d0 < rhalf;
     const bool rotated = d0 < a.rope_dim;
     const int src = first_half ? lane + rhalf / 8 : (rotated ? lane - rhalf / 8 : lane);
@@ -163,27 +202,38 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
     // and are masked), so the cross-lane permutes and reductions see a converged wave
     const int n_steps = (t_end - t_begin + STR - 1) / STR;
     int t = t0;
-    uint4 kc, vc;
+    Row8<EK> kc, vc;
     {
         const int64_t o = row_off(min(t, t_end - 1));
-        kc = load_stream(a.k_pool + o);
-        vc = load_stream(a.v_pool + o);
+        kc = load_row8<EK>(a.k_pool, o);
+        vc = load_row8<EK>(a.v_pool, o);
     }
     for (int step = 0; step < n_steps; ++step) {
         const int64_t on = row_off(min(t + STR, t_end - 1));
-        const uint4 kn = load_stream(a.k_pool + on);
-        const uint4 vn = load_stream(a.v_pool + on);
+        const Row8<EK> kn = load_row8<EK>(a.k_pool, on);
+        const Row8<EK> vn = load_row8<EK>(a.v_pool, on);
 
         const bool valid = t < t_end && t >= vis_lo;
-        const uint4 kp = permute_u4(kc, src);
-        float kf[8], kpf[8], vf[8];
-        decode8<BF16>(kc, kf);
-        decode8<BF16>(kp, kpf);
-        decode8<BF16>(valid ? vc : make_uint4(0, 0, 0, 0), vf);
-        float kr[8];
+        float kf[8], vf[8], kr[8];
+        decode_row8<EK>(kc, kf);
+        if (!valid) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            kr[j] = rotated ? fmaf(kf[j], cc[j], sgn * kpf[j] * ss[j]) : kf[j];
+            for (int i = 0; i < Row8<EK>::NW; ++i) vc.w[i] = make_uint4(0, 0, 0, 0);
+        }
+        decode_row8<EK>(vc, vf);
+        if (any_rot) {
+            Row8<EK> kp;
+#pragma unroll
+            for (int i = 0; i < Row8<EK>::NW; ++i) kp.w[i] = permute_u4(kc.w[i], src);
+            float kpf[8];
+            decode_row8<EK>(kp, kpf);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                kr[j] = rotated ? fmaf(kf[j], cc[j], sgn * kpf[j] * ss[j]) : kf[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kr[j] = kf[j];
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float dot = 0.f;
@@ -304,35 +354,35 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
     if (threadIdx.x == 0) store_shared(counter, 0);  // ready for the next call
 }
 
-template <int D, int G, bool BF16>
+template <int D, int G, int EK>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)a.B);
-    hipLaunchKernelGGL((decode_rope_kernel<D, G, BF16>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_rope_kernel<D, G, EK>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, int EK>
 hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
     switch (a.Hq / a.Hkv) {
-        case 1: return launch_typed<D, 1, BF16>(a, stream);
-        case 2: return launch_typed<D, 2, BF16>(a, stream);
-        case 3: return launch_typed<D, 3, BF16>(a, stream);
-        case 4: return launch_typed<D, 4, BF16>(a, stream);
-        case 5: return launch_typed<D, 5, BF16>(a, stream);
-        case 6: return launch_typed<D, 6, BF16>(a, stream);
-        case 7: return launch_typed<D, 7, BF16>(a, stream);
-        case 8: return launch_typed<D, 8, BF16>(a, stream);
+        case 1: return launch_typed<D, 1, EK>(a, stream);
+        case 2: return launch_typed<D, 2, EK>(a, stream);
+        case 3: return launch_typed<D, 3, EK>(a, stream);
+        case 4: return launch_typed<D, 4, EK>(a, stream);
+        case 5: return launch_typed<D, 5, EK>(a, stream);
+        case 6: return launch_typed<D, 6, EK>(a, stream);
+        case 7: return launch_typed<D, 7, EK>(a, stream);
+        case 8: return launch_typed<D, 8, EK>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool BF16>
+template <int EK>
 hipError_t dispatch_d(const DecodeArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 32: return dispatch_g<32, BF16>(a, stream);
-        case 64: return dispatch_g<64, BF16>(a, stream);
-        case 128: return dispatch_g<128, BF16>(a, stream);
-        case 256: return dispatch_g<256, BF16>(a, stream);
+        case 32: return dispatch_g<32, EK>(a, stream);
+        case 64: return dispatch_g<64, EK>(a, stream);
+        case 128: return dispatch_g<128, EK>(a, stream);
+        case 256: return dispatch_g<256, EK>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -340,7 +390,8 @@ hipError_t dispatch_d(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_rope(const DecodeArgs& a, hipStream_t stream) {
-    return a.bf16 ? dispatch_d<true>(a, stream) : dispatch_d<false>(a, stream);
+    if (a.f32) return dispatch_d<kF32>(a, stream);
+    return a.bf16 ? dispatch_d<kBF16>(a, stream) : dispatch_d<kF16>(a, stream);
 }
 
 }  // namespace pkv

@@ -39,6 +39,13 @@ using namespace dev;
 constexpr int kWaves = 4;
 constexpr int kMaxD = 256;
 
+// Stores one value into a pool: a 16-bit code, or the float itself for float32 pools (page
+// "makarna/pkg/kvcache/paged_cache.go", Append: float32 rows are copied unchanged).
+__device__ __forceinline__ void store_elem(uint16_t* pool, int64_t i, float y, const AppendArgs& a) {
+    if (a.f32) reinterpret_cast<float*>(pool)[i] = y;
+    else pool[i] = encode16(y, a.bf16);
+}
+
 // One workgroup per row (new token): the rotary cos / sin of the token's position are computed
 // once into LDS and shared by its Hq + Hkv head vectors, which the 4 waves take in turn.
 __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
@@ -100,15 +107,15 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
                 qo[i] = y0;
                 qo[i + rhalf] = y1;
             } else if (prow >= 0) {
-                a.k_pool[prow + i] = encode16(y0, a.bf16);
-                a.k_pool[prow + i + rhalf] = encode16(y1, a.bf16);
+                store_elem(a.k_pool, prow + i, y0, a);
+                store_elem(a.k_pool, prow + i + rhalf, y1, a);
             }
         }
         // partial rotary: the dims from rope_dim on are only normed
         for (int j = a.rope_dim + lane; j < D; j += 64) {
             const float y = w != nullptr ? norm_elem(x[j], r, w[j]) : x[j];
             if (is_q) qo[j] = y;
-            else if (prow >= 0) a.k_pool[prow + j] = encode16(y, a.bf16);
+            else if (prow >= 0) store_elem(a.k_pool, prow + j, y, a);
         }
         if (prow >= 0) {
             const float* vsrc = a.v_in + ((int64_t)row * a.Hkv + head) * D;
@@ -118,9 +125,9 @@ __global__ __launch_bounds__(kWaves * 64) void kv_append_kernel(AppendArgs a) {
                 wave_lds_sync();
                 const float sc = vnorm_scale(x, D, a.eps);
                 for (int d = lane; d < D; d += 64)
-                    a.v_pool[prow + d] = encode16(vnorm_elem(x[d], sc), a.bf16);
+                    store_elem(a.v_pool, prow + d, vnorm_elem(x[d], sc), a);
             } else {
-                for (int d = lane; d < D; d += 64) a.v_pool[prow + d] = encode16(vsrc[d], a.bf16);
+                for (int d = lane; d < D; d += 64) store_elem(a.v_pool, prow + d, vsrc[d], a);
             }
         }
         wave_lds_sync();  // x is reused by the wave's next vector

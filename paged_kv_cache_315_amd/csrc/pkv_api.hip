@@ -39,7 +39,7 @@ pkv_status fail(pkv_status st, const char* fmt, ...) {
 
 namespace {
 
-bool valid_dtype(pkv_dtype d) { return d == PKV_F16 || d == PKV_BF16; }
+bool valid_dtype(pkv_dtype d) { return d == PKV_F16 || d == PKV_BF16 || d == PKV_F32; }
 
 constexpr int kMaxGridDim = 65535;  // y / z grid limit used for Hkv and B
 constexpr int kDefaultCUs = 256;
@@ -289,6 +289,7 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
     a.rope_dim = var.rope_read ? 0 : var.rope_dim;  // rotation at read: the pool keeps un-rotated K
     a.v_norm = var.v_norm;
     a.bf16 = dtype == PKV_BF16;
+    a.f32 = dtype == PKV_F32;
     const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
@@ -431,8 +432,8 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
     if (B == 0 || max_context_len == 0) return PKV_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
         return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer argument");
-    if (var.rope_read) {
-        // rotation at read: the partitioned schedule of decode_rope.hip
+    if (var.rope_read || dtype == PKV_F32) {
+        // rotation at read or float32 pools: the partitioned schedule of decode_rope.hip
         const int P = split_tokens > 0 ? split_tokens
                                        : choose_split(B, num_kv_heads, max_context_len,
                                                       block_size, device_cus());
@@ -470,7 +471,8 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
         a.bf16 = dtype == PKV_BF16;
         a.lens_are_positions = false;
         a.rope_theta = var.read_theta;
-        a.rope_dim = var.rope_dim;
+        a.rope_dim = var.rope_read ? var.rope_dim : 0;
+        a.f32 = dtype == PKV_F32;
         const hipError_t e = pkv::launch_decode_rope(a, static_cast<hipStream_t>(stream));
         if (e != hipSuccess)
             return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
@@ -511,9 +513,10 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
     Variant var;
     st = resolve_variant("decode_step", variant, head_dim, var);
     if (st != PKV_OK) return st;
-    if (var.rope_read)
+    if (var.rope_read || dtype == PKV_F32)
         return fail(PKV_ERR_UNSUPPORTED,
-                    "decode_step: rope_on_read is served by pkv_kv_append + pkv_paged_attn_decode");
+                    "decode_step: rope_on_read and float32 pools are served by pkv_kv_append + "
+                    "pkv_paged_attn_decode");
     st = check_decode_shape("decode_step", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
     if (B == 0) return PKV_OK;
@@ -632,6 +635,7 @@ pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float*
     a.rope_dim = var.rope_read ? 0 : var.rope_dim;  // rotation at read: the pool keeps un-rotated K
     a.v_norm = var.v_norm;
     a.bf16 = dtype == PKV_BF16;
+    a.f32 = dtype == PKV_F32;
     const hipError_t e = pkv::launch_kv_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(PKV_ERR_HIP, "prefill_append: launch failed: %s", hipGetErrorString(e));
@@ -662,8 +666,9 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
     Variant var;
     st = resolve_variant("prefill", variant, head_dim, var);
     if (st != PKV_OK) return st;
-    if (var.rope_read)
-        return fail(PKV_ERR_UNSUPPORTED, "prefill: rope_on_read is not built for chunked prefill");
+    if (var.rope_read || dtype == PKV_F32)
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "prefill: rope_on_read and float32 pools are not built for chunked prefill");
     st = check_decode_shape("prefill", B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
     if (num_tokens < 0 || max_chunk < 0 || max_context_len < 0)

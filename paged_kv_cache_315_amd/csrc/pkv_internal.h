@@ -29,6 +29,7 @@ struct AppendArgs {
     int rope_dim;           // rotated dims (even, <= D)
     bool v_norm;            // V rows normalised per KV head before they are stored
     bool bf16;
+    bool f32;               // float32 pools: the values are stored as they are
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
@@ -83,7 +84,8 @@ struct DecodeArgs {
     bool bf16;
     bool lens_are_positions;  // context_lens holds positions: L = p + 1 (fused-step fallback)
     float rope_theta;         // decode_rope.hip only: RoPE base of the rotation at read
-    int rope_dim;             // decode_rope.hip only: rotated dims, a multiple of 16
+    int rope_dim;             // decode_rope.hip only: rotated dims, a multiple of 16 (0: none)
+    bool f32;                 // decode_rope.hip only: float32 pools
 };
 
 // Launches the decode kernel (partitions + in-kernel merge by the last partition).

@@ -62,7 +62,7 @@ def _decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=-1), 1), (dict(Hq=5), 1), (dict(Hkv=0), 1), (dict(bs=0), 1), (dict(nb=0), 1),
-    (dict(theta=0.0), 1), (dict(theta=float("inf")), 1), (dict(qn=FAKE), 1), (dict(dt=3), 1),
+    (dict(theta=0.0), 1), (dict(theta=float("inf")), 1), (dict(qn=FAKE), 1), (dict(dt=4), 1),
     (dict(D=63), 2), (dict(D=258), 2), (dict(q=None), 1), (dict(B=0, q=None), 0),
     (dict(var=_lib.variant(rope_dim=3)), 1), (dict(var=_lib.variant(rope_dim=66)), 1),
     (dict(var=_lib.variant(rope_dim=-2)), 1), (dict(var=_lib.variant(window=-1)), 1),
@@ -128,17 +128,26 @@ def _prefill(lib, **kw):
     (dict(B=70000, mc=64), 2), (dict(var=_lib.variant(window=-1)), 1),
     (dict(var=_lib.variant(window=64)), 3),
     (dict(var=_lib.variant(rope_on_read=True, read_theta=1e4)), 2),
+    (dict(dt=3), 2),                                  # float32 pools: decode and append only
 ])
 def test_prefill_argument_checks(lib, kw, status):
     assert _prefill(lib, **kw) == status
 
 
-def test_decode_step_rejects_rotation_at_read(lib):
-    var = _lib.variant(rope_on_read=True, read_theta=1e4)
+@pytest.mark.parametrize("dt,var", [(1, _lib.variant(rope_on_read=True, read_theta=1e4)),
+                                    (3, None)])
+def test_decode_step_rejects_rotation_at_read_and_f32(lib, dt, var):
     st = lib.pkv_decode_step(FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000), FAKE, FAKE, FAKE, 4, FAKE,
-                             None, None, 1e-6, 1e4, 0.125, FAKE, None, 0, 2, 4, 2, 64, 16, 16, 1,
+                             None, None, 1e-6, 1e4, 0.125, FAKE, None, 0, 2, 4, 2, 64, 16, 16, dt,
                              var, None)
     assert st == 2 and b"rope_on_read" in lib.pkv_last_error()
+
+
+def test_f32_pools_pass_the_checks(lib):
+    # float32 pools are accepted by the append and the decode (they stop at later checks here)
+    assert _append(lib, dt=3, B=0, q=None) == 0
+    assert _append(lib, dt=4) == 1
+    assert _decode(lib, dt=3) == 3
 
 
 def test_workspace_formula(lib):

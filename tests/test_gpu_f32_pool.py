@@ -1,0 +1,108 @@
+"""GPU parity of float32 KV pools: pkv_kv_append / pkv_prefill_append storing float32 rows
+unchanged and pkv_paged_attn_decode reading them (page "makarna/pkg/kvcache/paged_cache.go",
+Append: float32 rows are copied as they are; page "makarna/pkg/model/arch/hybrid_decoder.go":
+float32 KV goes to the plain paged kernel), through the C ABI, against the oracle's float32
+pools.
+
+Bar: stored pools bit-identical over the whole pool (float bits); q_out and out within
+1e-3 abs + 2e-3 rel with identical non-finite patterns (tests/gpu_util.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_315_amd as pkv
+from paged_kv_cache_315_amd import workloads as W
+from gpu_util import assert_close, log
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, rope_on_read, rope_dim, window, v_norm, split_tokens)
+    "d64-g2": (lambda: W.make_workload(301, [37, 50, 0], 4, 2, 64, 16, "f32", 1e4), False, 0, 0,
+               False, 0),
+    "llama-shape": (lambda: W.make_workload(302, [700, 2100, 4000, 1], 32, 8, 128, 16, "f32",
+                                            5e5), False, 0, 0, False, 0),
+    "rope-at-read": (lambda: W.make_workload(303, [300, 1999], 16, 4, 128, 16, "f32", 5e5),
+                     True, 0, 0, False, 64),
+    "qknorm-vnorm-window-partial": (lambda: W.make_workload(304, [90, 1000], 12, 4, 128, 8, "f32",
+                                                            1e6, qk_norm=True), False, 32, 200,
+                                    True, 0),
+    "d256-g8": (lambda: W.make_workload(305, [15, 260], 16, 2, 256, 32, "f32", 1e4), False, 0, 0,
+                False, 0),
+}
+
+
+def _upload_f32(wl, device="cuda:0"):
+    def t(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x if dt is None else x.view(dt))).to(device)
+    return {
+        "q": t(wl["q"]), "k_new": t(wl["k_new"]), "v_new": t(wl["v_new"]),
+        "k_pool": t(wl["k_pool"], np.int32), "v_pool": t(wl["v_pool"], np.int32),
+        "tables": t(wl["tables"]), "positions": t(wl["positions"]),
+        "context_lens": t(wl["context_lens"]),
+        "q_norm_w": None if wl["q_norm_w"] is None else t(wl["q_norm_w"]),
+        "k_norm_w": None if wl["k_norm_w"] is None else t(wl["k_norm_w"]),
+    }
+
+
+def _pool_bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_f32_pool_append_and_decode(name):
+    make, rope_read, rope_dim, window, v_norm, split = CASES[name]
+    wl = make()
+    log(f"f32 pool: {name} B={wl['B']} Hq={wl['Hq']} Hkv={wl['Hkv']} D={wl['D']} bs={wl['bs']}")
+    k_ref, v_ref = wl["k_pool"].copy(), wl["v_pool"].copy()
+    q_ref = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], k_ref, v_ref, wl["tables"],
+                             wl["positions"], wl["q_norm_w"], wl["k_norm_w"], wl["eps"],
+                             wl["theta"], "f32", rope_dim=rope_dim or None, v_norm=v_norm,
+                             rope_on_read=rope_read)
+    if rope_read:
+        out_ref = oracle.paged_attn_decode_rope(q_ref, k_ref, v_ref, wl["tables"],
+                                                wl["context_lens"], wl["theta"], wl["scale"],
+                                                "f32", rope_dim=rope_dim or None, window=window)
+    else:
+        out_ref = oracle.paged_attn_decode(q_ref, k_ref, v_ref, wl["tables"], wl["context_lens"],
+                                           wl["scale"], "f32", window=window)
+    dev = _upload_f32(wl)
+    q_out = pkv.kv_append(dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"],
+                          dev["tables"], dev["positions"], theta=wl["theta"],
+                          q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"], eps=wl["eps"],
+                          dtype="f32", rope_dim=rope_dim, v_norm=v_norm, rope_on_read=rope_read)
+    out = pkv.paged_attn_decode(q_out, dev["k_pool"], dev["v_pool"], dev["tables"],
+                                dev["context_lens"], wl["max_context_len"], wl["scale"],
+                                split_tokens=split, dtype="f32", window=window,
+                                rope_on_read=rope_read, read_theta=wl["theta"],
+                                rope_dim=rope_dim)
+    torch.cuda.synchronize()
+    assert np.array_equal(_pool_bits(dev["k_pool"]), k_ref), f"{name}: k_pool bits differ"
+    assert np.array_equal(_pool_bits(dev["v_pool"]), v_ref), f"{name}: v_pool bits differ"
+    assert_close(q_out.cpu().numpy(), q_ref, f"{name}: q_out")
+    assert_close(out.cpu().numpy(), out_ref, f"{name}: out")
+
+
+def test_f32_pool_prefill_append_and_nan_payload():
+    """Chunked append into a float32 pool: every row stored as the oracle stores it, and a V NaN
+    with a payload keeps its bits (no conversion touches it)."""
+    wl = W.make_prefill_workload(306, [0, 21, 40], [7, 30, 1], 4, 2, 64, 16, "f32", 1e4)
+    wl["v_new"][3, 1, 9] = np.array([0x7F800123], np.uint32).view(np.float32)[0]
+    k_ref, v_ref = wl["k_pool"].copy(), wl["v_pool"].copy()
+    q_ref = oracle.prefill_append(wl["q"], wl["k_new"], wl["v_new"], k_ref, v_ref, wl["tables"],
+                                  wl["cu_seqlens"], wl["start_pos"], None, None, wl["eps"],
+                                  wl["theta"], "f32")
+    dev = {k: torch.from_numpy(np.ascontiguousarray(wl[k])).cuda()
+           for k in ("q", "k_new", "v_new", "tables", "cu_seqlens", "start_pos")}
+    kp = torch.from_numpy(wl["k_pool"].view(np.int32).copy()).cuda()
+    vp = torch.from_numpy(wl["v_pool"].view(np.int32).copy()).cuda()
+    q_out = pkv.prefill_append(dev["q"], dev["k_new"], dev["v_new"], kp, vp, dev["tables"],
+                               dev["cu_seqlens"], dev["start_pos"], theta=wl["theta"],
+                               dtype="f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(_pool_bits(kp), k_ref)
+    assert np.array_equal(_pool_bits(vp), v_ref)
+    assert (v_ref == 0x7F800123).sum() == 1
+    assert_close(q_out.cpu().numpy(), q_ref, "prefill q_out")
