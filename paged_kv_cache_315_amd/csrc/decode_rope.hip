@@ -15,8 +15,10 @@
 // (g, s, b) owns P = split_tokens tokens of sequence b and the G query heads of KV head g, with
 // the same workspace (partials + counters, last partition merges). Inside a workgroup every row
 // of 8-dim columns is one token: lane column c holds dims 8c .. 8c+7 of the K and V rows
-// (16-byte loads), 64 / (D/8) rows per wave, waves interleaved, the next row's K/V in flight
-// while one is computed.
+// (16-byte loads), 64 / (D/8) rows per wave, waves interleaved. A lane takes U rows per
+// iteration (4, or 2 for float32 pools and groups above 4): their scores share one online-softmax
+// update (the running sums are rescaled only when some lane's maximum grew), and the next U rows'
+// K/V are in flight while these are computed.
 //
 // Rotation at read. rope_dim is a multiple of 16, so a column lies entirely in the first half of
 // the rotated dims, entirely in the second half, or past rope_dim. A first-half lane gets its
@@ -24,9 +26,10 @@
 // one cross-lane permute of the raw codes, a second-half lane from the lane as far to its left:
 //   first half:  k'_i = k_i cos(delta f_i) + k_{i+h} sin(delta f_i)
 //   second half: k'_{i+h} = k_{i+h} cos(delta f_i) - k_i sin(delta f_i).
-// cos / sin of each lane's 8 pairs are evaluated in double at its first token and then advanced
-// by the fixed step of the row stride with the angle-difference formulas in float (error about
-// one ulp per step, a few hundred steps at most per partition); the rest is float arithmetic:
+// cos / sin of every pair are evaluated once per workgroup in double at the partition's first
+// row, carried to the first rows of the lanes by one-token steps, and then advanced by the fixed
+// row stride with the angle-difference formulas in float (error about one ulp per step; the host
+// keeps partitions to at most 4096 tokens, a few hundred steps); the rest is float arithmetic:
 // dot products reduced over the row's lanes, online softmax in exp2 units, PV on the vector ALU.
 // Keys holding +-Inf are outside what this path reproduces (Inf times a zero sine is NaN here at
 // other tokens than in a rotation by absolute positions).
@@ -94,14 +97,17 @@ __device__ __forceinline__ uint4 permute_u4(uint4 x, int src_lane) {
     return y;
 }
 
-template <int D, int G, int EK>
+template <int D, int G, int EK, bool ROT>
 __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
     constexpr int R = D / 8;            // lanes per K/V row
     constexpr int RPW = 64 / R;         // rows per wave per step
     constexpr int STR = kWaves * RPW;   // tokens per step of the workgroup
+    constexpr int U = (EK == kF32 || G > 4) ? 2 : 4;   // rows per lane per iteration
     static_assert(D % 32 == 0 && G >= 1 && G <= 8, "shape");
 
     __shared__ int32_t s_tbl[kTblCap];
+    __shared__ float s_seed[STR * D / 2][2];   // cos / sin of the first row of each (row, pair)
+    __shared__ float s_step[D / 2][2];         // cos / sin of STR f_i
     __shared__ float s_acc[kWaves][G][D];
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[kWaves][G];
@@ -151,13 +157,40 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
 
     // ---- rotation role of the column, cos / sin at the first token and per step
     const int rhalf = a.rope_dim >> 1;
-    const bool any_rot = a.rope_dim > 0;          // uniform: 0 = plain decode (no rotation)
+    const bool any_rot = ROT && a.rope_dim > 0;   // the host picks ROT = (rope_dim > 0)
     const bool first_half = d0 < rhalf;
-    const bool rotated = d0 < a.rope_dim;
+    const bool rotated = ROT && d0 < a.rope_dim;
     const int src = first_half ? lane + rhalf / 8 : (rotated ? lane - rhalf / 8 : lane);
     const int pair0 = first_half ? d0 : d0 - rhalf;
     const float sgn = first_half ? 1.f : -1.f;
     const int t0 = t_begin + wave * RPW + rg;   // this lane's first token
+    // Per rotary pair i (one thread each, double): the frequency f_i, cos / sin of
+    // (pq - t_begin) f_i, of f_i and of STR f_i. The seeds of the STR first rows of the partition
+    // follow by one-token steps in float (at most 63 steps), so each lane starts from the seed of
+    // its own first row (t_begin + k, k = wave * RPW + rg) instead of evaluating 16 double-precision
+    // sines and cosines itself.
+    if (any_rot) {
+        for (int i = threadIdx.x; i < rhalf; i += kThreads) {
+            const double inv = pow((double)a.rope_theta, -2.0 * (double)i / a.rope_dim);
+            double sn, cs;
+            sincos((double)(pq - t_begin) * inv, &sn, &cs);
+            float c = (float)cs, sv = (float)sn;
+            sincos(inv, &sn, &cs);
+            const float c1 = (float)cs, s1 = (float)sn;
+            sincos((double)STR * inv, &sn, &cs);
+            s_step[i][0] = (float)cs;
+            s_step[i][1] = (float)sn;
+            for (int k = 0; k < STR; ++k) {
+                s_seed[k * rhalf + i][0] = c;
+                s_seed[k * rhalf + i][1] = sv;
+                const float nc = fmaf(c, c1, sv * s1);
+                const float ns = fmaf(sv, c1, -(c * s1));
+                c = nc;
+                sv = ns;
+            }
+        }
+    }
+    __syncthreads();  // s_tbl, s_seed, s_step
     float cc[8], ss[8], stc[8], sts[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -167,19 +200,15 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
         sts[j] = 0.f;
     }
     if (rotated) {
+        const int k = wave * RPW + rg;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const double inv = pow((double)a.rope_theta, -2.0 * (double)(pair0 + j) / a.rope_dim);
-            double sn, cs;
-            sincos((double)(pq - t0) * inv, &sn, &cs);
-            cc[j] = (float)cs;
-            ss[j] = (float)sn;
-            sincos((double)STR * inv, &sn, &cs);
-            stc[j] = (float)cs;
-            sts[j] = (float)sn;
+            cc[j] = s_seed[k * rhalf + pair0 + j][0];
+            ss[j] = s_seed[k * rhalf + pair0 + j][1];
+            stc[j] = s_step[pair0 + j][0];
+            sts[j] = s_step[pair0 + j][1];
         }
     }
-    __syncthreads();  // s_tbl
 
     float m[G], lsum[G], acc[G][8];
 #pragma unroll
@@ -200,69 +229,104 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
 
     // every lane runs the same number of steps (rows past the partition clamp to its last row
     // and are masked), so the cross-lane permutes and reductions see a converged wave
-    const int n_steps = (t_end - t_begin + STR - 1) / STR;
-    int t = t0;
-    Row8<EK> kc, vc;
-    {
-        const int64_t o = row_off(min(t, t_end - 1));
-        kc = load_row8<EK>(a.k_pool, o);
-        vc = load_row8<EK>(a.v_pool, o);
-    }
-    for (int step = 0; step < n_steps; ++step) {
-        const int64_t on = row_off(min(t + STR, t_end - 1));
-        const Row8<EK> kn = load_row8<EK>(a.k_pool, on);
-        const Row8<EK> vn = load_row8<EK>(a.v_pool, on);
-
-        const bool valid = t < t_end && t >= vis_lo;
-        float kf[8], vf[8], kr[8];
-        decode_row8<EK>(kc, kf);
-        if (!valid) {
+    // U rows per lane per iteration (rows t, t + STR, ..., t + (U-1) STR): their scores share one
+    // softmax update, and the next iteration's U rows are in flight while these are computed
+    // (two named register buffers, the loop unrolled by two, no divergent branch inside).
+    auto load_rows = [&](Row8<EK> (&kr)[U], Row8<EK> (&vr)[U], int tt) {
 #pragma unroll
-            for (int i = 0; i < Row8<EK>::NW; ++i) vc.w[i] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int64_t o = row_off(min(tt + u * STR, t_end - 1));
+            kr[u] = load_row8<EK>(a.k_pool, o);
+            vr[u] = load_row8<EK>(a.v_pool, o);
         }
-        decode_row8<EK>(vc, vf);
-        if (any_rot) {
-            Row8<EK> kp;
+    };
+    auto compute_rows = [&](const Row8<EK> (&kc)[U], const Row8<EK> (&vc)[U], int tt) {
+        float sc[U][G];
+        bool valid[U];
 #pragma unroll
-            for (int i = 0; i < Row8<EK>::NW; ++i) kp.w[i] = permute_u4(kc.w[i], src);
-            float kpf[8];
-            decode_row8<EK>(kp, kpf);
+        for (int u = 0; u < U; ++u) {
+            const int tu = tt + u * STR;
+            valid[u] = tu < t_end && tu >= vis_lo;
+            float kr[8];
+            decode_row8<EK>(kc[u], kr);
+            if constexpr (ROT) {
+                Row8<EK> kp;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                kr[j] = rotated ? fmaf(kf[j], cc[j], sgn * kpf[j] * ss[j]) : kf[j];
-        } else {
+                for (int i = 0; i < Row8<EK>::NW; ++i) kp.w[i] = permute_u4(kc[u].w[i], src);
+                float kpf[8];
+                decode_row8<EK>(kp, kpf);
+                // unrotated columns keep cos 1 / sin 0 and drop the partner term: exact, and
+                // branch-free (a divergent branch here made the compiler drain the prefetch)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) kr[j] = kf[j];
+                for (int j = 0; j < 8; ++j) {
+                    const float kp_eff = rotated ? kpf[j] : 0.f;
+                    kr[j] = fmaf(kr[j], cc[j], sgn * kp_eff * ss[j]);
+                }
+                // delta -> delta - STR: cos(a - b) = cos a cos b + sin a sin b,
+                //                       sin(a - b) = sin a cos b - cos a sin b
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float nc = fmaf(cc[j], stc[j], ss[j] * sts[j]);
+                    const float ns = fmaf(ss[j], stc[j], -(cc[j] * sts[j]));
+                    cc[j] = nc;
+                    ss[j] = ns;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float dot = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dot = fmaf(qv[h][j], kr[j], dot);
+#pragma unroll
+                for (int off = 1; off < R; off <<= 1) dot += __shfl_xor(dot, off);
+                sc[u][h] = valid[u] ? dot : -INFINITY;
+            }
         }
+        // one online-softmax update for the U rows
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float dot = 0.f;
+            float mn = m[h];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dot = fmaf(qv[h][j], kr[j], dot);
-#pragma unroll
-            for (int off = 1; off < R; off <<= 1) dot += __shfl_xor(dot, off);
-            const float sc = valid ? dot : -INFINITY;
-            const float mn = fmaxf(m[h], sc);
+            for (int u = 0; u < U; ++u) mn = fmaxf(mn, sc[u][h]);
             const float mu = mn == -INFINITY ? 0.f : mn;
             const float al = exp2f(m[h] - mu);
-            const float pe = exp2f(sc - mu);
-            lsum[h] = fmaf(lsum[h], al, pe);
+            float ps = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pe, vf[j], acc[h][j] * al);
+            for (int u = 0; u < U; ++u) {
+                sc[u][h] = exp2f(sc[u][h] - mu);
+                ps += sc[u][h];
+            }
+            lsum[h] = fmaf(lsum[h], al, ps);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[h][j] *= al;
             m[h] = mn;
         }
-        // delta -> delta - STR: cos(a - b) = cos a cos b + sin a sin b,
-        //                       sin(a - b) = sin a cos b - cos a sin b
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float nc = fmaf(cc[j], stc[j], ss[j] * sts[j]);
-            const float ns = fmaf(ss[j], stc[j], -(cc[j] * sts[j]));
-            cc[j] = nc;
-            ss[j] = ns;
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+            decode_row8<EK>(vc[u], vf);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vf[j] = valid[u] ? vf[j] : 0.f;  // poisoned slots
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(sc[u][h], vf[j], acc[h][j]);
         }
-        kc = kn;
-        vc = vn;
-        t += STR;
+    };
+
+    // iterations in pairs with no exit between them (an odd count runs one masked iteration
+    // more): an exit inside the pair made the compiler merge the two buffers with copies, and a
+    // load into a register a pending load still targets waits for every load in flight
+    const int n_pairs = (t_end - t_begin + 2 * U * STR - 1) / (2 * U * STR);
+    int t = t0;
+    Row8<EK> ka[U], va[U], kb[U], vb[U];
+    load_rows(ka, va, t);
+    for (int it = 0; it < n_pairs; ++it) {
+        load_rows(kb, vb, t + U * STR);
+        compute_rows(ka, va, t);
+        load_rows(ka, va, t + 2 * U * STR);
+        compute_rows(kb, vb, t + U * STR);
+        t += 2 * U * STR;
     }
 
     // ---- combine the rows of the wave (lanes of one column), then the waves through LDS
@@ -357,7 +421,13 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
 template <int D, int G, int EK>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)a.B);
-    hipLaunchKernelGGL((decode_rope_kernel<D, G, EK>), grid, dim3(kThreads), 0, stream, a);
+    // 16-bit pools come here only to be rotated at read (plain ones run the balanced kernel)
+    if (EK != kF32 || a.rope_dim > 0)
+        hipLaunchKernelGGL((decode_rope_kernel<D, G, EK, true>), grid, dim3(kThreads), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((decode_rope_kernel<D, G, kF32, false>), grid, dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -434,6 +434,10 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
         return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer argument");
     if (var.rope_read || dtype == PKV_F32) {
         // rotation at read or float32 pools: the partitioned schedule of decode_rope.hip
+        if (split_tokens > 4096)
+            return fail(PKV_ERR_INVALID_ARG,
+                        "decode: split_tokens=%d above 4096 for rope_on_read / float32 pools (the "
+                        "rotation is carried across a partition in float steps)", split_tokens);
         const int P = split_tokens > 0 ? split_tokens
                                        : choose_split(B, num_kv_heads, max_context_len,
                                                       block_size, device_cus());
