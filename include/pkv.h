@@ -193,7 +193,8 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *              different streams) need separate workspaces.
  * split_tokens 0 for the balanced schedule, or tokens per partition: a positive multiple of
  *              64 of at most 1022 * block_size (a partition stages its block ids in LDS).
- *              With rope_on_read (variant) the partitioned schedule always runs, and 0 means
+ *              With rope_on_read (variant) or float32 pools the partitioned vector-ALU kernel
+ *              always runs, split_tokens is at most 4096, and 0 means
  *              pkv_decode_split_tokens(...)'s choice (size the workspace with that value).
  * variant      (host) NULL, or a window as described under pkv_variant: then only the keys
  *              max(0, L - window) .. L - 1 are attended (the partitions and tiles start at the

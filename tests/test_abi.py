@@ -89,6 +89,8 @@ def test_append_argument_checks(lib, kw, status):
     (dict(var=_lib.variant(rope_dim=8, rope_on_read=True, read_theta=1e4)), 2),
     (dict(var=_lib.variant(rope_on_read=True, read_theta=1e4)), 3),
     (dict(var=_lib.variant(rope_dim=32, rope_on_read=True, read_theta=1e4, window=9)), 3),
+    (dict(split=4160, var=_lib.variant(rope_on_read=True, read_theta=1e4)), 1),
+    (dict(split=4160, dt=3), 1),
 ])
 def test_decode_argument_checks(lib, kw, status):
     assert _decode(lib, **kw) == status
