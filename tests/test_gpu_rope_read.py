@@ -31,6 +31,11 @@ CASES = {
                    64),
     "g5-d64-window": (lambda: W.make_workload(206, [17, 64, 65, 400], 10, 2, 64, 16, "f16", 1e4),
                       0, 50, 0),
+    # QK-norm with edge values in the new K/V (+-70000, 1e-7, NaN in 1 % of the elements): NaN
+    # keys poison their group, +-Inf values (fp16 overflow of V) reach the outputs
+    "qknorm-edges-f16": (lambda: W.make_workload(208, [300, 1000, 2000, 64], 32, 8, 128, 16,
+                                                 "f16", 1e6, qk_norm=True, edge_fraction=0.01),
+                         0, 0, 0),
 }
 
 
