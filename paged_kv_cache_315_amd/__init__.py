@@ -135,7 +135,10 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
     NB, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if out is None:
         out = torch.empty_like(q)
-    if rope_on_read and not split_tokens and B and max_context_len:
+    # rotation at read and float32 pools always run the partitioned schedule: size the
+    # workspace for the partition length the library will pick
+    vector_alu = rope_on_read or pool_dtype_code(k_pool, dtype) == PKV_F32
+    if vector_alu and not split_tokens and B and max_context_len:
         split_tokens = decode_split_tokens(B, Hq, Hkv, D, bs, max_context_len)
     need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, split_tokens) if B else 0
     if workspace is None and need:

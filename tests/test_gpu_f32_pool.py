@@ -110,3 +110,30 @@ def test_f32_pool_prefill_append_and_nan_payload():
     assert np.array_equal(_pool_bits(vp), v_ref)
     assert (v_ref == 0x7F800123).sum() == 1
     assert_close(q_out.cpu().numpy(), q_ref, "prefill q_out")
+
+
+def test_f32_pool_workspace_sized_for_partitions():
+    """Float32 pools run the partitioned schedule even where the balanced one would fit: with
+    2048 sequences (one of 4200 tokens) and two KV heads the partitions need more workspace than
+    the balanced schedule, and the binding must size it for the partitions it will get."""
+    cached = np.full(2048, 2)
+    cached[5] = 4200
+    wl = W.make_workload(308, cached, 2, 2, 32, 16, "f32", 1e4)
+    B, Hq, Hkv, D, bs = 2048, 2, 2, 32, 16
+    P = pkv.decode_split_tokens(B, Hq, Hkv, D, bs, wl["max_context_len"])
+    need = pkv.decode_workspace_bytes(B, Hq, Hkv, D, bs, wl["max_context_len"], P)
+    assert need > pkv.decode_workspace_bytes(B, Hq, Hkv, D, bs, wl["max_context_len"], 0)
+    k_ref, v_ref = wl["k_pool"].copy(), wl["v_pool"].copy()
+    q_ref = oracle.kv_append(wl["q"], wl["k_new"], wl["v_new"], k_ref, v_ref, wl["tables"],
+                             wl["positions"], None, None, wl["eps"], wl["theta"], "f32")
+    out_ref = oracle.paged_attn_decode(q_ref, k_ref, v_ref, wl["tables"], wl["context_lens"],
+                                       wl["scale"], "f32")
+    dev = _upload_f32(wl)
+    q_out = pkv.kv_append(dev["q"], dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"],
+                          dev["tables"], dev["positions"], theta=wl["theta"], dtype="f32")
+    out = pkv.paged_attn_decode(q_out, dev["k_pool"], dev["v_pool"], dev["tables"],
+                                dev["context_lens"], wl["max_context_len"], wl["scale"],
+                                dtype="f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(_pool_bits(dev["k_pool"]), k_ref)
+    assert_close(out.cpu().numpy(), out_ref, "2048 sequences, float32 pool")
