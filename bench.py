@@ -180,6 +180,21 @@ def main() -> int:
     torch.cuda.synchronize()
     decode_ms = e0.elapsed_time(e1) / args.steps
 
+    # per-launch distribution of the step: one event pair around each of 200 launches (a
+    # separate pass; the timed K steps above are back to back with no events between them)
+    n_lat = min(200, max(args.steps, 1))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_lat)]
+    for i in range(n_lat):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    lat_us = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])
+    lat = {"p10": round(float(np.percentile(lat_us, 10)), 2),
+           "p50": round(float(np.percentile(lat_us, 50)), 2),
+           "p90": round(float(np.percentile(lat_us, 90)), 2), "launches": n_lat}
+
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
     traffic_bytes = profiled_traffic(wl["name"]) if args.split_tokens == 0 else None
     tokens_per_s = B / (ms_per_step * 1e-3)
@@ -232,6 +247,7 @@ def main() -> int:
             "traffic_bytes_per_launch": traffic_bytes,
             "bytes_per_launch": nbytes["step"], "avg_launch_us": round(ms_per_step * 1e3, 3),
         },
+        "step_launch_us": lat,
         "decode_only": {"kernel": "pkv_paged_attn_decode", "avg_launch_us": round(decode_ms * 1e3, 3),
                         "gb_per_s": round(nbytes["decode"] / (decode_ms * 1e-3) / 1e9, 2)},
         "cpu_baseline": cpu,
