@@ -278,3 +278,100 @@ def test_native_errors():
         B.fill_block_tables([s], 1, pad_block=0)          # 2 blocks > row of 1
     s.destroy()
     pool.close()
+
+
+# ---------------------------------------------------------------- planted mistakes in the oracle
+
+_SCENARIO_PINS = [test_block_hash_byte_layout, test_cold_prompt_then_commit_then_shared_prompt,
+                  test_failed_admission_changes_nothing, test_freed_cached_block_is_found_until_reused,
+                  test_reserve_append_token_truncate]
+
+
+def _mut_no_chain(tokens, parent=None):
+    data = b""
+    for t in tokens:
+        data += O.struct.pack("<i", t)
+    return O.fnv1a64(data)
+
+
+def _mut_lifo_allocate(self, n):
+    if n > len(self.free):
+        raise O.BlockError("no room")
+    out = []
+    for _ in range(n):
+        b = self.free.pop()                      # newest freed block first
+        if b in self.cached_hash:
+            del self.cache[self.cached_hash.pop(b)]
+        self.ref[b] = 1
+        out.append(b)
+    return out
+
+
+def _mut_keep_stale_cache(self, n):
+    if n > len(self.free):
+        raise O.BlockError("no room")
+    out = []
+    for _ in range(n):
+        b = self.free.pop(0)                     # reused, but its old cache entry is kept
+        self.ref[b] = 1
+        out.append(b)
+    return out
+
+
+def _mut_borrow_without_reference(self, blocks):
+    for b in blocks:
+        if self.ref[b] == 0:
+            self.free.remove(b)
+
+
+def _mut_last_token_cached(self, tokens):
+    bs = self.pool.block_size
+    hashes = O.prompt_hashes(tokens, bs)
+    hit = self.pool.find_cached(hashes)
+    self.pool.touch(hit)
+    fresh = self.pool.allocate(len(hashes) - len(hit))
+    self.tokens, self.hashes = list(tokens), hashes
+    self.blocks = hit + fresh
+    self.owned = [False] * len(hit) + [True] * len(fresh)
+    self.num_computed = self.num_written = min(len(hit) * bs, len(tokens))
+    return self.num_computed
+
+
+def _mut_commit_partial_block(self, new_tokens):
+    bs = self.pool.block_size
+    old = self.num_computed
+    self.num_computed += new_tokens
+    self.num_written = max(self.num_written, self.num_computed)
+    lo, hi = old // bs, min(-(-self.num_computed // bs), len(self.hashes), len(self.blocks))
+    if hi > lo:
+        self.pool.cache_blocks(self.blocks[lo:hi], self.hashes[lo:hi])
+
+
+MUTANTS = {
+    "hash not chained to the parent": ("block_hash", O, _mut_no_chain),
+    "free list handed out newest first": ("allocate", O.Pool, _mut_lifo_allocate),
+    "reused block keeps its cache entry": ("allocate", O.Pool, _mut_keep_stale_cache),
+    "borrowed block takes no reference": ("touch", O.Pool, _mut_borrow_without_reference),
+    "last prompt token reported cached": ("allocate_for_tokens", O.Seq, _mut_last_token_cached),
+    "commit caches a partial block": ("commit", O.Seq, _mut_commit_partial_block),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_oracle_mutant_is_caught(name, monkeypatch):
+    attr, owner, fn = MUTANTS[name]
+    monkeypatch.setattr(owner, attr, fn)
+    caught = []
+    for pin in _SCENARIO_PINS:
+        try:
+            pin()
+        except (AssertionError, O.BlockError, ValueError):
+            caught.append(pin.__name__)
+    if not caught:   # invariants over random workloads as the last line
+        for seed in range(6):
+            try:
+                test_oracle_invariants_random(seed)
+            except (AssertionError, O.BlockError, ValueError):
+                caught.append(f"invariants[{seed}]")
+                break
+    assert caught, f"planted mistake '{name}' passed every pin"
