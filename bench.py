@@ -232,8 +232,7 @@ def main() -> int:
             "context_tokens": int(wl["context_lens"].sum()),
             "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
             "qk_norm": wl["q_norm_w"] is not None, "pool_copies": copies,
-            "split_tokens": split or pkv.decode_split_tokens(B, Hq, Hkv, D, wl["bs"],
-                                                             wl["max_context_len"]),
+            "schedule": "partitioned" if split else "balanced", "split_tokens": split,
             "bytes_per_step": nbytes["step"], "kv_bytes": nbytes["kv"],
         },
         # the step is one launch of the fused kernel, so the step time is its launch time;
