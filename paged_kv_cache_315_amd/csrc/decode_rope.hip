@@ -30,7 +30,8 @@
 // row, carried to the first rows of the lanes by one-token steps, and then advanced by the fixed
 // row stride with the angle-difference formulas in float (error about one ulp per step; the host
 // keeps partitions to at most 4096 tokens, a few hundred steps); the rest is float arithmetic:
-// dot products reduced over the row's lanes, online softmax in exp2 units, PV on the vector ALU.
+// dot products reduced over the row's lanes (DPP), online softmax in exp2 units, PV on the
+// vector ALU.
 // Keys holding +-Inf are outside what this path reproduces (Inf times a zero sine is NaN here at
 // other tokens than in a rotation by absolute positions).
 //
@@ -86,6 +87,19 @@ __device__ __forceinline__ void decode_row8(const Row8<EK>& r, float (&f)[8]) {
     } else {
         decode8<EK == kBF16>(r.w[0], f);
     }
+}
+
+// Sum over the R consecutive lanes of a row (R = 4, 8, 16, 32); every lane of the row receives
+// the total. DPP steps inside a row of 16 lanes (lane ^ 1, lane ^ 2, the other quad of the half
+// row, the other half of the row), one cross-lane exchange for the second row of 32.
+template <int R>
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    if constexpr (R >= 8) x += dpp_f<0x141>(x);
+    if constexpr (R >= 16) x += dpp_f<0x140>(x);
+    if constexpr (R >= 32) x += __shfl_xor(x, 16);
+    return x;
 }
 
 __device__ __forceinline__ uint4 permute_u4(uint4 x, int src_lane) {
@@ -277,8 +291,7 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
                 float dot = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) dot = fmaf(qv[h][j], kr[j], dot);
-#pragma unroll
-                for (int off = 1; off < R; off <<= 1) dot += __shfl_xor(dot, off);
+                dot = row_sum<R>(dot);
                 sc[u][h] = valid[u] ? dot : -INFINITY;
             }
         }
