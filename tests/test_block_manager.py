@@ -375,3 +375,61 @@ def test_oracle_mutant_is_caught(name, monkeypatch):
                 caught.append(f"invariants[{seed}]")
                 break
     assert caught, f"planted mistake '{name}' passed every pin"
+
+
+def test_native_pool_is_safe_under_concurrent_sequences():
+    """Threads driving their own sequences on one pool (ctypes releases the GIL, so the C++ calls
+    overlap): afterwards every reference count equals the number of sequences holding the block
+    and the free list holds exactly the unreferenced blocks."""
+    import threading
+    B = _lib()
+    pool = B.BlockPool(64, 4)
+    prefix = list(range(10))
+    errors = []
+
+    def worker(seed):
+        rng = random.Random(seed)
+        seqs = [B.SeqCache(pool, max_seq_len=64) for _ in range(2)]
+        try:
+            for _ in range(300):
+                s = rng.choice(seqs)
+                k = rng.randrange(4)
+                try:
+                    if k == 0:
+                        s.free()
+                        s.allocate_for_tokens(prefix[:rng.randrange(1, 11)] +
+                                              [rng.randrange(100) for _ in range(rng.randrange(4))])
+                    elif k == 1:
+                        s.reserve(rng.randrange(3))
+                    elif k == 2:
+                        s.commit(rng.randrange(3))
+                    else:
+                        s.free()
+                except Exception as e:   # noqa: BLE001 — pool exhaustion is an expected error
+                    if "PKV_ERR_INVALID_ARG" not in str(e):
+                        errors.append(e)
+        finally:
+            held = [s.blocks()[0].tolist() for s in seqs]
+            results[seed] = (seqs, held)
+
+    results = {}
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+    ref, cached, hashes, order = pool.block_state()
+    holders = np.zeros(64, np.int32)
+    for seqs, held in results.values():
+        for ids in held:
+            for b in ids:
+                holders[b] += 1
+    assert ref.tolist() == holders.tolist()
+    assert sorted(order.tolist()) == [b for b in range(64) if holders[b] == 0]
+    assert len(set(order.tolist())) == len(order)
+    for seqs, _ in results.values():
+        for s in seqs:
+            s.destroy()
+    assert (pool.block_state()[0] == 0).all() and pool.stats().num_free == 64
+    pool.close()
