@@ -446,7 +446,10 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
     constexpr int VS = KT + 4;          // LDS row stride of V^T ([dim][key]), in codes
     constexpr int PS = 20;
     constexpr int CH = KT * D / 8;      // 16-byte chunks of one stage of K (or V)
-    constexpr int PER = (2 * CH + kThreads - 1) / kThreads;   // chunks of K and V per thread
+    constexpr int NKC = CH / kThreads;  // K chunks per thread
+    constexpr int NV = CH / kThreads;   // V chunks (adjacent keys of one column) per thread
+    constexpr int PER = NKC + NV;       // chunks of K and V per thread
+    static_assert(CH % kThreads == 0 && (kThreads / (D / 8)) * NV == KT, "stage shape");
     static_assert(D % 32 == 0, "tile shape");
     static_assert(G >= 1 && G <= 8, "GQA group");
 
@@ -566,39 +569,63 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
             const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
             return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
         };
-        // the K and V rows of one stage, 16 bytes per chunk (chunk c < CH: K, else V); keys
-        // past the chunk of ids clamp to its last key (zeroed when stored)
+        // the K and V rows of one stage, 16 bytes (8 dims of one key) per chunk. K: chunk
+        // c = tid + k * kThreads (k < NKC) is key c / (D/8), column c % (D/8). V: a thread takes
+        // NV adjacent keys of one column (key group tid / (D/8), column tid % (D/8)), so the
+        // transposed store writes each dim's NV keys as one packed word instead of NV scattered
+        // 16-bit stores. Keys past the chunk of ids clamp to its last key (zeroed when stored).
         auto load_kv = [&](int base, uint4 (&r)[PER]) {
 #pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int c = min(threadIdx.x + k * kThreads, 2 * CH - 1);
-                const int cc = c < CH ? c : c - CH;
-                const int key = cc / (D / 8);
-                const int col = cc % (D / 8);
-                const uint16_t* pool = c < CH ? a.k_pool : a.v_pool;
-                r[k] = load_stream(pool + row_off(min(base + key, c_hi - 1)) + 8 * col);
+            for (int k = 0; k < NKC; ++k) {
+                const int c = threadIdx.x + k * kThreads;
+                const int key = c / (D / 8);
+                const int col = c % (D / 8);
+                r[k] = load_stream(a.k_pool + row_off(min(base + key, c_hi - 1)) + 8 * col);
             }
+            const int vcol = threadIdx.x % (D / 8);
+            const int vkey0 = (threadIdx.x / (D / 8)) * NV;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                r[NKC + j] = load_stream(a.v_pool + row_off(min(base + vkey0 + j, c_hi - 1)) +
+                                         8 * vcol);
         };
         auto store_kv = [&](int base, const uint4 (&r)[PER], int buf) {
 #pragma unroll
-            for (int k = 0; k < PER; ++k) {
+            for (int k = 0; k < NKC; ++k) {
                 const int c = threadIdx.x + k * kThreads;
-                if (c < 2 * CH) {
-                    const int cc = c < CH ? c : c - CH;
-                    const int key = cc / (D / 8);
-                    const int col = cc % (D / 8);
-                    const uint4 v = base + key < c_hi ? r[k] : make_uint4(0, 0, 0, 0);
-                    if (c < CH) {
-                        *reinterpret_cast<uint4*>(&s_k[buf][key][8 * col]) = v;
-                    } else {
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                const int key = c / (D / 8);
+                const int col = c % (D / 8);
+                const uint4 v = base + key < c_hi ? r[k] : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(&s_k[buf][key][8 * col]) = v;
+            }
+            const int vcol = threadIdx.x % (D / 8);
+            const int vkey0 = (threadIdx.x / (D / 8)) * NV;
+            uint16_t vv[NV][8];   // [key][dim] codes of this thread's keys
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            s_vt[buf][8 * col + 2 * j][key] = (uint16_t)(w[j] & 0xFFFFu);
-                            s_vt[buf][8 * col + 2 * j + 1][key] = (uint16_t)(w[j] >> 16);
-                        }
-                        if (any_nonfinite<BF16>(v)) s_vbad[buf][key / kTile] = base;
-                    }
+            for (int j = 0; j < NV; ++j) {
+                const uint4 v = base + vkey0 + j < c_hi ? r[NKC + j] : make_uint4(0, 0, 0, 0);
+                if (any_nonfinite<BF16>(v)) s_vbad[buf][(vkey0 + j) / kTile] = base;
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vv[j][2 * i] = (uint16_t)(w[i] & 0xFFFFu);
+                    vv[j][2 * i + 1] = (uint16_t)(w[i] >> 16);
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                uint16_t* dst = &s_vt[buf][8 * vcol + d][vkey0];
+                if constexpr (NV >= 4) {
+#pragma unroll
+                    for (int j = 0; j < NV; j += 4)
+                        *reinterpret_cast<uint2*>(dst + j) = make_uint2(
+                            (uint32_t)vv[j][d] | ((uint32_t)vv[j + 1][d] << 16),
+                            (uint32_t)vv[j + 2][d] | ((uint32_t)vv[j + 3][d] << 16));
+                } else if constexpr (NV == 2) {
+                    *reinterpret_cast<uint32_t*>(dst) =
+                        (uint32_t)vv[0][d] | ((uint32_t)vv[1][d] << 16);
+                } else {
+                    dst[0] = vv[0][d];
                 }
             }
         };
