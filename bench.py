@@ -59,10 +59,13 @@ def profiled_traffic(workload: str):
         return None
 
 
-def algorithmic_bytes(wl: dict) -> dict:
-    """Bytes the step must move (each input read once, each output written once)."""
+def algorithmic_bytes(wl: dict, window: int = 0) -> dict:
+    """Bytes the step must move (each input read once, each output written once); with a
+    sliding window only the last `window` tokens of each sequence are read."""
     B, Hq, Hkv, D, bs = wl["B"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"]
     L = wl["context_lens"].astype(np.int64)
+    if window:
+        L = np.minimum(L, window)
     E = 4 if wl["dtype"] == "f32" else 2           # bytes per pool element
     kv = int(L.sum()) * 2 * Hkv * D * E
     tables = int(((L + bs - 1) // bs).sum()) * 4
@@ -81,13 +84,20 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="pool copies (0: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--workload", choices=["decode", "prefill", "spec", "rope", "f32"],
+    ap.add_argument("--window", type=int, default=0,
+                    help="decode step with a sliding window of this many tokens (layer variant)")
+    ap.add_argument("--rope-dim", type=int, default=0,
+                    help="decode step with partial rotary over this many dims (layer variant)")
+    ap.add_argument("--v-norm", action="store_true",
+                    help="decode step with per-head V normalisation (layer variant)")
+    ap.add_argument("--workload", choices=["decode", "prefill", "spec", "rope", "f32", "blocks"],
                     default="decode",
                     help="decode: the decode step (default); prefill / spec: chunked prefill "
                          "(4 x 512-token chunks) / 4 draft tokens per sequence, append + "
                          "causal paged attention; rope: the decode step with RoPE applied at "
                          "read (un-rotated pool), append + decode; f32: the decode step over "
-                         "float32 pools, append + decode")
+                         "float32 pools, append + decode; blocks: the host block manager "
+                         "(admission with a shared prefix, per-step growth and tables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -96,6 +106,9 @@ def main() -> int:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode step "
               "has no multi-GPU path in this library", file=sys.stderr)
         return 2
+
+    if args.workload == "blocks":
+        return run_blocks(args)
 
     import torch
     import paged_kv_cache_315_amd as pkv
@@ -120,7 +133,9 @@ def main() -> int:
         return run_prefill(args, torch, pkv, W)
 
     wl = W.config(args.config)
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes(wl, args.window)
+    variant = dict(rope_dim=args.rope_dim, v_norm=args.v_norm, window=args.window)
+    has_variant = bool(args.window or args.rope_dim or args.v_norm)
     dev = torch.device("cuda:0")
 
     def t(a, dt=None):
@@ -147,13 +162,13 @@ def main() -> int:
         kp, vp = pools[i % copies]
         pkv.decode_step(q, k_new, v_new, kp, vp, tables, positions, theta=wl["theta"],
                         scale=wl["scale"], q_norm_w=qn, k_norm_w=kn, eps=wl["eps"], q_out=q_out,
-                        out=out, workspace=ws, dtype=wl["dtype"], stream=stream)
+                        out=out, workspace=ws, dtype=wl["dtype"], stream=stream, **variant)
 
     def decode_only(i):
         kp, vp = pools[i % copies]
         pkv.paged_attn_decode(q_out, kp, vp, tables, ctx, wl["max_context_len"], wl["scale"],
                               out=out, workspace=ws, split_tokens=split, dtype=wl["dtype"],
-                              stream=stream)
+                              window=args.window, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -196,7 +211,8 @@ def main() -> int:
            "p90": round(float(np.percentile(lat_us, 90)), 2), "launches": n_lat}
 
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    traffic_bytes = profiled_traffic(wl["name"]) if args.split_tokens == 0 else None
+    traffic_bytes = (profiled_traffic(wl["name"]) if args.split_tokens == 0 and not has_variant
+                     else None)
     tokens_per_s = B / (ms_per_step * 1e-3)
 
     cpu = None
@@ -204,7 +220,8 @@ def main() -> int:
         import oracle
         oracle.load()
         c0 = time.perf_counter()
-        oracle.decode_step(wl)
+        oracle.decode_step(wl, rope_dim=args.rope_dim or None, v_norm=args.v_norm,
+                           window=args.window)
         cpu_s = time.perf_counter() - c0
         cpu = {"value": round(nbytes["step"] / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
@@ -227,7 +244,9 @@ def main() -> int:
         "pct_of_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
         "config": {
-            "workload": wl["name"], "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "workload": wl["name"] + ("-variant" if has_variant else ""), "batch": B,
+            "num_q_heads": Hq, "num_kv_heads": Hkv, "window": args.window,
+            "rope_dim": args.rope_dim or D, "v_norm": args.v_norm,
             "head_dim": D, "block_size": wl["bs"], "kv_dtype": wl["dtype"],
             "context_tokens": int(wl["context_lens"].sum()),
             "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
@@ -238,7 +257,9 @@ def main() -> int:
         # the step is one launch of the fused kernel, so the step time is its launch time;
         # traffic = rocprofv3-measured HBM bytes per launch over the same launch time
         "roofline": {
-            "bound": "hbm", "kernel": "decode_balanced_kernel (append fused, pkv_decode_step)",
+            "bound": "hbm",
+            "kernel": "decode_balanced_kernel (append fused, pkv_decode_step" +
+                      (", variant fields read at run time)" if has_variant else ")"),
             "achieved": round(step_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(step_gbs / HBM_PEAK_GBS, 4),
             "traffic": (None if traffic_bytes is None
@@ -371,6 +392,88 @@ def run_rope(args, torch, pkv, W) -> int:
                    "avg_launch_us": round(append_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "wall_ms_timed_steps": round(wall_ms, 2),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_blocks(args) -> int:
+    """Host block manager (include/pkv_blocks.h) on the prefix-shared decode workload's shape:
+    128 sequences whose prompts share 2048 tokens plus a private tail of U{0..1024}, block size
+    16. Timed: admission of the batch (the first prompt cold and committed, the others borrowing
+    its 128 prefix blocks), then decode steps (room for one token, the table rows and positions
+    filled for the batch, one token committed and recorded per sequence: pkv_batch_prepare and
+    pkv_batch_commit). Host code only; the baseline is the Python oracle model doing the same
+    per sequence."""
+    from paged_kv_cache_315_amd import blocks as BM
+    rng = np.random.default_rng([5, 99])
+    B, bs, prefix_len = 128, 16, 2048
+    prefix = rng.integers(0, 32000, prefix_len).tolist()
+    tails = rng.integers(0, 1025, B)
+    prompts = [prefix + rng.integers(0, 32000, int(t)).tolist() for t in tails]
+    max_blocks = (prefix_len + 1024 + args.steps + bs - 1) // bs + 1
+    nb = 128 + B * (1024 // bs + 2) + B * (args.steps // bs + 2)
+    steps = max(args.steps, 1)
+
+    def run(make_pool, make_seq, fill):
+        pool = make_pool(nb, bs)
+        seqs = [make_seq(pool) for _ in range(B)]
+        t0 = time.perf_counter()
+        seqs[0].allocate_for_tokens(prompts[0])
+        seqs[0].commit(len(prompts[0]))
+        for s, p in zip(seqs[1:], prompts[1:]):
+            s.allocate_for_tokens(p)
+        t_admit = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for i in range(steps):
+            for s in seqs:
+                s.reserve(1)
+            fill(seqs)
+            for s in seqs:
+                s.commit(1)
+                s.append_token(i)
+        return t_admit, (time.perf_counter() - t0) / steps
+
+    # native: one C call per step for room + tables and one for the commit (Batch)
+    pool = BM.BlockPool(nb, bs)
+    seqs = [BM.SeqCache(pool, 0) for _ in range(B)]
+    t0 = time.perf_counter()
+    seqs[0].allocate_for_tokens(prompts[0])
+    seqs[0].commit(len(prompts[0]))
+    for s, p in zip(seqs[1:], prompts[1:]):
+        s.allocate_for_tokens(p)
+    t_admit = time.perf_counter() - t0
+    batch = BM.Batch(seqs, max_blocks, 0)
+    ids = np.zeros(B, np.int32)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        batch.prepare(1)
+        ids[:] = i
+        batch.commit(1, ids)
+    native = (t_admit, (time.perf_counter() - t0) / steps)
+    for s in seqs:
+        s.destroy()
+    pool.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.block_manager as OB
+        ref = run(lambda n, b: OB.Pool(n, b), lambda p: OB.Seq(p, 0),
+                  lambda ss: OB.fill_tables(ss, max_blocks, 0))
+        cpu = {"value": round(ref[1] * 1e6, 1), "unit": "us per decode step", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the same {steps} steps on the Python oracle model "
+                         f"(admission {ref[0] * 1e3:.1f} ms)"}
+    line = {
+        "metric": "host block manager: us per decode step (128 sequences, tables + growth)",
+        "value": round(native[1] * 1e6, 2), "unit": "us", "n_gpus": 0, "steps": steps,
+        "warmup": 0, "ms_per_step": round(native[1] * 1e3, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "prefix-shared-blocks", "batch": B, "block_size": bs,
+                   "shared_prefix_tokens": prefix_len, "tail_tokens": "U{0..1024}",
+                   "pool_blocks": nb, "max_blocks_per_seq": max_blocks},
+        "admission_ms": round(native[0] * 1e3, 3),
+        "roofline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0

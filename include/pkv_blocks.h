@@ -132,6 +132,19 @@ pkv_status pkv_seq_blocks(pkv_seq_cache* seq, int32_t* block_ids, uint8_t* owned
 pkv_status pkv_fill_block_tables(pkv_seq_cache* const* seqs, int B, int max_blocks_per_seq,
                                  int32_t pad_block, int32_t* block_tables, int32_t* positions);
 
+/* One decode (or chunk) step for a batch, host side: pkv_seq_reserve(seqs[b], new_tokens) for
+ * every sequence in order, then (block_tables non-NULL) pkv_fill_block_tables. On a failed
+ * reserve the sequences before it keep their room; the error names the sequence. */
+pkv_status pkv_batch_prepare(pkv_seq_cache* const* seqs, int B, int new_tokens,
+                             int max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
+                             int32_t* positions);
+
+/* After the step: for every sequence, its new_tokens token ids (host int32 [B, new_tokens], or
+ * NULL to record none) through pkv_seq_append_token, then pkv_seq_commit(new_tokens). Stops at
+ * the first failure. */
+pkv_status pkv_batch_commit(pkv_seq_cache* const* seqs, int B, int new_tokens,
+                            const int32_t* token_ids);
+
 #ifdef __cplusplus
 }
 #endif

@@ -146,3 +146,35 @@ def fill_block_tables(seqs, max_blocks_per_seq: int, pad_block: int):
                                                  tables.ctypes.data, positions.ctypes.data),
                "pkv_fill_block_tables")
     return tables, positions
+
+
+class Batch:
+    """A fixed list of sequences driven together: one C call per step for room + tables and one
+    for the commit (the per-sequence calls cost a Python round trip each)."""
+
+    def __init__(self, seqs, max_blocks_per_seq: int, pad_block: int):
+        self.seqs = list(seqs)
+        self.B = len(self.seqs)
+        self._arr = (ctypes.c_void_p * max(self.B, 1))(*[s.handle.value for s in self.seqs])
+        self.max_blocks = max_blocks_per_seq
+        self.pad = pad_block
+        self.tables = np.zeros((self.B, max_blocks_per_seq), np.int32)
+        self.positions = np.zeros(self.B, np.int32)
+        self._lib = _lib.load()
+
+    def prepare(self, new_tokens: int = 1):
+        """Room for new_tokens per sequence; returns (tables, positions), host int32 arrays
+        reused by every call."""
+        _lib.check(self._lib.pkv_batch_prepare(self._arr, self.B, new_tokens, self.max_blocks,
+                                               self.pad, self.tables.ctypes.data,
+                                               self.positions.ctypes.data), "pkv_batch_prepare")
+        return self.tables, self.positions
+
+    def commit(self, new_tokens: int = 1, token_ids=None):
+        ids = None if token_ids is None else _i32(token_ids)
+        if ids is not None:
+            assert ids.size == self.B * new_tokens
+        _lib.check(self._lib.pkv_batch_commit(self._arr, self.B, new_tokens,
+                                              None if ids is None else ids.ctypes.data),
+                   "pkv_batch_commit")
+

@@ -407,4 +407,38 @@ pkv_status pkv_fill_block_tables(pkv_seq_cache* const* seqs, int B, int max_bloc
     return PKV_OK;
 }
 
+pkv_status pkv_batch_prepare(pkv_seq_cache* const* seqs, int B, int new_tokens,
+                             int max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
+                             int32_t* positions) {
+    if (B < 0 || (B > 0 && !seqs) || new_tokens < 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_batch_prepare: NULL sequences, B < 0 or new_tokens < 0");
+    for (int b = 0; b < B; ++b) {
+        const pkv_status st = pkv_seq_reserve(seqs[b], new_tokens, nullptr);
+        if (st != PKV_OK) {
+            char msg[512];
+            snprintf(msg, sizeof(msg), "%s", pkv_last_error());
+            return fail(st, "pkv_batch_prepare: sequence %d: %s", b, msg);
+        }
+    }
+    if (!block_tables) return PKV_OK;
+    return pkv_fill_block_tables(seqs, B, max_blocks_per_seq, pad_block, block_tables, positions);
+}
+
+pkv_status pkv_batch_commit(pkv_seq_cache* const* seqs, int B, int new_tokens,
+                            const int32_t* token_ids) {
+    if (B < 0 || (B > 0 && !seqs) || new_tokens < 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_batch_commit: NULL sequences, B < 0 or new_tokens < 0");
+    for (int b = 0; b < B; ++b) {
+        if (!seqs[b]) return fail(PKV_ERR_INVALID_ARG, "pkv_batch_commit: sequence %d is NULL", b);
+        if (token_ids)
+            for (int i = 0; i < new_tokens; ++i) {
+                const pkv_status st = pkv_seq_append_token(seqs[b], token_ids[(size_t)b * new_tokens + i]);
+                if (st != PKV_OK) return st;
+            }
+        const pkv_status st = pkv_seq_commit(seqs[b], new_tokens);
+        if (st != PKV_OK) return st;
+    }
+    return PKV_OK;
+}
+
 }  // extern "C"

@@ -433,3 +433,39 @@ def test_native_pool_is_safe_under_concurrent_sequences():
             s.destroy()
     assert (pool.block_state()[0] == 0).all() and pool.stats().num_free == 64
     pool.close()
+
+
+def test_native_batch_calls_match_per_sequence_oracle():
+    """pkv_batch_prepare / pkv_batch_commit (one C call per step for the whole batch) leave the
+    pool and the sequences as the oracle's per-sequence reserve, table fill, token record and
+    commit do."""
+    B = _lib()
+    rng = random.Random(77)
+    npool, opool = B.BlockPool(80, 4), O.Pool(80, 4)
+    prefix = [rng.randrange(100) for _ in range(9)]
+    prompts = [prefix + [rng.randrange(100) for _ in range(rng.randrange(0, 7))] for _ in range(5)]
+    nseqs = [B.SeqCache(npool) for _ in prompts]
+    oseqs = [O.Seq(opool) for _ in prompts]
+    for i, (n, o, p) in enumerate(zip(nseqs, oseqs, prompts)):
+        assert n.allocate_for_tokens(p) == o.allocate_for_tokens(p)
+        if i == 0:
+            n.commit(len(p))
+            o.commit(len(p))
+    batch = B.Batch(nseqs, 12, pad_block=79)
+    for step in range(9):
+        k = 1 + step % 3
+        tables, pos = batch.prepare(k)
+        for o in oseqs:
+            o.reserve(k)
+        rows, opos = O.fill_tables(oseqs, 12, 79)
+        assert tables.tolist() == rows and pos.tolist() == opos
+        ids = [[rng.randrange(100) for _ in range(k)] for _ in oseqs]
+        batch.commit(k, ids)
+        for o, t in zip(oseqs, ids):
+            for x in t:
+                o.append_token(x)
+            o.commit(k)
+        _compare(npool, opool, nseqs, oseqs)
+    for s in nseqs:
+        s.destroy()
+    npool.close()
