@@ -61,6 +61,7 @@ typedef struct {
     int num_tokens;    /* token ids known (prompt + pkv_seq_append_token) */
     int num_blocks;    /* blocks held */
     int num_hashes;    /* block hashes known */
+    int num_dropped;   /* leading blocks given back by pkv_seq_drop_before (ids -1) */
 } pkv_seq_state;
 
 /* A pool of num_blocks ids (1 .. 2^31-1), all free, none cached; block_size > 0 tokens. */
@@ -113,7 +114,8 @@ pkv_status pkv_seq_commit(pkv_seq_cache* seq, int new_tokens);
 
 /* Truncate: rewinds num_computed (and num_written) to seq_len when it is smaller; blocks, token
  * ids and hashes are kept, as on the page (a rewind across a committed block leaves that block
- * cached under its old tokens' hash, so callers rewind only within the uncommitted tail). */
+ * cached under its old tokens' hash, so callers rewind only within the uncommitted tail).
+ * INVALID_ARG if seq_len falls inside blocks given back by pkv_seq_drop_before. */
 pkv_status pkv_seq_truncate(pkv_seq_cache* seq, int seq_len);
 
 /* Free: gives back every block (one reference each), clears tokens, hashes and counts. */
@@ -121,21 +123,37 @@ pkv_status pkv_seq_free(pkv_seq_cache* seq);
 
 pkv_status pkv_seq_info(pkv_seq_cache* seq, pkv_seq_state* state);
 
-/* The sequence's block ids, owned flags (0 = borrowed from the cache) and known hashes, into
- * host arrays of `capacity` entries (any may be NULL); INVALID_ARG if capacity is too small. */
+/* The sequence's block ids (-1 for blocks given back by pkv_seq_drop_before), owned flags (0 =
+ * borrowed from the cache, or given back) and known hashes, into host arrays of `capacity`
+ * entries (any may be NULL); INVALID_ARG if capacity is too small. */
 pkv_status pkv_seq_blocks(pkv_seq_cache* seq, int32_t* block_ids, uint8_t* owned,
                           uint64_t* hashes, int capacity);
 
+/* Sliding-window layers (page "soft3/glia/run/arch/decoder/forward.rs", forward_layer: a sliding layer keeps
+ * a ring of cache_seq slots, so a token older than the window is overwritten and never read
+ * again). In a paged pool the same reuse happens one block at a time: every block held whose
+ * tokens all lie before first_pos (block index < first_pos / block_size) is given back (one
+ * reference, as pkv_seq_free does) and its entry becomes -1; the table keeps its logical
+ * indexing, so the kernels address tokens as before and pkv_fill_block_tables writes pad_block
+ * for these entries. A decode step of window W attending L tokens reads from max(0, L - W) on,
+ * so first_pos = num_computed + 1 - W is safe before the step. Hashes and token ids are kept
+ * (later blocks' hashes chain through them). *num_dropped (may be NULL) receives the number of
+ * leading entries given back so far. Errors: first_pos < 0 or > num_computed. */
+pkv_status pkv_seq_drop_before(pkv_seq_cache* seq, int first_pos, int* num_dropped);
+
 /* Batch tables for the paged calls: row b of block_tables (host int32 [B, max_blocks_per_seq])
- * = seqs[b]'s block ids, padded with pad_block; positions[b] (host int32 [B], may be NULL) =
- * its num_computed. INVALID_ARG if a sequence holds more than max_blocks_per_seq blocks. */
+ * = seqs[b]'s block ids, padded with pad_block (also in place of entries given back by
+ * pkv_seq_drop_before); positions[b] (host int32 [B], may be NULL) = its num_computed.
+ * INVALID_ARG if a sequence holds more than max_blocks_per_seq entries. */
 pkv_status pkv_fill_block_tables(pkv_seq_cache* const* seqs, int B, int max_blocks_per_seq,
                                  int32_t pad_block, int32_t* block_tables, int32_t* positions);
 
-/* One decode (or chunk) step for a batch, host side: pkv_seq_reserve(seqs[b], new_tokens) for
- * every sequence in order, then (block_tables non-NULL) pkv_fill_block_tables. On a failed
- * reserve the sequences before it keep their room; the error names the sequence. */
-pkv_status pkv_batch_prepare(pkv_seq_cache* const* seqs, int B, int new_tokens,
+/* One decode (or chunk) step for a batch, host side: for every sequence in order, when
+ * window > 0, pkv_seq_drop_before(seqs[b], max(0, num_computed + 1 - window)) (the first key
+ * the step's first new token attends under a sliding window of that many tokens), then
+ * pkv_seq_reserve(seqs[b], new_tokens); then (block_tables non-NULL) pkv_fill_block_tables. On a
+ * failed reserve the sequences before it keep their room; the error names the sequence. */
+pkv_status pkv_batch_prepare(pkv_seq_cache* const* seqs, int B, int new_tokens, int window,
                              int max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
                              int32_t* positions);
 

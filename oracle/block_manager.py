@@ -10,7 +10,10 @@ does with its blocks, written from the PagedKVCache methods in the page's order:
   AppendToken       — record the token; when a block completes, hash it chained to the
                       previous block's hash and add a block if needed;
   Commit            — advance the computed count; cache the blocks it completed;
-  Truncate, Free, SeqLen.
+  Truncate, Free, SeqLen;
+and, for sliding-window layers (page "soft3/glia/run/arch/decoder/forward.rs", forward_layer:
+a sliding layer's cache is a ring whose slots older than the window are reused), drop_before
+gives back the blocks whose tokens all precede the window's first key (entries become -1).
 The pool (BlockPool) is not on the page; this model follows the reading its call sites
 support: reference counts; a free list handed out front first and refilled at the back; a
 hash -> block map; a freed cached block stays findable until it is handed out again; a hash
@@ -84,6 +87,8 @@ class Pool:
 
     def release(self, blocks):
         for b in blocks:
+            if b < 0:                          # already given back (drop_before)
+                continue
             if self.ref[b] > 0:
                 self.ref[b] -= 1
                 if self.ref[b] == 0:
@@ -121,6 +126,7 @@ class Seq:
         self.hashes = []
         self.num_computed = 0
         self.num_written = 0
+        self.dropped = 0
         pool.live_seqs += 1
 
     def allocate_for_tokens(self, tokens):
@@ -189,11 +195,28 @@ class Seq:
         self.num_written = max(self.num_written, self.num_computed)
         lo = old // bs
         hi = min(self.num_computed // bs, len(self.hashes), len(self.blocks))
-        if hi > lo:
-            self.pool.cache_blocks(self.blocks[lo:hi], self.hashes[lo:hi])
+        for i in range(lo, hi):
+            if self.blocks[i] >= 0:
+                self.pool.cache_blocks([self.blocks[i]], [self.hashes[i]])
+
+    def drop_before(self, first_pos):
+        """Blocks 0 .. first_pos // block_size - 1 go back to the pool (one reference each);
+        their entries become -1. Only computed tokens can be dropped."""
+        if first_pos < 0 or first_pos > self.num_computed:
+            raise BlockError("first_pos outside [0, num_computed]")
+        upto = min(len(self.blocks), first_pos // self.pool.block_size)
+        for i in range(upto):
+            if self.blocks[i] >= 0:
+                self.pool.release([self.blocks[i]])
+                self.blocks[i] = -1
+                self.owned[i] = False
+        self.dropped = max(self.dropped, upto)
+        return self.dropped
 
     def truncate(self, seq_len):
         seq_len = max(seq_len, 0)
+        if seq_len < self.num_computed and seq_len < self.dropped * self.pool.block_size:
+            raise BlockError("tokens before the dropped blocks' end are gone")
         if seq_len < self.num_computed:
             self.num_computed = seq_len
             self.num_written = min(self.num_written, seq_len)
@@ -202,6 +225,7 @@ class Seq:
         self.pool.release(self.blocks)
         self.blocks, self.owned, self.tokens, self.hashes = [], [], [], []
         self.num_computed = self.num_written = 0
+        self.dropped = 0
 
     def destroy(self):
         self.free()
@@ -214,6 +238,7 @@ def fill_tables(seqs, max_blocks_per_seq, pad_block):
     for s in seqs:
         if len(s.blocks) > max_blocks_per_seq:
             raise BlockError("more blocks than the table row holds")
-        rows.append(s.blocks + [pad_block] * (max_blocks_per_seq - len(s.blocks)))
+        rows.append([b if b >= 0 else pad_block for b in s.blocks]
+                    + [pad_block] * (max_blocks_per_seq - len(s.blocks)))
         positions.append(s.num_computed)
     return rows, positions

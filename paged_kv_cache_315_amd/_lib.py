@@ -66,11 +66,12 @@ SIGNATURES = {
     "pkv_seq_append_token": (_I, [_P, ctypes.c_int32]),
     "pkv_seq_commit": (_I, [_P, _I]),
     "pkv_seq_truncate": (_I, [_P, _I]),
+    "pkv_seq_drop_before": (_I, [_P, _I, _P]),
     "pkv_seq_free": (_I, [_P]),
     "pkv_seq_info": (_I, [_P, _P]),
     "pkv_seq_blocks": (_I, [_P, _P, _P, _P, _I]),
     "pkv_fill_block_tables": (_I, [_P, _I, _I, ctypes.c_int32, _P, _P]),
-    "pkv_batch_prepare": (_I, [_P, _I, _I, _I, ctypes.c_int32, _P, _P]),
+    "pkv_batch_prepare": (_I, [_P, _I, _I, _I, _I, ctypes.c_int32, _P, _P]),
     "pkv_batch_commit": (_I, [_P, _I, _I, _P]),
     "pkv_status_string": (ctypes.c_char_p, [_I]),
     "pkv_last_error": (ctypes.c_char_p, []),

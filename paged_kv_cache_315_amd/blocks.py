@@ -21,7 +21,7 @@ class PoolInfo(ctypes.Structure):
 class SeqState(ctypes.Structure):
     _fields_ = [("num_computed", ctypes.c_int), ("num_written", ctypes.c_int),
                 ("num_tokens", ctypes.c_int), ("num_blocks", ctypes.c_int),
-                ("num_hashes", ctypes.c_int)]
+                ("num_hashes", ctypes.c_int), ("num_dropped", ctypes.c_int)]
 
 
 def _i32(a) -> np.ndarray:
@@ -111,6 +111,14 @@ class SeqCache:
     def truncate(self, seq_len: int):
         _lib.check(self._lib.pkv_seq_truncate(self._h, seq_len), "pkv_seq_truncate")
 
+    def drop_before(self, first_pos: int) -> int:
+        """Give back the blocks whose tokens all lie before first_pos (sliding window); returns
+        how many leading entries are given back so far."""
+        n = ctypes.c_int(0)
+        _lib.check(self._lib.pkv_seq_drop_before(self._h, first_pos, ctypes.byref(n)),
+                   "pkv_seq_drop_before")
+        return n.value
+
     def free(self):
         _lib.check(self._lib.pkv_seq_free(self._h), "pkv_seq_free")
 
@@ -120,7 +128,7 @@ class SeqCache:
         return st
 
     def blocks(self):
-        """(block ids int32, owned bool, hashes uint64)."""
+        """(block ids int32 (-1 where given back by drop_before), owned bool, hashes uint64)."""
         st = self.state()
         cap = max(st.num_blocks, st.num_hashes, 1)
         ids = np.zeros(cap, np.int32)
@@ -162,10 +170,12 @@ class Batch:
         self.positions = np.zeros(self.B, np.int32)
         self._lib = _lib.load()
 
-    def prepare(self, new_tokens: int = 1):
-        """Room for new_tokens per sequence; returns (tables, positions), host int32 arrays
+    def prepare(self, new_tokens: int = 1, window: int = 0):
+        """Room for new_tokens per sequence (after giving back the blocks wholly behind a sliding
+        window of `window` tokens, when > 0); returns (tables, positions), host int32 arrays
         reused by every call."""
-        _lib.check(self._lib.pkv_batch_prepare(self._arr, self.B, new_tokens, self.max_blocks,
+        _lib.check(self._lib.pkv_batch_prepare(self._arr, self.B, new_tokens, window,
+                                               self.max_blocks,
                                                self.pad, self.tables.ctypes.data,
                                                self.positions.ctypes.data), "pkv_batch_prepare")
         return self.tables, self.positions

@@ -127,6 +127,7 @@ struct pkv_seq_cache {
     std::vector<uint64_t> hashes;
     int num_computed = 0;
     int num_written = 0;
+    int dropped = 0;  // leading entries given back behind a sliding window (id -1 in `blocks`)
 
     // grow the block list to `required` blocks, all or nothing
     bool ensure_capacity(int64_t required) {
@@ -138,9 +139,21 @@ struct pkv_seq_cache {
         return true;
     }
     void release_all() {
-        for (int32_t b : blocks) pool->release(b);
+        for (int32_t b : blocks)
+            if (b >= 0) pool->release(b);
         blocks.clear();
         owned.clear();
+        dropped = 0;
+    }
+    // give back every held block whose tokens all lie before first_pos
+    void drop_before(int first_pos) {
+        const int bs = pool->block_size;
+        const int upto = std::min((int)blocks.size(), first_pos / bs);
+        for (; dropped < upto; ++dropped) {
+            pool->release(blocks[dropped]);
+            blocks[dropped] = -1;
+            owned[dropped] = 0;
+        }
     }
 };
 
@@ -337,7 +350,8 @@ pkv_status pkv_seq_commit(pkv_seq_cache* s, int new_tokens) {
     const int bs = p->block_size;
     size_t lo = old_computed / bs, hi = s->num_computed / bs;
     hi = std::min(hi, std::min(s->hashes.size(), s->blocks.size()));
-    for (size_t i = lo; i < hi; ++i) p->cache(s->blocks[i], s->hashes[i]);
+    for (size_t i = lo; i < hi; ++i)
+        if (s->blocks[i] >= 0) p->cache(s->blocks[i], s->hashes[i]);
     return PKV_OK;
 }
 
@@ -346,6 +360,9 @@ pkv_status pkv_seq_truncate(pkv_seq_cache* s, int seq_len) {
     std::lock_guard<std::mutex> lk(s->pool->mu);
     if (seq_len < 0) seq_len = 0;
     if (seq_len >= s->num_computed) return PKV_OK;
+    if (seq_len < s->dropped * s->pool->block_size)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_seq_truncate: tokens before %d were given back (pkv_seq_drop_before)",
+                    s->dropped * s->pool->block_size);
     s->num_computed = seq_len;
     if (s->num_written > s->num_computed) s->num_written = s->num_computed;
     return PKV_OK;
@@ -369,6 +386,7 @@ pkv_status pkv_seq_info(pkv_seq_cache* s, pkv_seq_state* st) {
     st->num_tokens = (int)s->tokens.size();
     st->num_blocks = (int)s->blocks.size();
     st->num_hashes = (int)s->hashes.size();
+    st->num_dropped = s->dropped;
     return PKV_OK;
 }
 
@@ -401,18 +419,34 @@ pkv_status pkv_fill_block_tables(pkv_seq_cache* const* seqs, int B, int max_bloc
                         s->blocks.size(), max_blocks_per_seq);
         int32_t* row = block_tables + (size_t)b * max_blocks_per_seq;
         for (int i = 0; i < max_blocks_per_seq; ++i)
-            row[i] = i < (int)s->blocks.size() ? s->blocks[i] : pad_block;
+            row[i] = i < (int)s->blocks.size() && s->blocks[i] >= 0 ? s->blocks[i] : pad_block;
         if (positions) positions[b] = s->num_computed;
     }
     return PKV_OK;
 }
 
-pkv_status pkv_batch_prepare(pkv_seq_cache* const* seqs, int B, int new_tokens,
+pkv_status pkv_seq_drop_before(pkv_seq_cache* s, int first_pos, int* num_dropped) {
+    if (!s) return fail(PKV_ERR_INVALID_ARG, "pkv_seq_drop_before: sequence is NULL");
+    std::lock_guard<std::mutex> lk(s->pool->mu);
+    if (first_pos < 0 || first_pos > s->num_computed)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_seq_drop_before: first_pos %d outside [0, %d]", first_pos,
+                    s->num_computed);
+    s->drop_before(first_pos);
+    if (num_dropped) *num_dropped = s->dropped;
+    return PKV_OK;
+}
+
+pkv_status pkv_batch_prepare(pkv_seq_cache* const* seqs, int B, int new_tokens, int window,
                              int max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
                              int32_t* positions) {
-    if (B < 0 || (B > 0 && !seqs) || new_tokens < 0)
-        return fail(PKV_ERR_INVALID_ARG, "pkv_batch_prepare: NULL sequences, B < 0 or new_tokens < 0");
+    if (B < 0 || (B > 0 && !seqs) || new_tokens < 0 || window < 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_batch_prepare: NULL sequences, B < 0, new_tokens < 0 or window < 0");
     for (int b = 0; b < B; ++b) {
+        if (window > 0 && seqs[b]) {
+            pkv_seq_cache* s = seqs[b];
+            std::lock_guard<std::mutex> lk(s->pool->mu);
+            s->drop_before(std::max(0, s->num_computed + 1 - window));
+        }
         const pkv_status st = pkv_seq_reserve(seqs[b], new_tokens, nullptr);
         if (st != PKV_OK) {
             char msg[512];

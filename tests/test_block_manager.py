@@ -114,7 +114,10 @@ def test_reserve_append_token_truncate():
 def _invariants(pool: O.Pool, seqs):
     holders = [0] * pool.num_blocks
     for s in seqs:
-        for b in s.blocks:
+        for i, b in enumerate(s.blocks):
+            if b < 0:                          # given back behind a sliding window
+                assert i < s.dropped
+                continue
             holders[b] += 1
     assert pool.ref == holders
     assert sorted(pool.free) == [b for b in range(pool.num_blocks) if holders[b] == 0]
@@ -129,14 +132,15 @@ def _invariants(pool: O.Pool, seqs):
             parent = h
 
 
-def _random_ops(seed, n_ops=400):
+def _random_ops(seed, n_ops=400, drops=False):
     """A seeded list of operations over a few sequences: admissions of prompts drawn from a few
-    shared prefixes, reserves, token appends with commits, truncations, frees."""
+    shared prefixes, reserves, token appends with commits, truncations, frees (and, with drops,
+    sliding-window drop_before calls, some past the computed tokens)."""
     rng = random.Random(seed)
     prefixes = [[rng.randrange(50) for _ in range(rng.randrange(1, 14))] for _ in range(3)]
     ops = []
     for _ in range(n_ops):
-        k = rng.randrange(6)
+        k = rng.randrange(7 if drops else 6)
         s = rng.randrange(4)
         if k == 0:
             p = list(rng.choice(prefixes)) + [rng.randrange(50) for _ in range(rng.randrange(0, 6))]
@@ -151,8 +155,10 @@ def _random_ops(seed, n_ops=400):
             ops.append(("commit", s, rng.randrange(0, 9)))
         elif k == 4:
             ops.append(("truncate", s, rng.randrange(0, 12)))
-        else:
+        elif k == 5:
             ops.append(("free", s, None))
+        else:
+            ops.append(("drop", s, rng.randrange(0, 18)))
     return ops
 
 
@@ -168,16 +174,18 @@ def _apply_oracle(seq: O.Seq, op, arg):
             return seq.commit(arg)
         if op == "truncate":
             return seq.truncate(arg)
+        if op == "drop":
+            return seq.drop_before(arg)
         return seq.free()
     except O.BlockError:
         return "err"
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(9))
 def test_oracle_invariants_random(seed):
     pool = O.Pool(12, 4)
     seqs = [O.Seq(pool, max_seq_len=24) for _ in range(4)]
-    for op, s, arg in _random_ops(seed):
+    for op, s, arg in _random_ops(seed, drops=seed >= 6):
         _apply_oracle(seqs[s], op, arg)
         _invariants(pool, seqs)
     for s in seqs:
@@ -215,6 +223,8 @@ def _apply_native(seq, op, arg):
             return seq.commit(arg)
         if op == "truncate":
             return seq.truncate(arg)
+        if op == "drop":
+            return seq.drop_before(arg)
         return seq.free()
     except PkvError:
         return "err"
@@ -232,22 +242,22 @@ def _compare(npool, opool, nseqs, oseqs):
         assert ids.tolist() == os_.blocks and owned.tolist() == os_.owned
         assert [int(h) for h in hs] == os_.hashes
         s = ns.state()
-        assert (s.num_computed, s.num_written, s.num_tokens) == \
-            (os_.num_computed, os_.num_written, len(os_.tokens))
+        assert (s.num_computed, s.num_written, s.num_tokens, s.num_dropped) == \
+            (os_.num_computed, os_.num_written, len(os_.tokens), os_.dropped)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_native_matches_oracle_random(seed):
     B = _lib()
     nb, bs = (12, 4) if seed % 2 == 0 else (20, 3)
     npool, opool = B.BlockPool(nb, bs), O.Pool(nb, bs)
     nseqs = [B.SeqCache(npool, max_seq_len=24) for _ in range(4)]
     oseqs = [O.Seq(opool, max_seq_len=24) for _ in range(4)]
-    for i, (op, s, arg) in enumerate(_random_ops(100 + seed)):
+    for i, (op, s, arg) in enumerate(_random_ops(100 + seed, drops=seed >= 8)):
         rn = _apply_native(nseqs[s], op, arg)
         ro = _apply_oracle(oseqs[s], op, arg)
         assert (rn == "err") == (ro == "err"), (i, op, s, arg, rn, ro)
-        if op in ("admit", "reserve") and ro != "err":
+        if op in ("admit", "reserve", "drop") and ro != "err":
             assert rn == ro, (i, op, rn, ro)
         _compare(npool, opool, nseqs, oseqs)
     tables, pos = B.fill_block_tables(nseqs, 8, pad_block=nb - 1)
@@ -280,11 +290,39 @@ def test_native_errors():
     pool.close()
 
 
+def test_drop_before_gives_back_whole_blocks_only():
+    """Worked by hand (block size 4): a sequence with 10 computed tokens holds blocks for tokens
+    0-3, 4-7, 8-11. A sliding window whose first key is token 9 no longer needs tokens 0-8, but
+    token 8 shares its block with 9, so exactly the first two blocks go back, to the end of the
+    free list in order; a smaller first_pos later changes nothing; a rewind into the given-back
+    tokens is refused; the table pads the given-back entries."""
+    pool = O.Pool(6, 4)
+    s = O.Seq(pool)
+    s.allocate_for_tokens(list(range(10)))
+    s.commit(10)
+    assert s.blocks == [0, 1, 2] and pool.free == [3, 4, 5]
+    assert s.drop_before(9) == 2
+    assert s.blocks == [-1, -1, 2] and s.owned == [False, False, True]
+    assert pool.free == [3, 4, 5, 0, 1] and pool.ref[:3] == [0, 0, 1]
+    assert 0x0 not in pool.cached_hash or pool.cache[pool.cached_hash[0]] == 0   # still findable
+    assert s.drop_before(3) == 2 and pool.free == [3, 4, 5, 0, 1]
+    with pytest.raises(O.BlockError):
+        s.drop_before(11)                     # past the computed tokens
+    with pytest.raises(O.BlockError):
+        s.truncate(7)
+    s.truncate(8)
+    assert s.num_computed == 8
+    rows, pos = O.fill_tables([s], 4, 5)
+    assert rows == [[5, 5, 2, 5]] and pos == [8]
+    s.destroy()
+    assert pool.ref == [0] * 6 and pool.free == [3, 4, 5, 0, 1, 2]
+
+
 # ---------------------------------------------------------------- planted mistakes in the oracle
 
 _SCENARIO_PINS = [test_block_hash_byte_layout, test_cold_prompt_then_commit_then_shared_prompt,
                   test_failed_admission_changes_nothing, test_freed_cached_block_is_found_until_reused,
-                  test_reserve_append_token_truncate]
+                  test_reserve_append_token_truncate, test_drop_before_gives_back_whole_blocks_only]
 
 
 def _mut_no_chain(tokens, parent=None):
@@ -347,7 +385,21 @@ def _mut_commit_partial_block(self, new_tokens):
         self.pool.cache_blocks(self.blocks[lo:hi], self.hashes[lo:hi])
 
 
+def _mut_drop_partial_block(self, first_pos):
+    if first_pos < 0 or first_pos > self.num_computed:
+        raise O.BlockError("first_pos outside [0, num_computed]")
+    upto = min(len(self.blocks), -(-first_pos // self.pool.block_size))   # the block of first_pos too
+    for i in range(upto):
+        if self.blocks[i] >= 0:
+            self.pool.release([self.blocks[i]])
+            self.blocks[i] = -1
+            self.owned[i] = False
+    self.dropped = max(self.dropped, upto)
+    return self.dropped
+
+
 MUTANTS = {
+    "drop gives back the block holding first_pos": ("drop_before", O.Seq, _mut_drop_partial_block),
     "hash not chained to the parent": ("block_hash", O, _mut_no_chain),
     "free list handed out newest first": ("allocate", O.Pool, _mut_lifo_allocate),
     "reused block keeps its cache entry": ("allocate", O.Pool, _mut_keep_stale_cache),
@@ -433,6 +485,42 @@ def test_native_pool_is_safe_under_concurrent_sequences():
             s.destroy()
     assert (pool.block_state()[0] == 0).all() and pool.stats().num_free == 64
     pool.close()
+
+
+def test_native_batch_prepare_with_window_matches_oracle():
+    """pkv_batch_prepare with a sliding window: each sequence first gives back the blocks wholly
+    before num_computed + 1 - window, as the oracle's drop_before does, then gets its room; the
+    freed blocks are handed to the next allocations."""
+    B = _lib()
+    rng = random.Random(78)
+    npool, opool = B.BlockPool(40, 4), O.Pool(40, 4)
+    prompts = [[rng.randrange(100) for _ in range(n)] for n in (3, 17, 30)]
+    nseqs = [B.SeqCache(npool) for _ in prompts]
+    oseqs = [O.Seq(opool) for _ in prompts]
+    for n, o, p in zip(nseqs, oseqs, prompts):
+        n.allocate_for_tokens(p)
+        o.allocate_for_tokens(p)
+        n.commit(len(p) - 1)
+        o.commit(len(p) - 1)
+    batch = B.Batch(nseqs, 20, pad_block=39)
+    window = 10
+    for step in range(12):
+        tables, pos = batch.prepare(1, window=window)
+        for o in oseqs:
+            o.drop_before(max(0, o.num_computed + 1 - window))
+            o.reserve(1)
+        rows, opos = O.fill_tables(oseqs, 20, 39)
+        assert tables.tolist() == rows and pos.tolist() == opos
+        batch.commit(1)
+        for o in oseqs:
+            o.commit(1)
+        _compare(npool, opool, nseqs, oseqs)
+    # a sequence never holds more than ceil(window / 4) + 1 blocks
+    for o in oseqs:
+        assert sum(b >= 0 for b in o.blocks) <= -(-window // 4) + 1
+    for s in nseqs:
+        s.destroy()
+    npool.close()
 
 
 def test_native_batch_calls_match_per_sequence_oracle():

@@ -45,7 +45,7 @@ def _inputs(rng, n):
     return f(n, HQ, D), f(n, HKV, D), f(n, HKV, D)
 
 
-def _prefill(both, seqs, chunks, rng, what):
+def _prefill(both, seqs, chunks, rng, what, window=0):
     """Reserve and prefill chunks[b] new tokens of seqs[b] (from their computed count on)."""
     starts = np.array([s.reserve(c) for s, c in zip(seqs, chunks)], np.int32)
     tables, pos = fill_block_tables(seqs, MAXB, PAD)
@@ -54,11 +54,12 @@ def _prefill(both, seqs, chunks, rng, what):
     q, k, v = _inputs(rng, int(cu[-1]))
     q_ref = oracle.prefill_append(q, k, v, both.k, both.v, tables, cu, starts, None, None, 1e-6,
                                   THETA, DTYPE)
-    out_ref = oracle.paged_attn_prefill(q_ref, both.k, both.v, tables, cu, starts, SCALE, DTYPE)
+    out_ref = oracle.paged_attn_prefill(q_ref, both.k, both.v, tables, cu, starts, SCALE, DTYPE,
+                                        window=window)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q_out, out = pkv.prefill_step(t(q), t(k), t(v), both.kd, both.vd, t(tables), t(cu), t(starts),
                                   int(max(chunks)), int((starts + np.array(chunks)).max()),
-                                  theta=THETA, scale=SCALE, dtype=DTYPE)
+                                  theta=THETA, scale=SCALE, dtype=DTYPE, window=window)
     torch.cuda.synchronize()
     both.check_pools(what)
     assert_close(q_out.cpu().numpy(), q_ref, f"{what}: q_out")
@@ -68,18 +69,21 @@ def _prefill(both, seqs, chunks, rng, what):
     return q, k, v
 
 
-def _decode(both, seqs, rng, what, kv=None):
+def _decode(both, seqs, rng, what, kv=None, window=0):
     for s in seqs:
+        if window:
+            s.drop_before(max(0, s.state().num_computed + 1 - window))
         s.reserve(1)
     tables, pos = fill_block_tables(seqs, MAXB, PAD)
     q, k, v = _inputs(rng, len(seqs))
     if kv is not None:
         k, v = kv
     q_ref = oracle.kv_append(q, k, v, both.k, both.v, tables, pos, None, None, 1e-6, THETA, DTYPE)
-    out_ref = oracle.paged_attn_decode(q_ref, both.k, both.v, tables, pos + 1, SCALE, DTYPE)
+    out_ref = oracle.paged_attn_decode(q_ref, both.k, both.v, tables, pos + 1, SCALE, DTYPE,
+                                       window=window)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q_out, out = pkv.decode_step(t(q), t(k), t(v), both.kd, both.vd, t(tables), t(pos),
-                                 theta=THETA, scale=SCALE, dtype=DTYPE)
+                                 theta=THETA, scale=SCALE, dtype=DTYPE, window=window)
     torch.cuda.synchronize()
     both.check_pools(what)
     assert_close(q_out.cpu().numpy(), q_ref, f"{what}: q_out")
@@ -137,4 +141,45 @@ def test_shared_prefix_prefill_then_decode():
     for s in seqs + [e]:
         s.destroy()
     assert pool.stats().num_free == NB
+    pool.close()
+
+
+def test_sliding_window_blocks_reused_by_another_sequence():
+    """Sliding-window layer (window 24, blocks of 16) on a pool of six blocks: sequence A's
+    first block falls behind its window and goes back to the pool (drop_before), sequence B's
+    admission takes it and B's prefill overwrites it, and A keeps decoding over a table whose
+    given-back entries are the NaN padding block. Pools bit-identical to the oracle's at every
+    phase (so B's writes land where the manager put them), outputs within tolerance (so A never
+    reads a given-back entry: it would read NaN)."""
+    W = 24
+    rng = np.random.default_rng(316)
+    both = Both()
+    pool = BlockPool(6, BS)
+
+    log("sliding window: A prefills 40 tokens")
+    a = SeqCache(pool)
+    assert a.allocate_for_tokens(rng.integers(0, 32000, 40).tolist()) == 0
+    _prefill(both, [a], [40], rng, "window prefill A", window=W)
+    first_a = int(a.blocks()[0][0])
+
+    log("sliding window: A decodes; its first block goes back")
+    _decode(both, [a], rng, "window decode A", window=W)
+    assert a.state().num_dropped == 1 and a.blocks()[0][0] == -1
+    assert pool.block_state()[0][first_a] == 0
+
+    log("sliding window: B takes the given-back block and prefills over it")
+    b = SeqCache(pool)
+    assert b.allocate_for_tokens(rng.integers(0, 32000, 60).tolist()) == 0
+    assert b.blocks()[0].tolist()[-1] == first_a           # the last of the four free blocks
+    _prefill(both, [b], [60], rng, "window prefill B over A's old block", window=W)
+
+    log("sliding window: A and B decode together")
+    for step in range(16):
+        tables = _decode(both, [a, b], rng, f"window decode A+B {step}", window=W)
+        assert tables[0, 0] == PAD
+    # A attended 57 tokens last (keys 33..56: two blocks behind), B 76 (keys 52..75: three)
+    assert a.state().num_dropped == 2 and b.state().num_dropped == 3
+    for s in (a, b):
+        s.destroy()
+    assert pool.stats().num_free == 6
     pool.close()
