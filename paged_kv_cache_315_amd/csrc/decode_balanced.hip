@@ -34,8 +34,9 @@
 // its own loads of the row. No other workgroup reads that row, so one launch does the step.
 //
 // Layer variants (VAR): partial rotary, V normalisation and a sliding window are run-time fields
-// of the arguments; the kernel without VAR takes them as the plain layer's constants (rotary over
-// the whole head, no V norm, no window), which keeps the plain step free of their registers.
+// of the arguments. kVarNone takes them as the plain layer's constants (rotary over the whole
+// head, no V norm, no window), which keeps the plain step free of their registers; kVarWindow
+// reads only the window; kVarFull reads all three.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -49,6 +50,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
+constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;
 
 // Query rotation of one unit and, for the unit holding a segment's last tile, the new token's
 // K/V row (norm + RoPE in double over the first rope_dim dims, optional V norm in float,
@@ -57,7 +59,7 @@ constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 // by this thread block, not yet synchronised) and s_inv the angles per position of the rotary
 // pairs; ends with a barrier, after which this workgroup's own loads of the new row see the
 // stored codes.
-template <int D, int G, bool BF16, bool VAR>
+template <int D, int G, bool BF16, int VAR>
 __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, int g, int pnew,
                                                bool owns_new, bool seg_first, float* s_q,
                                                const float* s_kx, const float* s_vx,
@@ -66,13 +68,13 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, 
     const int tid = threadIdx.x;
     const int Hkv = a.Hkv;
     const int Hq = Hkv * G;
-    const int rope_dim = VAR ? a.rope_dim : D;
+    const int rope_dim = VAR == kVarFull ? a.rope_dim : D;
     const int rhalf = rope_dim >> 1;       // rotary pairs (i, i + rhalf), i < rhalf
     const int64_t tok_stride = (int64_t)Hkv * D;
     for (int i = tid; i < rhalf; i += kThreads)
         rope_cs_from(pnew, s_inv[i], s_cs[2 * i], s_cs[2 * i + 1]);
     const bool norm = a.q_norm_w != nullptr;
-    const bool vnorm = VAR && a.v_norm && owns_new;
+    const bool vnorm = VAR == kVarFull && a.v_norm && owns_new;
     if (norm) {
         if (tid < G) s_r[tid] = rms_inv(s_q + tid * D, D, a.eps);
         if (tid == G && owns_new) s_r[G] = rms_inv(s_kx, D, a.eps);
@@ -130,7 +132,7 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, 
                 const float y = norm ? norm_elem(s_kx[j], s_r[G], a.k_norm_w[j]) : s_kx[j];
                 a.k_pool[row + j] = encode16(y, BF16);
             }
-            if constexpr (VAR) {
+            if constexpr (VAR == kVarFull) {
                 const float vsc = vnorm ? *s_vsc : 1.f;
                 for (int i = tid; i < D; i += kThreads)
                     a.v_pool[row + i] = encode16(vnorm ? vnorm_elem(s_vx[i], vsc) : s_vx[i], BF16);
@@ -143,7 +145,7 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, 
     __syncthreads();
 }
 
-template <int D, int G, bool BF16, bool APPEND, bool VAR>
+template <int D, int G, bool BF16, bool APPEND, int VAR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void decode_balanced_kernel(BalancedArgs a) {
     using M = Mma<BF16>;
@@ -161,7 +163,7 @@ void decode_balanced_kernel(BalancedArgs a) {
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ __align__(16) float s_q[G][D];
     __shared__ float s_kx[APPEND ? D : 1];
-    __shared__ float s_vx[APPEND && VAR ? D : 1];
+    __shared__ float s_vx[APPEND && VAR == kVarFull ? D : 1];
     __shared__ float s_vsc;
     __shared__ double s_inv[APPEND ? HALF : 1];  // theta^(-2i/rope_dim) of rotary pair i
     __shared__ double s_cs[APPEND ? HALF : 1][2];
@@ -183,7 +185,7 @@ void decode_balanced_kernel(BalancedArgs a) {
     const int B = a.B;
     const int Hkv = a.Hkv;
     const int Hq = Hkv * G;
-    const int W = VAR ? a.window : 0;
+    const int W = VAR != kVarNone ? a.window : 0;
     // tiles of a sequence of L tokens: from the one holding its first visible key to the last
     auto ntiles = [W](int L) { return (L + kTile - 1) / kTile - window_lo(L, W) / kTile; };
 
@@ -207,7 +209,7 @@ void decode_balanced_kernel(BalancedArgs a) {
         }
     }
     if constexpr (APPEND) {  // while the lengths arrive
-        const int rope_dim = VAR ? a.rope_dim : D;
+        const int rope_dim = VAR == kVarFull ? a.rope_dim : D;
         for (int i = tid; i < (rope_dim >> 1); i += kThreads)
             s_inv[i] = rope_inv_freq(a.theta, i, rope_dim);
     }
@@ -301,7 +303,7 @@ void decode_balanced_kernel(BalancedArgs a) {
                     const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
                     for (int i = tid; i < D; i += kThreads) {
                         s_kx[i] = ksrc[i];
-                        if constexpr (VAR) s_vx[i] = vsrc[i];
+                        if constexpr (VAR == kVarFull) s_vx[i] = vsrc[i];
                     }
                 }
                 rotate_and_append<D, G, BF16, VAR>(a, b, g, pnew, owns_new, seg_first, &s_q[0][0],
@@ -567,9 +569,11 @@ void decode_balanced_kernel(BalancedArgs a) {
 
 template <int D, int G, bool BF16, bool APPEND>
 hipError_t launch_typed(const BalancedArgs& a, hipStream_t stream) {
-    const bool var = a.window != 0 || (APPEND && (a.rope_dim != D || a.v_norm));
-    auto kern = var ? decode_balanced_kernel<D, G, BF16, APPEND, true>
-                    : decode_balanced_kernel<D, G, BF16, APPEND, false>;
+    // the append's variant fields matter only when the append is fused
+    const bool full = APPEND && (a.rope_dim != D || a.v_norm);
+    auto kern = full            ? decode_balanced_kernel<D, G, BF16, APPEND, APPEND ? kVarFull : kVarWindow>
+                : a.window != 0 ? decode_balanced_kernel<D, G, BF16, APPEND, kVarWindow>
+                                : decode_balanced_kernel<D, G, BF16, APPEND, kVarNone>;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
         per_cu < 1)

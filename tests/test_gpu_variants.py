@@ -62,6 +62,7 @@ DECODE_VARIANTS = [
     ([0, 16, 17, 100, 700], 8, 1, 64, 4, "f16", 1e4, False, 0, False, 17),  # window off-tile
     ([0, 1, 50, 2000], 8, 2, 128, 16, "bf16", 1e4, False, 0, False, 1),    # own token only
     ([100, 1500, 4095], 32, 8, 128, 16, "bf16", 1e6, True, 64, True, 512),  # all three
+    ([0, 33, 900, 2500], 64, 8, 128, 16, "bf16", 1e6, True, 0, False, 300),  # window + QK norm
 ]
 
 
