@@ -61,7 +61,8 @@ constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;
 // stored codes.
 template <int D, int G, bool BF16, int VAR>
 __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, int g, int pnew,
-                                               bool owns_new, bool seg_first, float* s_q,
+                                               int64_t blk_new, bool owns_new, bool seg_first,
+                                               float* s_q,
                                                const float* s_kx, const float* s_vx,
                                                const double* s_inv, double* s_cs, double* s_r,
                                                float* s_vsc) {
@@ -111,9 +112,8 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, 
         }
     if (owns_new) {
         int64_t row = -1;
-        const int64_t blk = a.tables[(int64_t)b * a.max_blocks + pnew / a.bs];
-        if (blk >= 0 && blk < a.num_blocks)
-            row = (blk * a.bs + pnew % a.bs) * tok_stride + (int64_t)g * D;
+        if (blk_new >= 0 && blk_new < a.num_blocks)
+            row = (blk_new * a.bs + pnew % a.bs) * tok_stride + (int64_t)g * D;
         for (int i = tid; i < rhalf; i += kThreads) {
             float x0 = s_kx[i], x1 = s_kx[i + rhalf];
             if (norm) {
@@ -298,6 +298,9 @@ void decode_balanced_kernel(BalancedArgs a) {
             const float* qsrc = a.q + ((int64_t)b * Hq + g * G) * D;
             for (int i = tid; i < G * D; i += kThreads) s_q[i / D][i % D] = qsrc[i];
             if constexpr (APPEND) {
+                // the new row's block id, requested with the query (not after the barriers)
+                const int64_t blk_new =
+                    owns_new ? (int64_t)a.tables[(int64_t)b * a.max_blocks + pnew / a.bs] : -1;
                 if (owns_new) {
                     const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
                     const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
@@ -306,7 +309,7 @@ void decode_balanced_kernel(BalancedArgs a) {
                         if constexpr (VAR == kVarFull) s_vx[i] = vsrc[i];
                     }
                 }
-                rotate_and_append<D, G, BF16, VAR>(a, b, g, pnew, owns_new, seg_first, &s_q[0][0],
+                rotate_and_append<D, G, BF16, VAR>(a, b, g, pnew, blk_new, owns_new, seg_first, &s_q[0][0],
                                               s_kx, s_vx, s_inv, &s_cs[0][0], s_r, &s_vsc);
             } else {
                 __syncthreads();
