@@ -226,12 +226,14 @@ void pkvo_decode_array(const uint16_t* c, float* out, int64_t n, int dtype)
  * the projected Q and K before RoPE; [GL-FWD] forward_layer reshapes Q to [num_heads, head_dim]
  * and K to [kv_heads, head_dim] and normalises each row with the q_norm / k_norm weight, and its
  * per-head V norm shows the form x / sqrt(mean(x^2) + eps).
- * Pinned by: constant-vector closed form, mean(y^2) identity with unit weight, scale invariance,
- * an independent numpy formula (tests/test_oracle_norm_rope.py).
+ * Pinned by: constant-vector closed form, mean(y^2) identity with unit weight, an independent
+ * numpy formula (tests/oracle_pins.py, pin_norm_*), and inside the append by an independent
+ * numpy chain norm -> complex-form RoPE -> library cast with distinct q / k weights
+ * (pin_append_qk_norm_chain); the canonical NaN of norm / RoPE results by pin_append_nan_rows.
  * ------------------------------------------------------------------------------------------ */
 static float canonical_nan_if_nan(float v)
 {
-    if (isnan(v)) {
+    if (isnan(v) && !MUT(19)) {
         const uint32_t qnan = 0x7FC00000u;
         memcpy(&v, &qnan, 4);
     }
@@ -328,12 +330,14 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
     const int slot = pos % bs;
     if (blk < 0 || blk >= num_blocks)
         return PKVO_ERR_RANGE;
+    const float* qw = MUT(16) ? k_norm_w : q_norm_w;
+    const float* kw = MUT(16) ? q_norm_w : k_norm_w;
     /* Q: optional norm, then RoPE; the float result is the output (not stored in the pool). */
     for (int h = 0; h < Hq; ++h) {
         const float* x = q_in + (int64_t)h * D;
         const float* src = x;
-        if (q_norm_w) {
-            pkvo_rmsnorm_head(x, q_norm_w, eps, D, tmp);
+        if (qw) {
+            pkvo_rmsnorm_head(x, qw, eps, D, tmp);
             src = tmp;
         }
         pkvo_rope_head_partial(src, D, rope_dim, pos, theta, q_out + (int64_t)h * D);
@@ -342,11 +346,17 @@ static int append_token(const float* q_in, const float* k_in, const float* v_in,
     for (int g = 0; g < Hkv; ++g) {
         const float* x = k_in + (int64_t)g * D;
         const float* src = x;
-        if (k_norm_w) {
-            pkvo_rmsnorm_head(x, k_norm_w, eps, D, tmp);
-            src = tmp;
+        if (MUT(18) && kw) {
+            /* planted: rotated first, normed after */
+            pkvo_rope_head_partial(x, D, rope_dim, pos, theta, tmp);
+            pkvo_rmsnorm_head(tmp, kw, eps, D, rot);
+        } else {
+            if (kw && !MUT(17)) {
+                pkvo_rmsnorm_head(x, kw, eps, D, tmp);
+                src = tmp;
+            }
+            pkvo_rope_head_partial(src, D, rope_dim, pos, theta, rot);
         }
-        pkvo_rope_head_partial(src, D, rope_dim, pos, theta, rot);
         const float* v = v_in + (int64_t)g * D;
         if (v_norm) {
             pkvo_vnorm_head(v, D, eps, tmp);

@@ -76,6 +76,9 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, 
         rope_cs_from(pnew, s_inv[i], s_cs[2 * i], s_cs[2 * i + 1]);
     const bool norm = a.q_norm_w != nullptr;
     const bool vnorm = VAR == kVarFull && a.v_norm && owns_new;
+    // the norms read whole staged rows that other waves wrote: wait for every staging store
+    // (the condition is the same in every thread of the workgroup)
+    if (norm || vnorm) __syncthreads();
     if (norm) {
         if (tid < G) s_r[tid] = rms_inv(s_q + tid * D, D, a.eps);
         if (tid == G && owns_new) s_r[G] = rms_inv(s_kx, D, a.eps);

@@ -352,6 +352,116 @@ def pin_append_q_is_rotated_input(lib):
             assert _ulps(q_out[b, h], ref).max() <= 1
 
 
+def _np_norm(x, w, eps):
+    """Per-head RMS normalisation in float64 as the pages' form x / sqrt(mean(x^2) + eps) * w,
+    rounded once to float32 (an independent formulation: division, numpy mean)."""
+    xd = x.astype(np.float64)
+    r = np.sqrt(np.mean(xd * xd) + float(np.float32(eps)))
+    return (xd / r * w.astype(np.float64)).astype(np.float32)
+
+
+def _codes_near(codes, ref, dtype):
+    """True where the stored codes equal the library cast of `ref`, or of a float within two
+    float32 ulps of it (a chain that rounds to float32 twice may land on either side of a
+    16-bit rounding boundary only that close to it)."""
+    ref = np.asarray(ref, dtype=np.float32)
+    lo, hi = ref, ref
+    for _ in range(2):
+        lo = np.nextafter(lo, np.float32(-np.inf))
+        hi = np.nextafter(hi, np.float32(np.inf))
+    return (codes == _codes(ref, dtype)) | (codes == _codes(lo, dtype)) | (codes == _codes(hi, dtype))
+
+
+def pin_append_qk_norm_chain(lib):
+    """QK-norm inside the append: pages "makarna/pkg/model/arch/hybrid_decoder.go"
+    (runHybridAttentionBlock: QNorm / KNorm, then RoPE) and "soft3/glia/run/arch/decoder/
+    forward.rs" (forward_layer: every query head normed with the q weight, every KV head with
+    the k weight, before the rotation). Against an independent numpy chain: norm (float64,
+    division form) -> complex-form RoPE -> library cast, with distinct q and k weights and keys
+    far from unit scale, so a swapped weight, a skipped K norm or a rotation before the norm
+    all move the results by far more than the tolerance."""
+    rng = np.random.default_rng(13)
+    for dtype, theta, D in (("f16", 1e6, 64), ("bf16", 5e5, 128)):
+        wl = W.make_workload(108, [0, 5, 16, 300], 6, 2, D, 16, dtype, theta, spare_blocks=1)
+        w_q = rng.uniform(0.5, 1.5, D).astype(np.float32)
+        w_k = rng.uniform(0.5, 1.5, D).astype(np.float32)
+        eps = np.float32(1e-6)
+        k_in = (wl["k_new"] * 37.0).astype(np.float32)
+        kp = wl["k_pool"].copy()
+        vp = wl["v_pool"].copy()
+        q_out = oracle.kv_append(wl["q"], k_in, wl["v_new"], kp, vp, wl["tables"],
+                                 wl["positions"], w_q, w_k, eps, theta, dtype, lib=lib)
+        for b, p in enumerate(wl["positions"]):
+            p = int(p)
+            for h in range(wl["q"].shape[1]):
+                ref = _rope_complex(_np_norm(wl["q"][b, h], w_q, eps), p, theta)
+                assert _ulps(q_out[b, h], ref).max() <= 2, (dtype, b, h)
+            blk, slot = wl["tables"][b, p // 16], p % 16
+            for g in range(2):
+                ref_k = _rope_complex(_np_norm(k_in[b, g], w_k, eps), p, theta)
+                ok = _codes_near(kp[blk, slot, g], ref_k, dtype)
+                assert ok.all(), (dtype, b, g, np.flatnonzero(~ok))
+            assert np.array_equal(vp[blk, slot], _codes(wl["v_new"][b], dtype))
+
+
+def _page_nan_code(bits: int, dtype: str) -> int:
+    """16-bit code of a float32 NaN with the given bits: page "makarna/pkg/kvcache/
+    paged_cache.go" float32ToFloat16Bits keeps the sign and the 10 leading payload bits, forced
+    non-zero; bf16 (the reading for the page's rule without a NaN branch) the sign and the 7
+    leading payload bits, forced non-zero."""
+    sign = (bits >> 16) & 0x8000
+    if dtype == "f16":
+        return sign | 0x7C00 | max((bits >> 13) & 0x3FF, 1)
+    return sign | 0x7F80 | max((bits >> 16) & 0x7F, 1)
+
+
+def pin_append_nan_rows(lib):
+    """A NaN that the norm or the rotation produces is stored as the canonical quiet NaN
+    0x7FC00000 (-> 0x7E00 fp16, 0x7FC0 bf16), whatever the input NaN's sign and payload; a NaN
+    that reaches the converter untouched (V) keeps its sign and leading payload bits by the
+    page's rule. Under QK-norm one NaN element makes the whole head NaN (its mean square is
+    NaN); without norm only the element and its rotation partner are NaN."""
+    nan_in = np.array([0xFFC12345], dtype=np.uint32).view(np.float32)[0]   # negative, payload
+    nan_v = np.array([0x7FA00001], dtype=np.uint32).view(np.float32)[0]    # signalling, payload
+    canon = {"f16": 0x7E00, "bf16": 0x7FC0}
+    for dtype in ("f16", "bf16"):
+        D = 32
+        wl = W.make_workload(109, [7, 40], 4, 2, D, 8, dtype, 1e4, spare_blocks=1)
+        q = wl["q"].copy()
+        k = wl["k_new"].copy()
+        v = wl["v_new"].copy()
+        q[0, 1, 3] = nan_in
+        q[1, 2, 20] = nan_in
+        k[0, 1, 5] = nan_in
+        k[1, 0, 9] = nan_in
+        v[1, 1, 4] = nan_v
+        w = np.random.default_rng(14).uniform(0.5, 1.5, D).astype(np.float32)
+        for norm in (True, False):
+            kp = wl["k_pool"].copy()
+            vp = wl["v_pool"].copy()
+            q_out = oracle.kv_append(q, k, v, kp, vp, wl["tables"], wl["positions"],
+                                     w if norm else None, w if norm else None, 1e-6,
+                                     wl["theta"], dtype, lib=lib)
+            qbits = q_out.view(np.uint32)
+            rows = {b: (wl["tables"][b, int(p) // 8], int(p) % 8)
+                    for b, p in enumerate(wl["positions"])}
+            for (b, head, d), kind in (((0, 1, 3), "q"), ((1, 2, 20), "q"), ((0, 1, 5), "k"),
+                                       ((1, 0, 9), "k")):
+                hit = (np.arange(D) if norm else np.array([d % 16, d % 16 + 16]))
+                if kind == "q":
+                    assert np.all(qbits[b, head, hit] == 0x7FC00000), (dtype, norm, b, head)
+                    rest = np.setdiff1d(np.arange(D), hit)
+                    assert np.all(np.isfinite(q_out[b, head, rest]))
+                else:
+                    blk, slot = rows[b]
+                    row = kp[blk, slot, head]
+                    assert np.all(row[hit] == canon[dtype]), (dtype, norm, b, head, row[hit])
+                    rest = np.setdiff1d(np.arange(D), hit)
+                    assert np.all(np.isfinite(_decode_np(row[rest], dtype)))
+            blk, slot = rows[1]
+            assert int(vp[blk, slot, 1, 4]) == _page_nan_code(0x7FA00001, dtype), dtype
+
+
 # ------------------------------------------------------------------ chunked prefill
 def _prefill_small():
     yield W.prefill_config(1)

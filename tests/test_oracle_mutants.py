@@ -21,6 +21,10 @@ MUTANTS = {
     13: "V norm: eps dropped",
     14: "sliding window: one token too many",
     15: "RoPE at read: key positions off by one",
+    16: "QK-norm: q and k weights swapped",
+    17: "QK-norm: K norm skipped",
+    18: "QK-norm: K rotated before it is normed",
+    19: "norm / RoPE: an arithmetic NaN stored with its own sign and payload",
 }
 
 
