@@ -242,6 +242,39 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
                            int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
                            const pkv_variant* variant, void* stream);
 
+/*
+ * pkv_decode_step_noalloc — pkv_decode_step without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It allocates and frees nothing, and calls no allocating routine.
+ *
+ * The merge counters and partial pieces live in a 16 MiB array the library holds on each GPU
+ * it runs on, from the first call on that GPU until the process ends
+ * (pkv_decode_step_noalloc_scratch_bytes()). The first call on a GPU looks up the array's
+ * device address (hipGetSymbolAddress) with that GPU current; every call clears the counters
+ * with a small fill kernel on `stream` before the step's kernel. Every call on one GPU uses the
+ * same array, so calls that overlap in time on one GPU (different streams or threads) race and
+ * give wrong results; calls in one stream are ordered and safe.
+ *
+ * Arguments and results: as pkv_decode_step, without workspace / workspace_bytes.
+ * Limits: batches of at most 2048 sequences (UNSUPPORTED otherwise: pkv_decode_step's
+ * workspace path serves them); the counters (B * num_kv_heads ints) plus the pieces of at least
+ * one workgroup per compute unit (2 * G * (head_dim + 2) floats each) must fit in the array
+ * (WORKSPACE otherwise, e.g. B = 2048 with num_kv_heads above ~2000). Other errors as
+ * pkv_decode_step; PKV_ERR_HIP if the array's address cannot be found.
+ */
+pkv_status pkv_decode_step_noalloc(const float* q_in, const float* k_in, const float* v_in,
+                                   float* q_out, void* k_pool, void* v_pool,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* positions, const float* q_norm_w,
+                                   const float* k_norm_w, float rms_eps, float rope_theta,
+                                   float scale, float* out, int B, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int64_t num_blocks, pkv_dtype dtype,
+                                   const pkv_variant* variant, void* stream);
+
+/* Bytes of the per-GPU array pkv_decode_step_noalloc works in (16 MiB). Host only. */
+size_t pkv_decode_step_noalloc_scratch_bytes(void);
+
 /* Workspace bytes pkv_decode_step needs. Host only. */
 size_t pkv_decode_step_workspace_bytes(int B, int num_q_heads, int num_kv_heads, int head_dim,
                                        int block_size, int max_blocks_per_seq);

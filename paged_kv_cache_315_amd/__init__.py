@@ -19,7 +19,8 @@ from ._lib import PKV_BF16, PKV_F16, PKV_F32, PkvError
 __all__ = ["PKV_F16", "PKV_BF16", "PKV_F32", "kv_append", "paged_attn_decode", "decode_step",
            "decode_workspace_bytes",
            "prefill_append", "paged_attn_prefill", "prefill_workspace_bytes", "prefill_step",
-           "decode_step_workspace_bytes", "append_then_decode", "decode_split_tokens", "validate_tables", "version",
+           "decode_step_workspace_bytes", "decode_step_noalloc", "decode_step_noalloc_scratch_bytes",
+           "append_then_decode", "decode_split_tokens", "validate_tables", "version",
            "PkvError", "pool_dtype_code"]
 
 
@@ -203,6 +204,37 @@ def decode_step(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *, th
         _lib.variant(rope_dim, v_norm, window), _stream(stream))
     _lib.check(_lib.load().pkv_decode_step(*args), "pkv_decode_step")
     return q_out, out
+
+
+def decode_step_noalloc(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, *,
+                        theta: float, scale: float, q_out, out, q_norm_w=None, k_norm_w=None,
+                        eps: float = 1e-6, dtype=None, rope_dim: int = 0, v_norm: bool = False,
+                        window: int = 0, stream=None):
+    """decode_step without a workspace: the library's own per-GPU scratch array holds the
+    merge counters and partial pieces, and nothing is allocated (q_out and out are the
+    caller's). Calls that overlap in time on one GPU race. Returns (q_out, out)."""
+    torch = _torch()
+    B, Hq, D = q_in.shape
+    Hkv = k_in.shape[1]
+    NB, bs = k_pool.shape[0], k_pool.shape[1]
+    f32 = torch.float32
+    args = (
+        _dev_ptr(q_in, "q_in", dtype=f32, ndim=3), _dev_ptr(k_in, "k_in", dtype=f32, ndim=3),
+        _dev_ptr(v_in, "v_in", dtype=f32, ndim=3), _dev_ptr(q_out, "q_out", dtype=f32, ndim=3),
+        _dev_ptr(k_pool, "k_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(v_pool, "v_pool", ndim=4, elem_size=_pool_elem(k_pool, dtype)),
+        _dev_ptr(block_tables, "block_tables", dtype=torch.int32, ndim=2), block_tables.shape[1],
+        _dev_ptr(positions, "positions", dtype=torch.int32, ndim=1),
+        _dev_ptr(q_norm_w, "q_norm_w", dtype=f32), _dev_ptr(k_norm_w, "k_norm_w", dtype=f32),
+        float(eps), float(theta), float(scale), _dev_ptr(out, "out", dtype=f32, ndim=3),
+        B, Hq, Hkv, D, bs, NB, pool_dtype_code(k_pool, dtype),
+        _lib.variant(rope_dim, v_norm, window), _stream(stream))
+    _lib.check(_lib.load().pkv_decode_step_noalloc(*args), "pkv_decode_step_noalloc")
+    return q_out, out
+
+
+def decode_step_noalloc_scratch_bytes() -> int:
+    return _lib.load().pkv_decode_step_noalloc_scratch_bytes()
 
 
 def append_then_decode(q_in, k_in, v_in, k_pool, v_pool, block_tables, positions, context_lens,

@@ -44,6 +44,9 @@ SIGNATURES = {
                                    _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
     "pkv_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _F, _F, _F, _P, _P, _SZ,
                              _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
+    "pkv_decode_step_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _F, _F, _F,
+                                     _P, _I, _I, _I, _I, _I, _I64, _I, _V, _P]),
+    "pkv_decode_step_noalloc_scratch_bytes": (_SZ, []),
     "pkv_decode_step_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "pkv_decode_split_tokens": (_I, [_I, _I, _I, _I, _I, _I]),
     "pkv_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),

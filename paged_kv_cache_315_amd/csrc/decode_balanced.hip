@@ -584,7 +584,9 @@ hipError_t launch_typed(const BalancedArgs& a, hipStream_t stream) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
-    const int grid = (int)std::min<int64_t>((int64_t)per_cu * a.num_cus, kMaxBalancedGrid);
+    int64_t cap = kMaxBalancedGrid;
+    if (a.max_grid > 0) cap = std::min<int64_t>(cap, a.max_grid);
+    const int grid = (int)std::min<int64_t>((int64_t)per_cu * a.num_cus, cap);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -501,46 +501,134 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                       static_cast<hipStream_t>(stream));
 }
 
-pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_in, float* q_out,
-                           void* k_pool, void* v_pool, const int32_t* block_tables,
-                           int max_blocks_per_seq, const int32_t* positions,
-                           const float* q_norm_w, const float* k_norm_w, float rms_eps,
-                           float rope_theta, float scale, float* out, void* workspace,
-                           size_t workspace_bytes, int B, int num_q_heads, int num_kv_heads,
-                           int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
-                           const pkv_variant* variant, void* stream) {
-    pkv_status st = check_common("decode_step", B, num_q_heads, num_kv_heads, head_dim,
+}  // extern "C"
+
+// ---- scratch of the decode step that allocates nothing (pkv_decode_step_noalloc) ------------
+// Device memory of this library, one copy per GPU, held until the process ends: the merge
+// counters (B * Hkv ints) and the partial pieces of the balanced schedule (two per workgroup).
+// In host code `scratch` names a host-side stand-in, not a device address; kernels get the
+// address hipGetSymbolAddress returns for the current device (scratch_device_ptr).
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+__global__ void zero_ints_kernel(int* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+pkv_status scratch_device_ptr(char** out) {
+    static std::mutex mu;
+    static std::vector<void*> cache;
+    int dev = -1;
+    const hipError_t ge = hipGetDevice(&dev);
+    if (ge != hipSuccess || dev < 0)
+        return fail(PKV_ERR_HIP, "decode_step_noalloc: hipGetDevice failed: %s",
+                    hipGetErrorString(ge));
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, nullptr);
+    if (cache[dev] == nullptr) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(PKV_ERR_HIP, "decode_step_noalloc: hipGetSymbolAddress failed: %s",
+                        hipGetErrorString(e));
+        cache[dev] = ptr;
+    }
+    *out = static_cast<char*>(cache[dev]);
+    return PKV_OK;
+}
+
+// The decode step with the caller's workspace (noalloc false) or with the library's scratch
+// array (noalloc true: balanced schedule only, counters cleared by a fill kernel first, pieces
+// for as many workgroups as the array holds).
+pkv_status decode_step_impl(const float* q_in, const float* k_in, const float* v_in,
+                            float* q_out, void* k_pool, void* v_pool,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* positions, const float* q_norm_w,
+                            const float* k_norm_w, float rms_eps, float rope_theta, float scale,
+                            float* out, void* workspace, size_t workspace_bytes, int B,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int64_t num_blocks, pkv_dtype dtype, const pkv_variant* variant,
+                            void* stream, bool noalloc) {
+    const char* who = noalloc ? "decode_step_noalloc" : "decode_step";
+    pkv_status st = check_common(who, B, num_q_heads, num_kv_heads, head_dim,
                                  block_size, num_blocks, max_blocks_per_seq, dtype);
     if (st != PKV_OK) return st;
-    st = check_rope("decode_step", rope_theta, q_norm_w, k_norm_w, head_dim);
+    st = check_rope(who, rope_theta, q_norm_w, k_norm_w, head_dim);
     if (st != PKV_OK) return st;
     Variant var;
-    st = resolve_variant("decode_step", variant, head_dim, var);
+    st = resolve_variant(who, variant, head_dim, var);
     if (st != PKV_OK) return st;
     if (var.rope_read || dtype == PKV_F32)
         return fail(PKV_ERR_UNSUPPORTED,
-                    "decode_step: rope_on_read and float32 pools are served by pkv_kv_append + "
-                    "pkv_paged_attn_decode");
-    st = check_decode_shape("decode_step", B, num_q_heads, num_kv_heads, head_dim);
+                    "%s: rope_on_read and float32 pools are served by pkv_kv_append + "
+                    "pkv_paged_attn_decode", who);
+    st = check_decode_shape(who, B, num_q_heads, num_kv_heads, head_dim);
     if (st != PKV_OK) return st;
     if (B == 0) return PKV_OK;
     if (!q_in || !k_in || !v_in || !q_out || !k_pool || !v_pool || !block_tables || !positions ||
         !out)
-        return fail(PKV_ERR_INVALID_ARG, "decode_step: NULL pointer argument");
+        return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer argument", who);
     if (q_out == q_in)
         return fail(PKV_ERR_INVALID_ARG,
-                    "decode_step: q_out must not alias q_in (workgroups of one sequence read "
-                    "q_in while another writes q_out)");
+                    "%s: q_out must not alias q_in (workgroups of one sequence read "
+                    "q_in while another writes q_out)", who);
     const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
     const int max_ctx = (int)std::min<int64_t>(cap, 0x7FFFFFFF);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bal = balanced_ok(B, num_kv_heads, max_ctx);
     const int P = bal ? 0 : choose_split(B, num_kv_heads, max_ctx, block_size, device_cus());
-    const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim, max_ctx, P,
-                                          block_size, bal);
-    if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
-        return fail(PKV_ERR_WORKSPACE, "decode_step: workspace %zu bytes, need %zu",
-                    workspace_bytes, wl.total);
+    WorkspaceLayout wl;
+    int max_grid = 0;
+    if (noalloc) {
+        if (!bal)
+            return fail(PKV_ERR_UNSUPPORTED,
+                        "decode_step_noalloc: %d sequences (max_blocks_per_seq %d): only batches "
+                        "of at most %d sequences run without a workspace; use pkv_decode_step",
+                        B, max_blocks_per_seq, pkv::kMaxBalancedBatch);
+        // counters, then the pieces of as many workgroups as the array holds (at most the
+        // balanced schedule's cap; at least one per compute unit)
+        const int G = num_q_heads / num_kv_heads;
+        const size_t cnt = align256((size_t)B * num_kv_heads * sizeof(int));
+        const size_t per_wg = (size_t)2 * G * head_dim * sizeof(float) + (size_t)2 * G * 2 * sizeof(float);
+        const size_t room = cnt + 512 < kScratchBytes ? kScratchBytes - cnt - 512 : 0;
+        max_grid = (int)std::min<size_t>(room / per_wg, (size_t)pkv::kMaxBalancedGrid);
+        const int cus = device_cus();
+        if (max_grid < cus)
+            return fail(PKV_ERR_WORKSPACE,
+                        "decode_step_noalloc: B=%d, Hkv=%d, G=%d, head_dim=%d needs more than the "
+                        "library's %zu-byte scratch (counters %zu bytes, pieces for %d workgroups); "
+                        "use pkv_decode_step with a workspace",
+                        B, num_kv_heads, G, head_dim, kScratchBytes, cnt, cus);
+        wl.balanced = true;
+        wl.S = 1;
+        wl.cnt_off = 0;
+        wl.acc_off = cnt;
+        wl.ml_off = wl.acc_off + align256((size_t)max_grid * 2 * G * head_dim * sizeof(float));
+        wl.total = wl.ml_off + align256((size_t)max_grid * 2 * G * 2 * sizeof(float));
+        char* base = nullptr;
+        st = scratch_device_ptr(&base);
+        if (st != PKV_OK) return st;
+        workspace = base;
+        workspace_bytes = kScratchBytes;
+        // the counters must start at zero: a fill kernel (not a memset) on the call's stream
+        const int n_cnt = B * num_kv_heads;
+        hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)((n_cnt + 255) / 256)), dim3(256), 0,
+                           s, reinterpret_cast<int*>(base + wl.cnt_off), n_cnt);
+        const hipError_t ze = hipGetLastError();
+        if (ze != hipSuccess)
+            return fail(PKV_ERR_HIP, "decode_step_noalloc: launch failed: %s",
+                        hipGetErrorString(ze));
+    } else {
+        wl = layout_for(B, num_q_heads, num_kv_heads, head_dim, max_ctx, P, block_size, bal);
+        if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
+            return fail(PKV_ERR_WORKSPACE, "decode_step: workspace %zu bytes, need %zu",
+                        workspace_bytes, wl.total);
+    }
     if (!bal) {
         // batches too large for the balanced schedule: the append kernel, then the partitioned
         // decode reading positions + 1 as the attended lengths
@@ -581,6 +669,7 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
     a.bs = block_size;
     a.num_blocks = num_blocks;
     a.num_cus = device_cus();
+    a.max_grid = max_grid;
     a.rope_dim = var.rope_dim;
     a.v_norm = var.v_norm;
     a.window = var.window;
@@ -588,9 +677,45 @@ pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_
     a.append = true;
     const hipError_t e = pkv::launch_decode_balanced(a, s);
     if (e != hipSuccess)
-        return fail(PKV_ERR_HIP, "decode_step: launch failed: %s", hipGetErrorString(e));
+        return fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
     return PKV_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_decode_step(const float* q_in, const float* k_in, const float* v_in, float* q_out,
+                           void* k_pool, void* v_pool, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* positions,
+                           const float* q_norm_w, const float* k_norm_w, float rms_eps,
+                           float rope_theta, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, int B, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks, pkv_dtype dtype,
+                           const pkv_variant* variant, void* stream) {
+    return decode_step_impl(q_in, k_in, v_in, q_out, k_pool, v_pool, block_tables,
+                            max_blocks_per_seq, positions, q_norm_w, k_norm_w, rms_eps,
+                            rope_theta, scale, out, workspace, workspace_bytes, B, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, dtype, variant, stream,
+                            false);
+}
+
+pkv_status pkv_decode_step_noalloc(const float* q_in, const float* k_in, const float* v_in,
+                                   float* q_out, void* k_pool, void* v_pool,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* positions, const float* q_norm_w,
+                                   const float* k_norm_w, float rms_eps, float rope_theta,
+                                   float scale, float* out, int B, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int64_t num_blocks, pkv_dtype dtype,
+                                   const pkv_variant* variant, void* stream) {
+    return decode_step_impl(q_in, k_in, v_in, q_out, k_pool, v_pool, block_tables,
+                            max_blocks_per_seq, positions, q_norm_w, k_norm_w, rms_eps,
+                            rope_theta, scale, out, nullptr, 0, B, num_q_heads, num_kv_heads,
+                            head_dim, block_size, num_blocks, dtype, variant, stream, true);
+}
+
+size_t pkv_decode_step_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 pkv_status pkv_prefill_append(const float* q_in, const float* k_in, const float* v_in,
                               float* q_out, void* k_pool, void* v_pool,

@@ -122,6 +122,7 @@ struct BalancedArgs {
     int B, Hq, Hkv, D, bs;
     int64_t num_blocks;
     int num_cus;
+    int max_grid;           // cap on the workgroups (piece slots: 2 per workgroup); 0: none
     int rope_dim;           // append only: rotated dims (even, <= D)
     int window;             // sliding window (0: every token)
     bool v_norm;            // append only: V rows normalised per KV head
