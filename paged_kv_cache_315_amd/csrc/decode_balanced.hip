@@ -14,10 +14,12 @@
 // [w*T, (w+1)*T), T = ceil(total / grid): every workgroup streams the same number of bytes
 // whatever the mix of lengths, and all of them are resident from start to end. Inside a
 // workgroup the 4 waves interleave the 16-token tiles of each unit (the part of one segment
-// that falls in the range) exactly as the partitioned kernel does: QK^T on the matrix cores,
-// online softmax, P through LDS, PV on the vector ALU, the next tile's K/V loads in flight. A
-// unit requests its query heads (and, fused, the new K row) together with its first chunk of
-// block ids, and the angles per position of the rotary pairs are computed once per workgroup.
+// that falls in the range); a tile is computed as decode_tile.h describes (QK^T and PV on the
+// matrix cores, online softmax in registers, an exact float path for tiles holding non-finite
+// codes), with the next tile's K/V loads in flight. When the block size is a multiple of 16 a
+// tile lies in one block: one block id per tile, read from LDS by the whole wave. A unit
+// requests its query heads (and, fused, the new K row) together with its first chunk of block
+// ids, and the angles per position of the rotary pairs are computed once per workgroup.
 //
 // Pieces. A segment that lies inside one range is finished there (out = acc / l). A segment cut
 // by range boundaries leaves one piece (m, l, acc) per workgroup it touches; a workgroup holds at
@@ -37,6 +39,7 @@
 // of the arguments. kVarNone takes them as the plain layer's constants (rotary over the whole
 // head, no V norm, no window), which keeps the plain step free of their registers; kVarWindow
 // reads only the window; kVarFull reads all three.
+#include "decode_tile.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -50,6 +53,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
+constexpr int kGMax = 8;          // query heads per KV head
+constexpr int kDefCap = 8;        // exact-path tiles a wave lists before it runs them
 constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;
 
 // Query rotation of one unit and, for the unit holding a segment's last tile, the new token's
@@ -59,8 +64,8 @@ constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;
 // by this thread block, not yet synchronised) and s_inv the angles per position of the rotary
 // pairs; ends with a barrier, after which this workgroup's own loads of the new row see the
 // stored codes.
-template <int D, int G, bool BF16, int VAR>
-__device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, int g, int pnew,
+template <int D, bool BF16, int VAR>
+__device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int G, int b, int g, int pnew,
                                                int64_t blk_new, bool owns_new, bool seg_first,
                                                float* s_q,
                                                const float* s_kx, const float* s_vx,
@@ -148,49 +153,46 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int b, 
     __syncthreads();
 }
 
-template <int D, int G, bool BF16, bool APPEND, int VAR>
+template <int D, bool BF16, bool APPEND, int VAR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void decode_balanced_kernel(BalancedArgs a) {
-    using M = Mma<BF16>;
-    constexpr int NK = D / 32;          // MFMA k-steps (and K loads) per tile
-    constexpr int R = D / 8;            // lanes per V row (8 codes per lane)
-    constexpr int TPL = 64 / R;         // V rows per load instruction
-    constexpr int U = kTile / TPL;      // V loads per tile
+    using Tile = DecodeTile<D, BF16>;
     constexpr int HALF = D / 2;
-    static_assert(D % 32 == 0 && U * TPL == kTile, "tile shape");
-    static_assert(G >= 1 && G <= 8, "GQA group");
 
     __shared__ int s_len[kMaxBalancedBatch];
     __shared__ int s_pre[kMaxBalancedBatch + 1];
     __shared__ int s_scan[kThreads];
     __shared__ int32_t s_tbl[kTblCap];
-    __shared__ __align__(16) float s_q[G][D];
+    __shared__ __align__(16) float s_q[kGMax][D];
     __shared__ float s_kx[APPEND ? D : 1];
     __shared__ float s_vx[APPEND && VAR == kVarFull ? D : 1];
     __shared__ float s_vsc;
     __shared__ double s_inv[APPEND ? HALF : 1];  // theta^(-2i/rope_dim) of rotary pair i
     __shared__ double s_cs[APPEND ? HALF : 1][2];
-    __shared__ double s_r[G + 1];
-    __shared__ __align__(16) float s_p[kWaves][kTile][16];
-    __shared__ __align__(16) float s_alpha[kWaves][16];
-    __shared__ float s_acc[kWaves][G][D];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
+    __shared__ double s_r[kGMax + 1];
+    // per wave: the exact path's tile while streaming, the wave's partial result after it
+    union WaveLds {
+        typename Tile::Scratch scr;
+        float acc[kGMax][D];
+    };
+    __shared__ __align__(16) WaveLds s_w[kWaves];
+    __shared__ float s_m[kWaves][kGMax];
+    __shared__ float s_l[kWaves][kGMax];
+    __shared__ int s_def[kWaves][kDefCap];   // tiles a wave left for the exact path
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int l16 = lane & 15;          // token of the score layout / row of the Q operand
-    const int q4 = lane >> 4;           // lane group: k-slice of the operands, head quad of S
-    const int vrow = lane / R;          // V layout: token row within a load
-    const int vcol = lane % R;          //           8-dim column
+    const int l16 = lane & 15;
+    const int q4 = lane >> 4;
     const int B = a.B;
     const int Hkv = a.Hkv;
-    const int Hq = Hkv * G;
+    const int G = a.Hq / a.Hkv;
+    const int Hq = a.Hq;
     const int W = VAR != kVarNone ? a.window : 0;
     // tiles of a sequence of L tokens: from the one holding its first visible key to the last
-    auto ntiles = [W](int L) { return (L + kTile - 1) / kTile - window_lo(L, W) / kTile; };
+    auto ntiles = [=](int L) { return (L + kTile - 1) / kTile - window_lo(L, W) / kTile; };
 
     // ---- 1. lengths and the tile prefix of every sequence (all heads) -> LDS
     const int64_t cap64 = (int64_t)a.max_blocks * a.bs;
@@ -257,9 +259,12 @@ void decode_balanced_kernel(BalancedArgs a) {
     int g = (r0 - s_pre[b]) / ntiles(s_len[b]);
 
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
+    const bool tile_in_block = a.bs % kTile == 0;   // a 16-token tile never crosses a block
     const int64_t nb_max = a.num_blocks - 1;
     const int64_t tok_stride = (int64_t)Hkv * D;   // codes between consecutive slots
     const int chunk_tokens = ((kTblCap - 2) * a.bs) / 64 * 64;
+    const uint32_t koff = Tile::k_lane_off(tok_stride);
+    const float qs = a.scale * kLog2e;
     float* part_acc = a.part_acc;
     float* part_ml = a.part_ml;
 
@@ -280,10 +285,6 @@ void decode_balanced_kernel(BalancedArgs a) {
         const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
         const int64_t head_off = (int64_t)g * D;
 
-        float m[4], lsum[4], acc[G][8];
-        typename M::vec qhi[NK], qlo[NK];
-        float score_fix = 1.f;
-
         // chunk of the block table staged in LDS (kTblCap ids cover chunk_tokens tokens)
         auto stage_table = [&](int c_lo, int c_hi) {
             const int first_blk = (int)bdiv.div((uint32_t)c_lo);
@@ -296,7 +297,14 @@ void decode_balanced_kernel(BalancedArgs a) {
 
         // Q of this segment (rotated here when the append is fused) and the first table chunk,
         // requested together; then the MFMA operands.
-        auto setup_q = [&]() {
+        auto qf = [&](int h, int d0, float (&o)[8]) {
+            const float4* src = reinterpret_cast<const float4*>(&s_q[h][d0]);
+            const float4 x0 = src[0], x1 = src[1];
+            o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+            o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+        };
+        typename Tile::Query qop;
+        {
             stage_table(tok_lo, min(tok_hi, tok_lo + chunk_tokens));
             const float* qsrc = a.q + ((int64_t)b * Hq + g * G) * D;
             for (int i = tid; i < G * D; i += kThreads) s_q[i / D][i % D] = qsrc[i];
@@ -312,54 +320,17 @@ void decode_balanced_kernel(BalancedArgs a) {
                         if constexpr (VAR == kVarFull) s_vx[i] = vsrc[i];
                     }
                 }
-                rotate_and_append<D, G, BF16, VAR>(a, b, g, pnew, blk_new, owns_new, seg_first, &s_q[0][0],
-                                              s_kx, s_vx, s_inv, &s_cs[0][0], s_r, &s_vsc);
+                rotate_and_append<D, BF16, VAR>(a, G, b, g, pnew, blk_new, owns_new, seg_first,
+                                                &s_q[0][0], s_kx, s_vx, s_inv, &s_cs[0][0], s_r,
+                                                &s_vsc);
             } else {
                 __syncthreads();
             }
-            const float qs = a.scale * kLog2e;
-            float qv[NK][8];
-            float qmax = 0.f;
-#pragma unroll
-            for (int i = 0; i < NK; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    qv[i][j] = l16 < G ? s_q[l16][32 * i + 8 * q4 + j] * qs : 0.f;
-                    qmax = fmaxf(qmax, fabsf(qv[i][j]));
-                }
-            float qscale = 1.f;
-            score_fix = 1.f;
-            if constexpr (!BF16) {
-                // fp16 operand: bring max |q| below 2^14 with an exact power-of-two scale
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
-                if (qmax >= 16384.f && qmax <= 3.0e38f) {
-                    const int e = ilogbf(qmax) - 13;
-                    qscale = ldexpf(1.f, -e);
-                    score_fix = ldexpf(1.f, e);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NK; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float xq = qv[i][j] * qscale;
-                    const typename M::elem hi = (typename M::elem)xq;
-                    qhi[i][j] = hi;
-                    qlo[i][j] = (typename M::elem)(xq - (float)hi);
-                }
-        };
-
-        setup_q();
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            m[r] = -INFINITY;
-            lsum[r] = 0.f;
         }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+        Tile::setup_query(qf, G, qs, qop);
+        typename Tile::State st;
+        Tile::init(st);
+
         for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
             const int c_hi = min(tok_hi, c_lo + chunk_tokens);
             const int first_blk = (int)bdiv.div((uint32_t)c_lo);
@@ -368,123 +339,77 @@ void decode_balanced_kernel(BalancedArgs a) {
                 stage_table(c_lo, c_hi);
                 __syncthreads();
             }
+            const int last_base = c_lo + (c_hi - 1 - c_lo) / kTile * kTile;
 
             auto row_off = [&](int t) -> int64_t {
                 const int j = (int)bdiv.div((uint32_t)t);
                 const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
                 return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
             };
-            // loads are unconditional (tokens past the chunk clamp to its last row, masked at
-            // use) so that no load sits behind a branch and the prefetch is never drained
-            auto load_tile = [&](int base, uint4 (&kr)[NK], uint4 (&vr)[U]) {
-                const uint16_t* kp = a.k_pool + row_off(min(base + l16, c_hi - 1)) + 8 * q4;
+            // tiles past the chunk (prefetch beyond the end) read its last tile again; the
+            // loads themselves are unconditional so that none sits behind a branch (which made
+            // the compiler drain the prefetch)
+            auto load_tile = [&](int base, typename Tile::Regs& r) {
+                const int bb = min(base, last_base);
+                const uint16_t* kp;
+                const uint16_t* vp[4];
+                if (tile_in_block) {
+                    const int j = (int)bdiv.div((uint32_t)bb);
+                    const int blk = __builtin_amdgcn_readfirstlane(
+                        s_tbl[min(j - first_blk, kTblCap - 1)]);
+                    const int64_t row0 = ((int64_t)blk * a.bs + (bb - j * a.bs)) * tok_stride + head_off;
+                    kp = a.k_pool + row0 + koff;
 #pragma unroll
-                for (int i = 0; i < NK; ++i) kr[i] = load_stream(kp + 32 * i);
+                    for (int jj = 0; jj < 4; ++jj) vp[jj] = a.v_pool + row0 + (4 * q4 + jj) * tok_stride;
+                } else {
+                    kp = a.k_pool + row_off(min(bb + l16, c_hi - 1)) + 8 * q4;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int tv = min(base + u * TPL + vrow, c_hi - 1);
-                    vr[u] = load_stream(a.v_pool + row_off(tv) + 8 * vcol);
+                    for (int jj = 0; jj < 4; ++jj)
+                        vp[jj] = a.v_pool + row_off(min(bb + 4 * q4 + jj, c_hi - 1));
                 }
-            };
-            auto compute_tile = [&](int base, const uint4 (&kc)[NK], const uint4 (&vc)[U]) {
-                f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < NK; ++i) {
-                    const typename M::vec kv = __builtin_bit_cast(typename M::vec, kc[i]);
-                    sacc = M::mma(qhi[i], kv, sacc);
-                    sacc = M::mma(qlo[i], kv, sacc);
-                }
-                const bool tok_ok = base + l16 < c_hi && base + l16 >= vis_lo;
-                float p[4], alpha[4];
-                bool grew = false;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool ok = tok_ok && (4 * q4 + r) < G;
-                    const float sc = ok ? sacc[r] * score_fix : -INFINITY;
-                    const float tmax = row16_max(sc);
-                    const float m_new = fmaxf(m[r], tmax);
-                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                    alpha[r] = exp2f(m[r] - m_use);
-                    p[r] = exp2f(sc - m_use);
-                    lsum[r] = fmaf(lsum[r], alpha[r], p[r]);
-                    grew |= m_new != m[r];
-                    m[r] = m_new;
-                }
-                *reinterpret_cast<float4*>(&s_p[wave][l16][4 * q4]) =
-                    make_float4(p[0], p[1], p[2], p[3]);
-                const bool rescale = __any(grew);
-                if (rescale && l16 == 0)
-                    *reinterpret_cast<float4*>(&s_alpha[wave][4 * q4]) =
-                        make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
-                wave_lds_sync();
-                if (rescale) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float al = s_alpha[wave][h];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[h][j] *= al;
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int tt = u * TPL + vrow;
-                    float pv[G];
-#pragma unroll
-                    for (int h = 0; h < G; ++h) pv[h] = s_p[wave][tt][h];
-                    const uint4 raw =
-                        base + tt < c_hi && base + tt >= vis_lo ? vc[u] : make_uint4(0, 0, 0, 0);
-                    float vf[8];
-                    decode8<BF16>(raw, vf);
-#pragma unroll
-                    for (int h = 0; h < G; ++h)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pv[h], vf[j], acc[h][j]);
-                }
-                wave_lds_sync();
+                Tile::load_rows(kp, vp, r);
             };
 
             // two register buffers: the next tile's K/V rows load while this one is computed
-            // (the loop is unrolled by two so each buffer keeps its registers)
+            // (the loop is unrolled by two so each buffer keeps its registers); tiles that need
+            // the exact path are listed and done after the loop, reloaded
             constexpr int kStride = kWaves * kTile;
             int base = c_lo + wave * kTile;
-            uint4 ka[NK], va[U], kb[NK], vb[U];
-            load_tile(base, ka, va);
             while (base < c_hi) {
-                load_tile(base + kStride, kb, vb);
-                compute_tile(base, ka, va);
-                base += kStride;
-                if (base >= c_hi) break;
-                load_tile(base + kStride, ka, va);
-                compute_tile(base, kb, vb);
-                base += kStride;
+                int ndef = 0;
+                {
+                    typename Tile::Regs ra, rb;
+                    load_tile(base, ra);
+                    while (true) {
+                        load_tile(base + kStride, rb);
+                        if (Tile::compute(ra, base, vis_lo, c_hi, qop, st)) {
+                            if (lane == 0) s_def[wave][ndef] = base;
+                            ++ndef;
+                        }
+                        base += kStride;
+                        if (base >= c_hi || ndef == kDefCap) break;
+                        load_tile(base + kStride, ra);
+                        if (Tile::compute(rb, base, vis_lo, c_hi, qop, st)) {
+                            if (lane == 0) s_def[wave][ndef] = base;
+                            ++ndef;
+                        }
+                        base += kStride;
+                        if (base >= c_hi || ndef == kDefCap) break;
+                    }
+                }
+                for (int i = 0; i < ndef; ++i) {
+                    wave_lds_sync();
+                    const int tb = s_def[wave][i];
+                    typename Tile::Regs r;
+                    load_tile(tb, r);
+                    Tile::exact(r, tb, vis_lo, c_hi, st, G, qs, qf, s_w[wave].scr);
+                }
             }
         }
 
         // ---- combine within each wave, then across the waves
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] = cross_group_sum<R>(acc[h][j]);
-        if (l16 == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int h = 4 * q4 + r;
-                if (h < G) {
-                    s_m[wave][h] = m[r];
-                    s_l[wave][h] = lsum[r];
-                }
-            }
-        }
-        if (vrow == 0) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s_acc[wave][h][vcol * 8 + j] = acc[h][j];
-        }
+        Tile::flush(st, G, s_m[wave], s_l[wave], &s_w[wave].acc[0][0]);
         __syncthreads();
-
         const bool full = seg_first && u_end == seg_end;
         const int slot = blockIdx.x * 2 + (seg_start > r0 ? 1 : 0);
         for (int i = tid; i < G * D; i += kThreads) {
@@ -498,7 +423,7 @@ void decode_balanced_kernel(BalancedArgs a) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float e = exp2f(s_m[w][h] - M_use);
-                num = fmaf(e, s_acc[w][h][d], num);
+                num = fmaf(e, s_w[w].acc[h][d], num);
                 den = fmaf(e, s_l[w][h], den);
             }
             if (full) {
@@ -573,13 +498,14 @@ void decode_balanced_kernel(BalancedArgs a) {
     }
 }
 
-template <int D, int G, bool BF16, bool APPEND>
+template <int D, bool BF16, bool APPEND>
 hipError_t launch_typed(const BalancedArgs& a, hipStream_t stream) {
+    if (a.Hq / a.Hkv > kGMax) return hipErrorInvalidValue;
     // the append's variant fields matter only when the append is fused
     const bool full = APPEND && (a.rope_dim != D || a.v_norm);
-    auto kern = full            ? decode_balanced_kernel<D, G, BF16, APPEND, APPEND ? kVarFull : kVarWindow>
-                : a.window != 0 ? decode_balanced_kernel<D, G, BF16, APPEND, kVarWindow>
-                                : decode_balanced_kernel<D, G, BF16, APPEND, kVarNone>;
+    auto kern = full            ? decode_balanced_kernel<D, BF16, APPEND, APPEND ? kVarFull : kVarWindow>
+                : a.window != 0 ? decode_balanced_kernel<D, BF16, APPEND, kVarWindow>
+                                : decode_balanced_kernel<D, BF16, APPEND, kVarNone>;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
         per_cu < 1)
@@ -591,28 +517,13 @@ hipError_t launch_typed(const BalancedArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool BF16, bool APPEND>
-hipError_t dispatch_g(const BalancedArgs& a, hipStream_t stream) {
-    switch (a.Hq / a.Hkv) {
-        case 1: return launch_typed<D, 1, BF16, APPEND>(a, stream);
-        case 2: return launch_typed<D, 2, BF16, APPEND>(a, stream);
-        case 3: return launch_typed<D, 3, BF16, APPEND>(a, stream);
-        case 4: return launch_typed<D, 4, BF16, APPEND>(a, stream);
-        case 5: return launch_typed<D, 5, BF16, APPEND>(a, stream);
-        case 6: return launch_typed<D, 6, BF16, APPEND>(a, stream);
-        case 7: return launch_typed<D, 7, BF16, APPEND>(a, stream);
-        case 8: return launch_typed<D, 8, BF16, APPEND>(a, stream);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 template <bool BF16, bool APPEND>
 hipError_t dispatch_d(const BalancedArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 32: return dispatch_g<32, BF16, APPEND>(a, stream);
-        case 64: return dispatch_g<64, BF16, APPEND>(a, stream);
-        case 128: return dispatch_g<128, BF16, APPEND>(a, stream);
-        case 256: return dispatch_g<256, BF16, APPEND>(a, stream);
+        case 32: return launch_typed<32, BF16, APPEND>(a, stream);
+        case 64: return launch_typed<64, BF16, APPEND>(a, stream);
+        case 128: return launch_typed<128, BF16, APPEND>(a, stream);
+        case 256: return launch_typed<256, BF16, APPEND>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
