@@ -98,6 +98,11 @@ def main() -> int:
                          "read (un-rotated pool), append + decode; f32: the decode step over "
                          "float32 pools, append + decode; blocks: the host block manager "
                          "(admission with a shared prefix, per-step growth and tables)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="decode workloads: per-workgroup phase stamps of the fused step from the "
+                         "profiling build libpkv_timeline.so (python -m "
+                         "paged_kv_cache_315_amd.build --timeline); prints the start / stream / "
+                         "tail breakdown instead of the bench line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -109,6 +114,9 @@ def main() -> int:
 
     if args.workload == "blocks":
         return run_blocks(args)
+    if args.timeline:
+        os.environ.setdefault("PKV_LIBRARY", os.path.join(ROOT, "paged_kv_cache_315_amd",
+                                                          "libpkv_timeline.so"))
 
     import torch
     import paged_kv_cache_315_amd as pkv
@@ -163,6 +171,9 @@ def main() -> int:
         pkv.decode_step(q, k_new, v_new, kp, vp, tables, positions, theta=wl["theta"],
                         scale=wl["scale"], q_norm_w=qn, k_norm_w=kn, eps=wl["eps"], q_out=q_out,
                         out=out, workspace=ws, dtype=wl["dtype"], stream=stream, **variant)
+
+    if args.timeline:
+        return run_timeline(args, torch, pkv, wl, step)
 
     def decode_only(i):
         kp, vp = pools[i % copies]
@@ -274,6 +285,117 @@ def main() -> int:
         "wall_ms_timed_steps": round(wall_ms, 2),
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_timeline(args, torch, pkv, wl, step) -> int:
+    """Per-workgroup phase stamps of the fused step (profiling build): where a launch's time
+    goes between the first workgroup's start and the last one's end."""
+    import ctypes
+    lib = pkv._lib.load()
+    lib.pkv_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.pkv_timeline_set.restype = None
+    n_wg_max, n_st = 2048, 10
+    buf = torch.zeros(n_wg_max * n_st, dtype=torch.int64, device="cuda:0")
+    lib.pkv_timeline_set(buf.data_ptr(), 0)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    launches = max(1, min(args.steps, 200))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    ev_us = []
+    for i in range(launches):
+        buf.zero_()
+        e0.record()
+        step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ev_us.append(e0.elapsed_time(e1) * 1e3)
+        per.append(buf.cpu().numpy().reshape(n_wg_max, n_st).copy())
+    # the same launches with the tile ranges dealt out rotated by a third of the grid: if a
+    # workgroup id stays slow it is where it runs; if a range stays slow it is the data
+    rot = None
+    per_rot = []
+    n_wg = int((per[0][:, 0] != 0).sum())
+    if n_wg > 2:
+        rot = n_wg // 3
+        lib.pkv_timeline_set(buf.data_ptr(), rot)
+        for i in range(launches):
+            buf.zero_()
+            step(i)
+            torch.cuda.synchronize()
+            per_rot.append(buf.cpu().numpy().reshape(n_wg_max, n_st).copy())
+    lib.pkv_timeline_set(None, 0)
+    tick_us = 0.01  # the real-time counter runs at 100 MHz
+
+    def pct(x, q):
+        return float(np.percentile(x, q))
+
+    rows = []
+    for t in per:
+        t = t[t[:, 0] != 0]
+        t0 = t[:, 0].min()
+        rel = (t[:, :7].astype(np.float64) - t0) * tick_us
+        work = t[:, 8] > 0
+        w = rel[work]
+        exit_ = rel[:, 6]
+        rows.append({
+            "span": exit_.max(), "entry_p50": pct(rel[:, 0], 50), "entry_max": rel[:, 0].max(),
+            "lengths_p50": pct(w[:, 1] - w[:, 0], 50),
+            "prefix_p50": pct(w[:, 2] - w[:, 1], 50),
+            "query_p50": pct(w[:, 3] - w[:, 2], 50),
+            "first_tile_p50": pct(w[:, 4] - w[:, 3], 50),
+            "stream_p10": pct(w[:, 5] - w[:, 4], 10), "stream_p50": pct(w[:, 5] - w[:, 4], 50),
+            "stream_p90": pct(w[:, 5] - w[:, 4], 90),
+            "merge_p50": pct(w[:, 6] - w[:, 5], 50),
+            "exit_p10": pct(exit_[work], 10), "exit_p50": pct(exit_[work], 50),
+            "exit_p90": pct(exit_[work], 90), "exit_max": exit_.max(),
+            "tail": exit_.max() - pct(exit_[work], 50),
+            "units_max": int(t[work, 7].max()), "units_mean": float(t[work, 7].mean()),
+            "tiles_per_wg": int(t[work, 8].max()), "workgroups": int(len(t)),
+        })
+    med = {k: round(float(np.median([r[k] for r in rows])), 2) for k in rows[0]}
+    # is a workgroup slow because of where it runs (the same workgroups every launch) or at
+    # random? Stream time per workgroup id, its correlation between launches, and by XCD
+    # (workgroup ids are dealt round-robin over the 8 XCDs)
+    n = min(len(t[t[:, 0] != 0]) for t in per)
+    dur = np.array([(t[:n, 5] - t[:n, 4]).astype(np.float64) * tick_us for t in per])
+    work = per[0][:n, 8] > 0
+    dur = dur[:, work]
+    ids = np.arange(n)[work]
+    ranks = np.argsort(np.argsort(dur, axis=1), axis=1).astype(np.float64)
+    corr = [float(np.corrcoef(ranks[i], ranks[i + 1])[0, 1]) for i in range(len(ranks) - 1)]
+    mean_dur = dur.mean(axis=0)
+    by_xcd = [round(float(np.median(mean_dur[ids % 8 == x])), 2) for x in range(8)]
+    # range of workgroup w (the kernel's XCD-aware deal): per = n // 8 ranges per XCD
+    per_x, rem_x = n // 8, n % 8
+    rng_of = (ids % 8) * per_x + np.minimum(ids % 8, rem_x) + ids // 8
+    by_range_mod8 = [round(float(np.median(mean_dur[rng_of % 8 == k])), 2) for k in range(8)]
+    half = [round(float(np.median(mean_dur[ids < n // 2])), 2),
+            round(float(np.median(mean_dur[ids >= n // 2])), 2)]
+    rot_corr = None
+    if per_rot:
+        d_rot = np.array([(t[:n, 5] - t[:n, 4]).astype(np.float64) * tick_us
+                          for t in per_rot])[:, work].mean(axis=0)
+        # workgroup ids[i] ran range (ids[i] + rot) % n in the rotated launches
+        by_wg = float(np.corrcoef(mean_dur, d_rot)[0, 1])
+        by_range = None
+        if len(ids) == n:   # every workgroup had a range: range r ran on workgroup r - rot
+            same_range = d_rot[(np.arange(n) - rot) % n]
+            by_range = round(float(np.corrcoef(mean_dur, same_range)[0, 1]), 3)
+        rot_corr = {"rotation": rot, "corr_same_workgroup": round(by_wg, 3),
+                    "corr_same_range": by_range}
+    print(json.dumps({"timeline": wl["name"], "launches": launches, "rotated": rot_corr,
+                      "event_us_median": round(float(np.median(ev_us)), 2),
+                      "median_over_launches_us": med,
+                      "stream_rank_corr_between_launches": round(float(np.median(corr)), 3)
+                      if corr else None,
+                      "stream_us_by_xcd": by_xcd, "stream_us_first_second_half_of_ids": half,
+                      "stream_us_by_range_mod8": by_range_mod8,
+                      "stream_us_mean_per_wg_p10_p50_p90": [
+                          round(float(np.percentile(mean_dur, q)), 2) for q in (10, 50, 90)]}),
+          flush=True)
     return 0
 
 

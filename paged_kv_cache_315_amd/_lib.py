@@ -10,7 +10,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpkv.so")
+# PKV_LIBRARY selects another build of the same library (the profiling build of bench.py
+# --timeline); by default the in-tree libpkv.so
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = 1

@@ -1,6 +1,7 @@
 """Build libpkv.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m paged_kv_cache_315_amd.build
+    python -m paged_kv_cache_315_amd.build              # libpkv.so
+    python -m paged_kv_cache_315_amd.build --timeline   # libpkv_timeline.so (profiling build)
 
 Every HIP source is compiled with packed-fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops): the compiler otherwise forms
@@ -85,5 +86,13 @@ def build(out_path: str = LIB_PATH, extra_flags: tuple[str, ...] = (), verbose: 
     return out_path
 
 
+TIMELINE_LIB_PATH = os.path.join(PKG, "libpkv_timeline.so")
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--timeline" in sys.argv:
+        # profiling build: the balanced decode kernel stamps its phases per workgroup
+        # (bench.py --timeline loads it through PKV_LIBRARY)
+        print(build(TIMELINE_LIB_PATH, extra_flags=("-DPKV_TIMELINE",), verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -48,27 +48,39 @@ namespace {
 
 using namespace dev;
 
+#ifdef PKV_TIMELINE
+#define PKV_STAMP(k, v)                                                                       \
+    do {                                                                                      \
+        if (threadIdx.x == 0 && a.timeline != nullptr)                                        \
+            a.timeline[(int64_t)blockIdx.x * kTimelineStamps + (k)] = (v);                    \
+    } while (0)
+#else
+#define PKV_STAMP(k, v) \
+    do {                \
+    } while (0)
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 constexpr int kGMax = 8;          // query heads per KV head
-constexpr int kDefCap = 8;        // exact-path tiles a wave lists before it runs them
 constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;
 
 // Query rotation of one unit and, for the unit holding a segment's last tile, the new token's
 // K/V row (norm + RoPE in double over the first rope_dim dims, optional V norm in float,
 // round-to-nearest-even codes; see kv_append.hip), stored into the pool before the unit streams
-// its tiles. Expects s_q to hold the raw query heads and s_kx / s_vx the new K / V rows (written
-// by this thread block, not yet synchronised) and s_inv the angles per position of the rotary
-// pairs; ends with a barrier, after which this workgroup's own loads of the new row see the
-// stored codes.
+// its tiles. Expects s_q to hold the raw query heads, s_kx / s_vx the new K / V rows and s_wq /
+// s_wk the norm weights (all staged in LDS, so the rotation issues no global loads), and s_inv
+// the angles per position of the rotary pairs; ends with a barrier, after which this
+// workgroup's own loads of the new row see the stored codes.
 template <int D, bool BF16, int VAR>
 __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int G, int b, int g, int pnew,
                                                int64_t blk_new, bool owns_new, bool seg_first,
                                                float* s_q,
                                                const float* s_kx, const float* s_vx,
+                                               const float* s_wq, const float* s_wk,
                                                const double* s_inv, double* s_cs, double* s_r,
                                                float* s_vsc) {
     const int tid = threadIdx.x;
@@ -96,8 +108,8 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int G, 
         const int i = idx - h * rhalf;
         float x0 = s_q[h * D + i], x1 = s_q[h * D + i + rhalf];
         if (norm) {
-            x0 = norm_elem(x0, s_r[h], a.q_norm_w[i]);
-            x1 = norm_elem(x1, s_r[h], a.q_norm_w[i + rhalf]);
+            x0 = norm_elem(x0, s_r[h], s_wq[i]);
+            x1 = norm_elem(x1, s_r[h], s_wq[i + rhalf]);
         }
         float y0, y1;
         rope_rotate(x0, x1, s_cs[2 * i], s_cs[2 * i + 1], y0, y1);
@@ -114,7 +126,7 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int G, 
         for (int idx = tid; idx < G * rest; idx += kThreads) {
             const int h = idx / rest;
             const int j = rope_dim + (idx - h * rest);
-            const float y = norm ? norm_elem(s_q[h * D + j], s_r[h], a.q_norm_w[j]) : s_q[h * D + j];
+            const float y = norm ? norm_elem(s_q[h * D + j], s_r[h], s_wq[j]) : s_q[h * D + j];
             s_q[h * D + j] = y;
             if (seg_first) qo[h * D + j] = y;
         }
@@ -125,8 +137,8 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int G, 
         for (int i = tid; i < rhalf; i += kThreads) {
             float x0 = s_kx[i], x1 = s_kx[i + rhalf];
             if (norm) {
-                x0 = norm_elem(x0, s_r[G], a.k_norm_w[i]);
-                x1 = norm_elem(x1, s_r[G], a.k_norm_w[i + rhalf]);
+                x0 = norm_elem(x0, s_r[G], s_wk[i]);
+                x1 = norm_elem(x1, s_r[G], s_wk[i + rhalf]);
             }
             float y0, y1;
             rope_rotate(x0, x1, s_cs[2 * i], s_cs[2 * i + 1], y0, y1);
@@ -137,17 +149,12 @@ __device__ __forceinline__ void rotate_and_append(const BalancedArgs& a, int G, 
         }
         if (row >= 0) {
             for (int j = rope_dim + tid; j < D; j += kThreads) {
-                const float y = norm ? norm_elem(s_kx[j], s_r[G], a.k_norm_w[j]) : s_kx[j];
+                const float y = norm ? norm_elem(s_kx[j], s_r[G], s_wk[j]) : s_kx[j];
                 a.k_pool[row + j] = encode16(y, BF16);
             }
-            if constexpr (VAR == kVarFull) {
-                const float vsc = vnorm ? *s_vsc : 1.f;
-                for (int i = tid; i < D; i += kThreads)
-                    a.v_pool[row + i] = encode16(vnorm ? vnorm_elem(s_vx[i], vsc) : s_vx[i], BF16);
-            } else {
-                const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
-                for (int i = tid; i < D; i += kThreads) a.v_pool[row + i] = encode16(vsrc[i], BF16);
-            }
+            const float vsc = vnorm ? *s_vsc : 1.f;
+            for (int i = tid; i < D; i += kThreads)
+                a.v_pool[row + i] = encode16(vnorm ? vnorm_elem(s_vx[i], vsc) : s_vx[i], BF16);
         }
     }
     __syncthreads();
@@ -161,11 +168,13 @@ void decode_balanced_kernel(BalancedArgs a) {
 
     __shared__ int s_len[kMaxBalancedBatch];
     __shared__ int s_pre[kMaxBalancedBatch + 1];
-    __shared__ int s_scan[kThreads];
+    __shared__ int s_scan[kWaves];
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ __align__(16) float s_q[kGMax][D];
     __shared__ float s_kx[APPEND ? D : 1];
-    __shared__ float s_vx[APPEND && VAR == kVarFull ? D : 1];
+    __shared__ float s_vx[APPEND ? D : 1];
+    __shared__ float s_wq[APPEND ? D : 1];   // QK-norm weights
+    __shared__ float s_wk[APPEND ? D : 1];
     __shared__ float s_vsc;
     __shared__ double s_inv[APPEND ? HALF : 1];  // theta^(-2i/rope_dim) of rotary pair i
     __shared__ double s_cs[APPEND ? HALF : 1][2];
@@ -178,9 +187,10 @@ void decode_balanced_kernel(BalancedArgs a) {
     __shared__ __align__(16) WaveLds s_w[kWaves];
     __shared__ float s_m[kWaves][kGMax];
     __shared__ float s_l[kWaves][kGMax];
-    __shared__ int s_def[kWaves][kDefCap];   // tiles a wave left for the exact path
+    __shared__ int s_def[kWaves][kDecodeDefCap];   // tiles a wave left for the exact path
     __shared__ int s_last;
 
+    PKV_STAMP(0, wall_clock64());
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -217,17 +227,26 @@ void decode_balanced_kernel(BalancedArgs a) {
         const int rope_dim = VAR == kVarFull ? a.rope_dim : D;
         for (int i = tid; i < (rope_dim >> 1); i += kThreads)
             s_inv[i] = rope_inv_freq(a.theta, i, rope_dim);
+        if (a.q_norm_w != nullptr)
+            for (int i = tid; i < D; i += kThreads) {
+                s_wq[i] = a.q_norm_w[i];
+                s_wk[i] = a.k_norm_w[i];
+            }
     }
-    s_scan[tid] = cnt;
+    // prefix of the tile counts: inclusive scan inside each wave, the wave totals through LDS
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_scan[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const int v = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
+    PKV_STAMP(1, wall_clock64());
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_scan[w];
     {
-        int run = (s_scan[tid] - cnt) * Hkv;
+        int run = (before + incl - cnt) * Hkv;
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
             const int b = tid * kPerThread + k;
@@ -236,16 +255,32 @@ void decode_balanced_kernel(BalancedArgs a) {
                 run += Hkv * ntiles(s_len[b]);
             }
         }
-        if (tid == kThreads - 1) s_pre[B] = s_scan[tid] * Hkv;
+        if (tid == kThreads - 1) s_pre[B] = (before + incl) * Hkv;
     }
     __syncthreads();
 
     // ---- 2. this workgroup's tile range
     const int total = s_pre[B];
     const int T = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int r0 = (int)min((int64_t)blockIdx.x * T, (int64_t)total);
+    // range of this workgroup (profiling builds can deal the ranges out rotated)
+#ifdef PKV_TIMELINE
+    const int wr = xcd_range((int)((blockIdx.x + (unsigned)a.timeline_rot) % gridDim.x),
+                             (int)gridDim.x);
+#else
+    const int wr = xcd_range((int)blockIdx.x, (int)gridDim.x);
+#endif
+    const int r0 = (int)min((int64_t)wr * T, (int64_t)total);
     const int r1 = min(total, r0 + T);
-    if (r0 >= r1) return;  // whole workgroup together
+    PKV_STAMP(2, wall_clock64());
+    PKV_STAMP(8, (uint64_t)(r1 > r0 ? r1 - r0 : 0));
+    if (r0 >= r1) {  // whole workgroup together
+        PKV_STAMP(6, wall_clock64());
+        return;
+    }
+#ifdef PKV_TIMELINE
+    int n_units = 0;
+    bool first_tile = true;
+#endif
 
     int b;
     {  // last sequence whose prefix is <= r0 (its segment list contains tile r0)
@@ -263,7 +298,6 @@ void decode_balanced_kernel(BalancedArgs a) {
     const int64_t nb_max = a.num_blocks - 1;
     const int64_t tok_stride = (int64_t)Hkv * D;   // codes between consecutive slots
     const int chunk_tokens = ((kTblCap - 2) * a.bs) / 64 * 64;
-    const uint32_t koff = Tile::k_lane_off(tok_stride);
     const float qs = a.scale * kLog2e;
     float* part_acc = a.part_acc;
     float* part_ml = a.part_ml;
@@ -303,115 +337,89 @@ void decode_balanced_kernel(BalancedArgs a) {
             o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
             o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
         };
-        typename Tile::Query qop;
+        auto source = [&](int c_lo) {
+            TileSource src;
+            src.k_pool = a.k_pool;
+            src.v_pool = a.v_pool;
+            src.tbl = s_tbl;
+            src.first_blk = (int)bdiv.div((uint32_t)c_lo);
+            src.tbl_cap = kTblCap;
+            src.bdiv = bdiv;
+            src.bs = a.bs;
+            src.tile_in_block = tile_in_block;
+            src.tok_stride = tok_stride;
+            src.head_off = head_off;
+            return src;
+        };
+        // The first table chunk, the query rows (and, fused, the new K / V rows) are staged
+        // together; then each wave's first tile is requested before the query work, so its
+        // latency overlaps the rotation (not for the tile holding the new token, whose row the
+        // rotation stores).
+        const int c_hi0 = min(tok_hi, tok_lo + chunk_tokens);
+        stage_table(tok_lo, c_hi0);
         {
-            stage_table(tok_lo, min(tok_hi, tok_lo + chunk_tokens));
             const float* qsrc = a.q + ((int64_t)b * Hq + g * G) * D;
             for (int i = tid; i < G * D; i += kThreads) s_q[i / D][i % D] = qsrc[i];
-            if constexpr (APPEND) {
-                // the new row's block id, requested with the query (not after the barriers)
-                const int64_t blk_new =
-                    owns_new ? (int64_t)a.tables[(int64_t)b * a.max_blocks + pnew / a.bs] : -1;
-                if (owns_new) {
-                    const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
-                    const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
-                    for (int i = tid; i < D; i += kThreads) {
-                        s_kx[i] = ksrc[i];
-                        if constexpr (VAR == kVarFull) s_vx[i] = vsrc[i];
-                    }
+        }
+        int64_t blk_new = -1;
+        if constexpr (APPEND) {
+            // the new row's block id, requested with the query
+            if (owns_new) blk_new = (int64_t)a.tables[(int64_t)b * a.max_blocks + pnew / a.bs];
+            if (owns_new) {
+                const float* ksrc = a.k_in + ((int64_t)b * Hkv + g) * D;
+                const float* vsrc = a.v_in + ((int64_t)b * Hkv + g) * D;
+                for (int i = tid; i < D; i += kThreads) {
+                    s_kx[i] = ksrc[i];
+                    s_vx[i] = vsrc[i];
                 }
-                rotate_and_append<D, BF16, VAR>(a, G, b, g, pnew, blk_new, owns_new, seg_first,
-                                                &s_q[0][0], s_kx, s_vx, s_inv, &s_cs[0][0], s_r,
-                                                &s_vsc);
-            } else {
-                __syncthreads();
             }
         }
+        __syncthreads();
+        const TileSource src0 = source(tok_lo);
+        const int first_base = tok_lo + wave * kTile;
+        const bool have_first = first_base < c_hi0 && !(owns_new && first_base + kTile > pnew);
+        typename Tile::Regs first;  // requested in every wave (in bounds), used if have_first
+        Tile::load_tile(src0, first_base, tok_lo, c_hi0, first);
+        if constexpr (APPEND)
+            rotate_and_append<D, BF16, VAR>(a, G, b, g, pnew, blk_new, owns_new, seg_first,
+                                            &s_q[0][0], s_kx, s_vx, s_wq, s_wk, s_inv,
+                                            &s_cs[0][0], s_r, &s_vsc);
+        typename Tile::Query qop;
         Tile::setup_query(qf, G, qs, qop);
+#ifdef PKV_TIMELINE
+        if (n_units++ == 0) PKV_STAMP(3, wall_clock64());
+#endif
         typename Tile::State st;
         Tile::init(st);
 
         for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
             const int c_hi = min(tok_hi, c_lo + chunk_tokens);
-            const int first_blk = (int)bdiv.div((uint32_t)c_lo);
             if (c_lo != tok_lo) {  // the first chunk was staged with the query
                 __syncthreads();  // previous readers of s_tbl are done
                 stage_table(c_lo, c_hi);
                 __syncthreads();
             }
-            const int last_base = c_lo + (c_hi - 1 - c_lo) / kTile * kTile;
-
-            auto row_off = [&](int t) -> int64_t {
-                const int j = (int)bdiv.div((uint32_t)t);
-                const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
-                return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
-            };
-            // tiles past the chunk (prefetch beyond the end) read its last tile again; the
-            // loads themselves are unconditional so that none sits behind a branch (which made
-            // the compiler drain the prefetch)
-            auto load_tile = [&](int base, typename Tile::Regs& r) {
-                const int bb = min(base, last_base);
-                const uint16_t* kp;
-                const uint16_t* vp[4];
-                if (tile_in_block) {
-                    const int j = (int)bdiv.div((uint32_t)bb);
-                    const int blk = __builtin_amdgcn_readfirstlane(
-                        s_tbl[min(j - first_blk, kTblCap - 1)]);
-                    const int64_t row0 = ((int64_t)blk * a.bs + (bb - j * a.bs)) * tok_stride + head_off;
-                    kp = a.k_pool + row0 + koff;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) vp[jj] = a.v_pool + row0 + (4 * q4 + jj) * tok_stride;
-                } else {
-                    kp = a.k_pool + row_off(min(bb + l16, c_hi - 1)) + 8 * q4;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        vp[jj] = a.v_pool + row_off(min(bb + 4 * q4 + jj, c_hi - 1));
-                }
-                Tile::load_rows(kp, vp, r);
-            };
-
-            // two register buffers: the next tile's K/V rows load while this one is computed
-            // (the loop is unrolled by two so each buffer keeps its registers); tiles that need
-            // the exact path are listed and done after the loop, reloaded
-            constexpr int kStride = kWaves * kTile;
-            int base = c_lo + wave * kTile;
-            while (base < c_hi) {
-                int ndef = 0;
-                {
-                    typename Tile::Regs ra, rb;
-                    load_tile(base, ra);
-                    while (true) {
-                        load_tile(base + kStride, rb);
-                        if (Tile::compute(ra, base, vis_lo, c_hi, qop, st)) {
-                            if (lane == 0) s_def[wave][ndef] = base;
-                            ++ndef;
-                        }
-                        base += kStride;
-                        if (base >= c_hi || ndef == kDefCap) break;
-                        load_tile(base + kStride, ra);
-                        if (Tile::compute(rb, base, vis_lo, c_hi, qop, st)) {
-                            if (lane == 0) s_def[wave][ndef] = base;
-                            ++ndef;
-                        }
-                        base += kStride;
-                        if (base >= c_hi || ndef == kDefCap) break;
-                    }
-                }
-                for (int i = 0; i < ndef; ++i) {
-                    wave_lds_sync();
-                    const int tb = s_def[wave][i];
-                    typename Tile::Regs r;
-                    load_tile(tb, r);
-                    Tile::exact(r, tb, vis_lo, c_hi, st, G, qs, qf, s_w[wave].scr);
-                }
-            }
+            Tile::stream(source(c_lo), c_lo, c_hi, vis_lo, qop, st, G, qs, qf, s_w[wave].scr,
+                         s_def[wave],
+                         [&]() {
+#ifdef PKV_TIMELINE
+                             if (first_tile) {
+                                 PKV_STAMP(4, wall_clock64());
+                                 first_tile = false;
+                             }
+#endif
+                         },
+                         first, have_first && c_lo == tok_lo);
         }
 
         // ---- combine within each wave, then across the waves
+#ifdef PKV_TIMELINE
+        if (u_end == r1) PKV_STAMP(5, wall_clock64());
+#endif
         Tile::flush(st, G, s_m[wave], s_l[wave], &s_w[wave].acc[0][0]);
         __syncthreads();
         const bool full = seg_first && u_end == seg_end;
-        const int slot = blockIdx.x * 2 + (seg_start > r0 ? 1 : 0);
+        const int slot = wr * 2 + (seg_start > r0 ? 1 : 0);
         for (int i = tid; i < G * D; i += kThreads) {
             const int h = i / D;
             const int d = i % D;
@@ -496,6 +504,10 @@ void decode_balanced_kernel(BalancedArgs a) {
             }
         }
     }
+    PKV_STAMP(6, wall_clock64());
+#ifdef PKV_TIMELINE
+    PKV_STAMP(7, (uint64_t)n_units);
+#endif
 }
 
 template <int D, bool BF16, bool APPEND>

@@ -94,6 +94,24 @@ __device__ __forceinline__ float code_to_float(uint32_t c) {
     else return (float)__builtin_bit_cast(_Float16, (unsigned short)c);
 }
 
+// Where the tiles of one chunk of a KV head's tokens live: the block ids of the chunk staged in
+// LDS (tbl[j - first_blk] is the id of the sequence's block j), the pools and strides.
+struct TileSource {
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* tbl;     // LDS, tbl_cap ids
+    int first_blk;
+    int tbl_cap;
+    BlockDiv bdiv;          // division by the block size
+    int bs;
+    bool tile_in_block;     // bs % 16 == 0: a 16-token tile lies in one block
+    int64_t tok_stride;     // codes between consecutive slots (Hkv * D)
+    int64_t head_off;       // codes of the KV head inside a slot (g * D)
+};
+
+constexpr int kDecodeWaves = 4;     // waves per workgroup of the decode kernels
+constexpr int kDecodeDefCap = 8;    // exact-path tiles a wave lists before it runs them
+
 template <int D, bool BF16>
 struct DecodeTile {
     static constexpr int NK = D / 32;              // K loads (and MFMA k-steps) per lane
@@ -381,6 +399,91 @@ struct DecodeTile {
                 }
         }
         wave_lds_sync();
+    }
+
+    // Loads tile `base` (clamped to the chunk's last tile, so prefetches past the end stay in
+    // range) of tokens [c_lo, c_hi). The loads are unconditional: a load behind a branch made
+    // the compiler wait for the whole prefetch.
+    static __device__ __forceinline__ void load_tile(const TileSource& src, int base, int c_lo,
+                                                     int c_hi, Regs& r) {
+        const int lane = threadIdx.x & 63;
+        const int l16 = lane & 15, q4 = lane >> 4;
+        const int bb = min(base, c_lo + (c_hi - 1 - c_lo) / 16 * 16);
+        const uint16_t* kp;
+        const uint16_t* vp[4];
+        if (src.tile_in_block) {
+            const int j = (int)src.bdiv.div((uint32_t)bb);
+            const int blk =
+                __builtin_amdgcn_readfirstlane(src.tbl[min(j - src.first_blk, src.tbl_cap - 1)]);
+            const int64_t row0 =
+                ((int64_t)blk * src.bs + (bb - j * src.bs)) * src.tok_stride + src.head_off;
+            kp = src.k_pool + row0 + k_lane_off(src.tok_stride);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) vp[jj] = src.v_pool + row0 + (4 * q4 + jj) * src.tok_stride;
+        } else {
+            auto row_off = [&](int t) -> int64_t {
+                const int j = (int)src.bdiv.div((uint32_t)t);
+                const int64_t blk = src.tbl[min(j - src.first_blk, src.tbl_cap - 1)];
+                return (blk * src.bs + (t - j * src.bs)) * src.tok_stride + src.head_off;
+            };
+            kp = src.k_pool + row_off(min(bb + l16, c_hi - 1)) + 8 * q4;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) vp[jj] = src.v_pool + row_off(min(bb + 4 * q4 + jj, c_hi - 1));
+        }
+        load_rows(kp, vp, r);
+    }
+
+    // The tiles of tokens [c_lo, c_hi) (c_lo a multiple of 16 apart from the range start),
+    // tokens before lo not attended: wave w takes tiles c_lo + 16 (w + 4 k). Two register
+    // buffers: the next tile's K/V rows load while one is computed (the loop is unrolled by two
+    // so each buffer keeps its registers). Tiles that need the exact path are listed (def: this
+    // wave's kDecodeDefCap ints of LDS) and run after the loop, reloaded. after_tile() is
+    // called after each streamed tile.
+    // ra: the first buffer; have_first: it already holds this wave's first tile (c_lo + 16
+    // wave), requested by the caller.
+    template <typename QF, typename After>
+    static __device__ __forceinline__ void stream(const TileSource& src, int c_lo, int c_hi,
+                                                  int lo, const Query& q, State& st, int G,
+                                                  float qs, QF&& qf, Scratch& scr, int* def,
+                                                  After&& after_tile, Regs& ra,
+                                                  bool have_first) {
+        constexpr int kStride = kDecodeWaves * 16;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        const bool lane0 = (threadIdx.x & 63) == 0;
+        int base = c_lo + wave * 16;
+        Regs rb;
+        if (!have_first) load_tile(src, base, c_lo, c_hi, ra);
+        while (base < c_hi) {
+            int ndef = 0;
+            {
+                while (true) {
+                    load_tile(src, base + kStride, c_lo, c_hi, rb);
+                    if (compute(ra, base, lo, c_hi, q, st)) {
+                        if (lane0) def[ndef] = base;
+                        ++ndef;
+                    }
+                    after_tile();
+                    base += kStride;
+                    if (base >= c_hi || ndef == kDecodeDefCap) break;
+                    load_tile(src, base + kStride, c_lo, c_hi, ra);
+                    if (compute(rb, base, lo, c_hi, q, st)) {
+                        if (lane0) def[ndef] = base;
+                        ++ndef;
+                    }
+                    after_tile();
+                    base += kStride;
+                    if (base >= c_hi || ndef == kDecodeDefCap) break;
+                }
+            }
+            for (int i = 0; i < ndef; ++i) {
+                wave_lds_sync();
+                const int tb = def[i];
+                Regs r;
+                load_tile(src, tb, c_lo, c_hi, r);
+                exact(r, tb, lo, c_hi, st, G, qs, qf, scr);
+            }
+            if (base < c_hi) load_tile(src, base, c_lo, c_hi, ra);  // after a full list
+        }
     }
 
     // End of a unit: this wave's (m, l, acc) of heads h < G into LDS (m_w / l_w [h],

@@ -228,6 +228,25 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int D, int bs, int max_chunk, i
     return p;
 }
 
+#ifdef PKV_TIMELINE
+namespace pkv {
+namespace {
+uint64_t* g_timeline = nullptr;
+int g_timeline_rot = 0;
+}
+uint64_t* timeline_buffer() { return g_timeline; }
+int timeline_rotation() { return g_timeline_rot; }
+}  // namespace pkv
+
+// Profiling builds only (not part of include/pkv.h): the balanced decode kernel writes
+// kTimelineStamps stamps per workgroup into buf (device, at least 2048 * 8 uint64), or nothing
+// when buf is NULL; workgroup w takes tile range (w + rot) % grid.
+extern "C" void pkv_timeline_set(void* buf, int rot) {
+    pkv::g_timeline = static_cast<uint64_t*>(buf);
+    pkv::g_timeline_rot = rot;
+}
+#endif
+
 extern "C" {
 
 const char* pkv_version(void) { return "0.1.0"; }
@@ -364,6 +383,10 @@ pkv_status run_decode(const float* q, const void* k_pool, const void* v_pool,
         a.window = window;
         a.bf16 = dtype == PKV_BF16;
         a.append = false;
+#ifdef PKV_TIMELINE
+        a.timeline = pkv::timeline_buffer();
+        a.timeline_rot = pkv::timeline_rotation();
+#endif
         e = pkv::launch_decode_balanced(a, stream);
     } else {
         pkv::DecodeArgs a;
@@ -675,6 +698,10 @@ pkv_status decode_step_impl(const float* q_in, const float* k_in, const float* v
     a.window = var.window;
     a.bf16 = dtype == PKV_BF16;
     a.append = true;
+#ifdef PKV_TIMELINE
+    a.timeline = pkv::timeline_buffer();
+    a.timeline_rot = pkv::timeline_rotation();
+#endif
     const hipError_t e = pkv::launch_decode_balanced(a, s);
     if (e != hipSuccess)
         return fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));

@@ -195,6 +195,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroups are dealt to the 8 XCDs round robin (workgroup w runs on XCD w % 8, each XCD with
+// its own L2). A block of consecutive work items per XCD keeps the work of one XCD spread over
+// all KV heads, i.e. over all 256-byte head slices of the token rows and so over all of its L2
+// channels: item = first item of XCD (w % 8) + w / 8. A permutation of [0, n).
+__device__ __forceinline__ int xcd_range(int w, int n) {
+    constexpr int kXcds = 8;
+    const int x = w % kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    return x * per + min(x, rem) + w / kXcds;
+}
+
 // First position a query at attended length L sees under a sliding window of W positions
 // (0: no window).
 __device__ __forceinline__ int window_lo(int L, int W) { return (W > 0 && L > W) ? L - W : 0; }

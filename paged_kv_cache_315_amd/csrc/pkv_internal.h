@@ -123,6 +123,8 @@ struct BalancedArgs {
     int64_t num_blocks;
     int num_cus;
     int max_grid;           // cap on the workgroups (piece slots: 2 per workgroup); 0: none
+    uint64_t* timeline;     // builds with PKV_TIMELINE: kTimelineStamps stamps per workgroup
+    int timeline_rot;       // builds with PKV_TIMELINE: workgroup w takes range (w + rot) % grid
     int rope_dim;           // append only: rotated dims (even, <= D)
     int window;             // sliding window (0: every token)
     bool v_norm;            // append only: V rows normalised per KV head
@@ -131,5 +133,14 @@ struct BalancedArgs {
 };
 
 hipError_t launch_decode_balanced(const BalancedArgs& a, hipStream_t stream);
+
+// Profiling builds (-DPKV_TIMELINE): per workgroup of the balanced kernel, real-time counter
+// stamps (100 MHz) at entry, lengths loaded, tile range known, first unit's query ready, wave
+// 0's first tile done, last unit's streaming done, exit; then the number of units and tiles.
+constexpr int kTimelineStamps = 10;
+#ifdef PKV_TIMELINE
+uint64_t* timeline_buffer();  // set by pkv_timeline_set (pkv_api.hip); nullptr: off
+int timeline_rotation();
+#endif
 
 }  // namespace pkv
