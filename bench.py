@@ -30,8 +30,23 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("paged_kv_cache_315_amd/csrc/decode_balanced.hip",
+                  "paged_kv_cache_315_amd/csrc/decode_tile.h",
                   "paged_kv_cache_315_amd/csrc/pkv_device.h",
                   "paged_kv_cache_315_amd/csrc/pkv_internal.h")
+
+
+def host_cpu() -> dict:
+    """The host's logical core count and CPU model (for the CPU baseline's context)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"of_cores": os.cpu_count(), "cpu_model": model}
 
 
 def profiled_traffic(workload: str):
@@ -103,6 +118,9 @@ def main() -> int:
                          "profiling build libpkv_timeline.so (python -m "
                          "paged_kv_cache_315_amd.build --timeline); prints the start / stream / "
                          "tail breakdown instead of the bench line")
+    ap.add_argument("--pool-offset", default="0,0",
+                    help="K,V: bytes by which each pool copy starts past a 4 KiB-aligned "
+                         "allocation (the caller's pool placement; decode workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -156,7 +174,24 @@ def main() -> int:
     pool_bytes = 2 * wl["k_pool"].nbytes
     copies = args.copies or max(2, int(np.ceil(1.0e9 / pool_bytes)))
     k0, v0 = t(wl["k_pool"], np.int16), t(wl["v_pool"], np.int16)
-    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    k_off, v_off = (int(x) for x in args.pool_offset.split(","))
+
+    def placed(x, off_bytes):
+        """A copy of pool x starting off_bytes past a 4 KiB-aligned allocation."""
+        if off_bytes == 0:
+            return x.clone()
+        assert off_bytes % 16 == 0, "pool offsets must keep 16-byte rows aligned"
+        n = x.numel() + (4096 + off_bytes) // 2
+        buf = torch.empty(n, dtype=x.dtype, device=x.device)
+        skip = ((-buf.data_ptr()) % 4096 + off_bytes) // 2
+        y = buf[skip:skip + x.numel()].view(x.shape)
+        y.copy_(x)
+        return y
+
+    if k_off or v_off:
+        pools = [(placed(k0, k_off), placed(v0, v_off)) for _ in range(copies)]
+    else:
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     B, Hq, Hkv, D = wl["B"], wl["Hq"], wl["Hkv"], wl["D"]
     split = args.split_tokens
     ws_bytes = max(pkv.decode_workspace_bytes(B, Hq, Hkv, D, wl["bs"], wl["max_context_len"], split),
@@ -235,7 +270,7 @@ def main() -> int:
                            window=args.window)
         cpu_s = time.perf_counter() - c0
         cpu = {"value": round(nbytes["step"] / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
+               **host_cpu(), "kind": "oracle",
                "sample": f"one full step of the {wl['name']} workload ({B} sequences), "
                          f"{cpu_s:.2f} s single-threaded; {B / cpu_s:.2f} tokens/s"}
 
@@ -263,6 +298,7 @@ def main() -> int:
             "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
             "qk_norm": wl["q_norm_w"] is not None, "pool_copies": copies,
             "schedule": "partitioned" if split else "balanced", "split_tokens": split,
+            "pool_offset_bytes": args.pool_offset,
             "bytes_per_step": nbytes["step"], "kv_bytes": nbytes["kv"],
         },
         # the step is one launch of the fused kernel, so the step time is its launch time;
@@ -486,7 +522,7 @@ def run_rope(args, torch, pkv, W) -> int:
         L = wl["context_lens"].astype(np.int64)
         E = 4 if wl["dtype"] == "f32" else 2
         kv_sample = int(L[mask.astype(bool)].sum()) * 2 * Hkv * D * E
-        cpu = {"value": round(kv_sample / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+        cpu = {"value": round(kv_sample / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1, **host_cpu(),
                "kind": "oracle",
                "sample": f"attention of {int(mask.sum())} of the {B} sequences (every 4th), "
                          f"{cpu_s:.2f} s single-threaded"}
@@ -581,7 +617,7 @@ def run_blocks(args) -> int:
         import oracle.block_manager as OB
         ref = run(lambda n, b: OB.Pool(n, b), lambda p: OB.Seq(p, 0),
                   lambda ss: OB.fill_tables(ss, max_blocks, 0))
-        cpu = {"value": round(ref[1] * 1e6, 1), "unit": "us per decode step", "cores": 1,
+        cpu = {"value": round(ref[1] * 1e6, 1), "unit": "us per decode step", "cores": 1, **host_cpu(),
                "kind": "oracle",
                "sample": f"the same {steps} steps on the Python oracle model "
                          f"(admission {ref[0] * 1e3:.1f} ms)"}
@@ -701,7 +737,7 @@ def run_prefill(args, torch, pkv, W) -> int:
             cpu_val = 4 * D * Hq * int(tok_len[sel].sum()) / cpu_s / 1e12
         else:
             cpu_val = attn_bytes / cpu_s / 1e9
-        cpu = {"value": round(cpu_val, 6), "unit": unit, "cores": 1, "kind": "oracle",
+        cpu = {"value": round(cpu_val, 6), "unit": unit, "cores": 1, **host_cpu(), "kind": "oracle",
                "sample": f"causal attention of {int(sel.sum())} of the {N} query tokens "
                          f"(every {stride}th), {cpu_s:.2f} s single-threaded"}
 

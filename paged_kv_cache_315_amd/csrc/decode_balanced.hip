@@ -450,7 +450,7 @@ void decode_balanced_kernel(BalancedArgs a) {
             __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores are complete
             __syncthreads();                // ... and so are every other thread's
             int* counter = a.counters + (int64_t)b * Hkv + g;
-            if (tid == 0) s_last = fetch_add_shared(counter, 1) == w_b - w_a;
+            if (tid == 0) s_last = arrive(counter) == w_b - w_a;
             __syncthreads();
             if (s_last) {
                 for (int i = tid; i < G * D; i += kThreads) {

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void decode_rope_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int* counter = a.counters + (int64_t)b * a.Hkv + g;
-    if (threadIdx.x == 0) s_last = fetch_add_shared(counter, 1) == nsplit - 1;
+    if (threadIdx.x == 0) s_last = arrive(counter) == nsplit - 1;
     __syncthreads();
     if (!s_last) return;
     for (int i = threadIdx.x; i < G * D; i += kThreads) {

@@ -246,11 +246,11 @@ struct DecodeTile {
         tmax = swap32_max(tmax);
         const bool grow = tmax > st.m + 8.f;   // -inf base: any finite score; NaN: never
         const float m_new = grow ? tmax : st.m;
-        const float alpha = grow ? exp2f(st.m - m_new) : 1.f;
+        const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;
         st.m = m_new;
         const float mb = m_new == -INFINITY ? 0.f : m_new;   // all scores so far masked
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = exp2f(sc[r] - mb);
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - mb);
         st.l = fmaf(st.l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
         if (__any(grow)) {
 #pragma unroll

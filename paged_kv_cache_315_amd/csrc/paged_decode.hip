@@ -175,7 +175,7 @@ void paged_decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();                // ... and so are every other thread's
     int* counter = a.counters + (int64_t)b * a.Hkv + g;
-    if (threadIdx.x == 0) s_last = fetch_add_shared(counter, 1) == nsplit - 1;
+    if (threadIdx.x == 0) s_last = arrive(counter) == nsplit - 1;
     __syncthreads();
     if (!s_last) return;
     for (int i = threadIdx.x; i < G * D; i += kWaves * 64) {

@@ -206,6 +206,11 @@ __device__ __forceinline__ int xcd_range(int w, int n) {
     return x * per + min(x, rem) + w / kXcds;
 }
 
+// 2^x with the hardware instruction alone (v_exp_f32, about 1 ulp): softmax weights whose value
+// would be a float denormal (below 2^-126, i.e. scores more than 126 below the exponent base)
+// come out as zero, which moves a weighted sum by less than 2^-126 of its largest term.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // First position a query at attended length L sees under a sliding window of W positions
 // (0: no window).
 __device__ __forceinline__ int window_lo(int L, int W) { return (W > 0 && L > W) ? L - W : 0; }
@@ -231,6 +236,11 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
     typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 16-byte load of K/V codes that other workgroups read again (kept in the caches).
+__device__ __forceinline__ uint4 load_cached(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
 }
 
 // Unsigned division by the block size: shift for powers of two, otherwise a multiply-high
@@ -261,17 +271,25 @@ __device__ __forceinline__ BlockDiv make_div(uint32_t d) {
 }
 
 // ---- values shared between workgroups -----------------------------------------------------
-// Partials and counters may be written and read by workgroups on different XCDs (each with its
-// own L2). Agent-scope atomic accesses are coherent device-wide without writing back or
-// invalidating whole L2s, which an agent-scope release / acquire fence would do.
+// Partial results and merge counters are written by one workgroup and read by another, which
+// may sit on another XCD (each XCD has its own L2). Every access to them is an agent-scope
+// atomic: on gfx950 those carry the sc1 cache policy, so a store is written through the XCD's
+// L2 to the device-coherent memory side and counted complete (vmcnt) once it is there, a load
+// misses the L2 and reads the memory side, and a read-modify-write is performed there. The
+// protocol: every thread stores its pieces, waits for its stores (s_waitcnt vmcnt(0)), the
+// workgroup meets at a barrier, then one thread counts the arrival (arrive, relaxed); the
+// workgroup that brings the count to the total reads the pieces after the count returned. So the
+// pieces are at the memory side before the count moves, and are read from there after it.
+// Acquire / release order on the count would do the same through a whole-L2 write-back before
+// and an invalidate after each count (measured: +46 % on the 32-sequence decode step).
 __device__ __forceinline__ void store_shared(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float load_shared(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int fetch_add_shared(int* p, int v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int arrive(int* counter) {
+    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_shared(int* p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -25,6 +25,7 @@
 //     give NaN where float arithmetic gives Inf or nothing).
 //   The waves merge through LDS; a tile with one partition writes out, otherwise the last of
 //   its partitions merges the pieces (agent-scope atomics, as the decode does).
+#include "decode_tile.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -37,28 +38,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr int kTblCap = 1024;
-
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-
-template <bool BF16>
-struct Mma16;
-template <>
-struct Mma16<true> {
-    using vec = bf16x4;
-    using elem = __bf16;
-    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-    }
-};
-template <>
-struct Mma16<false> {
-    using vec = f16x4;
-    using elem = _Float16;
-    static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-    }
-};
 
 template <bool BF16>
 __device__ __forceinline__ float code_to_float(uint16_t c) {
@@ -381,7 +360,7 @@ void prefill_attn_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores are complete
     __syncthreads();                // ... and so are every other thread's
     int* counter = a.counters + item;
-    if (threadIdx.x == 0) s_last = fetch_add_shared(counter, 1) == nsplit - 1;
+    if (threadIdx.x == 0) s_last = arrive(counter) == nsplit - 1;
     __syncthreads();
     if (!s_last) return;
     for (int i = threadIdx.x; i < 16 * D; i += kThreads) {
@@ -427,7 +406,7 @@ void prefill_attn_kernel(PrefillArgs a) {
 
 // Long chunks: a workgroup takes 4 consecutive query tiles of one sequence and KV head (wave w
 // owns tile 4k + w and all of its keys), and the K/V rows of 64 keys at a time are loaded once
-// into LDS (double-buffered: the next 64 keys' loads are in flight while these are used) for
+// (ordinary cached loads: every query tile of the sequence reads them again) into LDS (double-buffered: the next 64 keys' loads are in flight while these are used) for
 // the 4 waves; V is stored transposed ([dim][key]) so a PV operand is one 8-byte read, and a
 // 16-key group holding an Inf / NaN V code is flagged while it is stored. Each wave keeps its
 // own rows' running max / sum / output and writes them at the end; a wave whose tokens all lie
@@ -444,7 +423,6 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
     constexpr int NSUB = KT / kTile;    // 16-key groups per stage
     constexpr int KS = D + 8;           // LDS row stride of K ([key][dim]), in codes
     constexpr int VS = KT + 4;          // LDS row stride of V^T ([dim][key]), in codes
-    constexpr int PS = 20;
     constexpr int CH = KT * D / 8;      // 16-byte chunks of one stage of K (or V)
     constexpr int NKC = CH / kThreads;  // K chunks per thread
     constexpr int NV = CH / kThreads;   // V chunks (adjacent keys of one column) per thread
@@ -455,12 +433,12 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
 
     __shared__ __align__(16) uint16_t s_k[2][KT][KS];
     __shared__ __align__(16) uint16_t s_vt[2][D][VS];
-    __shared__ __align__(16) float s_p[kWaves][16][PS];
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ int s_vbad[2][NSUB];     // stage base whose group holds a non-finite V code
 
     const int g = blockIdx.x;
     const int b = blockIdx.z;
+    const int qtg = blockIdx.y;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15;
@@ -469,7 +447,7 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
 
     const int c0 = a.cu_seqlens[b];
     const int T = max(0, a.cu_seqlens[b + 1] - c0);
-    const int tok_wg = blockIdx.y * kWaves * QT;          // first token of the workgroup
+    const int tok_wg = qtg * kWaves * QT;                 // first token of the workgroup
     if (tok_wg >= T) return;
     const int st = a.start_pos[b];
     const int64_t cap = min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
@@ -527,23 +505,21 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
                 qlo[i][j] = (typename M::elem)(x - (float)hi);
             }
     }
-    int lim[4], lo[4];   // the row sees keys lo .. lim-1
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * q4 + r;
-        const int t = row / G;
-        const bool ok = row < QT * G && t < ntok;
-        lim[r] = ok ? limit_of(tok0 + t) : 0;
-        lo[r] = ok ? window_lo(lim[r], a.window) : 0;
+    // this lane's query row: row l16 of the tile = token l16 / G, head l16 % G; it sees keys
+    // lo_r .. lim_r - 1
+    int lim_r = 0, lo_r = 0;
+    {
+        const int t = l16 / G;
+        if (l16 < QT * G && t < ntok) {
+            lim_r = limit_of(tok0 + t);
+            lo_r = window_lo(lim_r, a.window);
+        }
     }
-
-    float m[4], lsum[4];
-    f32x4 acc[NT];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m[r] = -INFINITY;
-        lsum[r] = 0.f;
-    }
+    // keys every row of the wave sees (limits grow with the token): groups inside need no mask
+    const int w_min_lim = ntok > 0 ? limit_of(tok0) : 0;
+    const int w_max_lo = ntok > 0 ? window_lo(limit_of(tok0 + ntok - 1), a.window) : 0;
+    float m = -INFINITY, lsum = 0.f;   // row l16's exponent base and this lane's part of its sum
+    f32x4 acc[NT];                     // O^T: dims 16 n + 4 q4 + r of row l16
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -574,126 +550,207 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
         // NV adjacent keys of one column (key group tid / (D/8), column tid % (D/8)), so the
         // transposed store writes each dim's NV keys as one packed word instead of NV scattered
         // 16-bit stores. Keys past the chunk of ids clamp to its last key (zeroed when stored).
+        // the K and V rows of one stage, 16 bytes (8 dims of one key) per chunk. K: chunk
+        // c = tid + k * kThreads (k < NKC) is key c / (D/8), column c % (D/8). V: a thread takes
+        // NV adjacent keys of one column (key group tid / (D/8), column tid % (D/8)), so the
+        // transposed store writes each dim's keys as packed words. With the block size a
+        // multiple of 16 every 16-key group of the stage lies in one block: its id is one
+        // wave-uniform table read; otherwise each key's row is looked up. Keys past the chunk
+        // of ids clamp to its last key (zeroed when stored).
+        const bool grp_in_block = a.bs % kTile == 0;
+        const int kkey0 = (int)threadIdx.x / (D / 8);          // K key of chunk k: kkey0 + k * KSTEP
+        const int kcol = (int)threadIdx.x % (D / 8);
+        constexpr int KSTEP = kThreads / (D / 8);              // keys between a thread's K chunks
+        const int vkey0 = ((int)threadIdx.x / (D / 8)) * NV;
         auto load_kv = [&](int base, uint4 (&r)[PER]) {
+            if (grp_in_block) {
+                // block row of the 16-key group holding key `key` (group clamped into the chunk)
+                auto grp_row = [&](int key) -> int64_t {
+                    const int gk = min(base + key, c_hi - 1) / kTile * kTile;
+                    const int j = (int)bdiv.div((uint32_t)gk);
+                    const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
+                    return (blk * a.bs + (gk - j * a.bs)) * tok_stride + head_off;
+                };
 #pragma unroll
-            for (int k = 0; k < NKC; ++k) {
-                const int c = threadIdx.x + k * kThreads;
-                const int key = c / (D / 8);
-                const int col = c % (D / 8);
-                r[k] = load_stream(a.k_pool + row_off(min(base + key, c_hi - 1)) + 8 * col);
+                for (int k = 0; k < NKC; ++k) {
+                    const int key = kkey0 + k * KSTEP;
+                    r[k] = load_cached(a.k_pool + grp_row(key) + (key % kTile) * tok_stride +
+                                       8 * kcol);
+                }
+                const int64_t vrow = grp_row(vkey0);
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    r[NKC + j] = load_cached(a.v_pool + vrow + ((vkey0 + j) % kTile) * tok_stride +
+                                             8 * kcol);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NKC; ++k) {
+                    const int key = kkey0 + k * KSTEP;
+                    r[k] = load_cached(a.k_pool + row_off(min(base + key, c_hi - 1)) + 8 * kcol);
+                }
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    r[NKC + j] = load_cached(a.v_pool + row_off(min(base + vkey0 + j, c_hi - 1)) +
+                                             8 * kcol);
             }
-            const int vcol = threadIdx.x % (D / 8);
-            const int vkey0 = (threadIdx.x / (D / 8)) * NV;
-#pragma unroll
-            for (int j = 0; j < NV; ++j)
-                r[NKC + j] = load_stream(a.v_pool + row_off(min(base + vkey0 + j, c_hi - 1)) +
-                                         8 * vcol);
         };
-        auto store_kv = [&](int base, const uint4 (&r)[PER], int buf) {
+        auto store_kv = [&](int base, uint4 (&r)[PER], int buf) {
+            if (base + KT > c_hi) {   // the chunk's last stage: keys past its end stored as zero
 #pragma unroll
-            for (int k = 0; k < NKC; ++k) {
-                const int c = threadIdx.x + k * kThreads;
-                const int key = c / (D / 8);
-                const int col = c % (D / 8);
-                const uint4 v = base + key < c_hi ? r[k] : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4*>(&s_k[buf][key][8 * col]) = v;
+                for (int k = 0; k < NKC; ++k)
+                    if (base + kkey0 + k * KSTEP >= c_hi) r[k] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    if (base + vkey0 + j >= c_hi) r[NKC + j] = make_uint4(0, 0, 0, 0);
             }
-            const int vcol = threadIdx.x % (D / 8);
-            const int vkey0 = (threadIdx.x / (D / 8)) * NV;
-            uint16_t vv[NV][8];   // [key][dim] codes of this thread's keys
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const uint4 v = base + vkey0 + j < c_hi ? r[NKC + j] : make_uint4(0, 0, 0, 0);
-                if (any_nonfinite<BF16>(v)) s_vbad[buf][(vkey0 + j) / kTile] = base;
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int k = 0; k < NKC; ++k)
+                *reinterpret_cast<uint4*>(&s_k[buf][kkey0 + k * KSTEP][8 * kcol]) = r[k];
+            // V codes that may be Inf / NaN (IEEE-half view of code pairs: a * b + c stays
+            // finite unless one is all-ones-exponent; for bf16 codes it also flags |x| >= 2^121,
+            // which only sends a group down the exact path)
+            {
+                typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+                h2 chk = {(_Float16)0.f, (_Float16)0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    vv[j][2 * i] = (uint16_t)(w[i] & 0xFFFFu);
-                    vv[j][2 * i + 1] = (uint16_t)(w[i] >> 16);
+                for (int j = 0; j + 1 < NV; j += 2) {
+                    const uint32_t x[4] = {r[NKC + j].x, r[NKC + j].y, r[NKC + j].z, r[NKC + j].w};
+                    const uint32_t y[4] = {r[NKC + j + 1].x, r[NKC + j + 1].y, r[NKC + j + 1].z,
+                                           r[NKC + j + 1].w};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        chk = __builtin_elementwise_fma(__builtin_bit_cast(h2, x[w]),
+                                                        __builtin_bit_cast(h2, y[w]), chk);
+                }
+                if constexpr (NV == 1) {
+                    if (any_nonfinite<BF16>(r[NKC])) s_vbad[buf][vkey0 / kTile] = base;
+                } else if (!__builtin_isfinite((float)chk[0]) || !__builtin_isfinite((float)chk[1])) {
+                    s_vbad[buf][vkey0 / kTile] = base;
                 }
             }
+            // transposed V: dim 8 kcol + d of keys vkey0 .. vkey0 + NV - 1, two keys per word
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                uint16_t* dst = &s_vt[buf][8 * vcol + d][vkey0];
+                uint16_t* dst = &s_vt[buf][8 * kcol + d][vkey0];
+                const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+                auto word = [&](int j) -> uint32_t {
+                    const uint4 v = r[NKC + j];
+                    const int w = d >> 1;
+                    return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+                };
                 if constexpr (NV >= 4) {
 #pragma unroll
                     for (int j = 0; j < NV; j += 4)
-                        *reinterpret_cast<uint2*>(dst + j) = make_uint2(
-                            (uint32_t)vv[j][d] | ((uint32_t)vv[j + 1][d] << 16),
-                            (uint32_t)vv[j + 2][d] | ((uint32_t)vv[j + 3][d] << 16));
+                        *reinterpret_cast<uint2*>(dst + j) =
+                            make_uint2(__builtin_amdgcn_perm(word(j + 1), word(j), sel),
+                                       __builtin_amdgcn_perm(word(j + 3), word(j + 2), sel));
                 } else if constexpr (NV == 2) {
-                    *reinterpret_cast<uint32_t*>(dst) =
-                        (uint32_t)vv[0][d] | ((uint32_t)vv[1][d] << 16);
+                    *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(word(1), word(0), sel);
                 } else {
-                    dst[0] = vv[0][d];
+                    dst[0] = (uint16_t)((d & 1) ? word(0) >> 16 : word(0) & 0xFFFFu);
                 }
             }
         };
 
-        // one 16-key group (keys base .. base+15, LDS keys kk .. kk+15 of buffer buf)
+        // one 32-key group (keys base .. base+31 = LDS keys kk .. kk+31 of buffer buf).
+        // S^T = K Q^T: lane (q4, l16) gets keys base + 4 q4 + j (s0) and base + 16 + 4 q4 + j
+        // (s1) of row l16, which is the B operand of O^T += V^T P^T (16x16x32, keys in the
+        // order 4 q4 + j, 16 + 4 q4 + j), so P stays in registers; V^T is two 8-byte reads of
+        // the transposed stage.
         auto compute_group = [&](int base, int kk, int buf, bool vbad) {
-            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                const uint4 kw =
-                    *reinterpret_cast<const uint4*>(&s_k[buf][kk + l16][32 * i + 8 * q4]);
-                const typename M::vec kv = __builtin_bit_cast(typename M::vec, kw);
-                sacc = M::mma(qhi[i], kv, sacc);
-                sacc = M::mma(qlo[i], kv, sacc);
+                const typename M::vec k0v = __builtin_bit_cast(
+                    typename M::vec,
+                    *reinterpret_cast<const uint4*>(&s_k[buf][kk + l16][32 * i + 8 * q4]));
+                const typename M::vec k1v = __builtin_bit_cast(
+                    typename M::vec,
+                    *reinterpret_cast<const uint4*>(&s_k[buf][kk + 16 + l16][32 * i + 8 * q4]));
+                s0 = M::mma(k0v, qhi[i], s0);
+                s0 = M::mma(k0v, qlo[i], s0);
+                s1 = M::mma(k1v, qhi[i], s1);
+                s1 = M::mma(k1v, qlo[i], s1);
             }
-            const int key = base + l16;
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float sc = key < lim[r] && key >= lo[r] ? sacc[r] * score_fix : -INFINITY;
-                const float tmax = row16_max(sc);
-                const float m_new = fmaxf(m[r], tmax);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = exp2f(m[r] - m_use);
-                p[r] = exp2f(sc - m_use);
-                lsum[r] = fmaf(lsum[r], alpha, p[r]);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) acc[n][r] *= alpha;
-                m[r] = m_new;
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_p[wave][4 * q4 + r][l16] = p[r];
-            wave_lds_sync();
-            if (!vbad) {
-                const float4 pr = *reinterpret_cast<const float4*>(&s_p[wave][l16][4 * q4]);
-                const float pf[4] = {pr.x, pr.y, pr.z, pr.w};
-                typename M16::vec phi, plo;
+            float sc[8];
+            if (base >= w_max_lo && base + 32 <= w_min_lim) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const typename M16::elem h = (typename M16::elem)pf[j];
+                    sc[j] = s0[j] * score_fix;
+                    sc[4 + j] = s1[j] * score_fix;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int ka = base + 4 * q4 + j, kb = ka + 16;
+                    sc[j] = ka < lim_r && ka >= lo_r ? s0[j] * score_fix : -INFINITY;
+                    sc[4 + j] = kb < lim_r && kb >= lo_r ? s1[j] * score_fix : -INFINITY;
+                }
+            }
+            float tmax = sc[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
+            tmax = swap16_max(tmax);
+            tmax = swap32_max(tmax);
+            // the exponent base moves only when a score passes it by more than 8 (p <= 256)
+            const bool grow = tmax > m + 8.f;
+            const float m_new = grow ? tmax : m;
+            const float alpha = grow ? fast_exp2(m - m_new) : 1.f;
+            m = m_new;
+            const float mb = m == -INFINITY ? 0.f : m;
+            float p[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                p[j] = fast_exp2(sc[j] - mb);
+                psum += p[j];
+            }
+            lsum = fmaf(lsum, alpha, psum);
+            if (__any(grow)) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+            }
+            if (!vbad) {
+                typename M::vec phi, plo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const typename M::elem h = (typename M::elem)p[j];
                     phi[j] = h;
-                    plo[j] = (typename M16::elem)(pf[j] - (float)h);
+                    plo[j] = (typename M::elem)(p[j] - (float)h);
                 }
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    // B = V keys kk + 4*q4 .. +3 of dim 16*n + l16: one 8-byte read of V^T
-                    const uint2 vw =
+                    const uint2 va =
                         *reinterpret_cast<const uint2*>(&s_vt[buf][16 * n + l16][kk + 4 * q4]);
-                    const typename M16::vec vb = __builtin_bit_cast(typename M16::vec, vw);
-                    acc[n] = M16::mma(phi, vb, acc[n]);
-                    acc[n] = M16::mma(plo, vb, acc[n]);
+                    const uint2 vb =
+                        *reinterpret_cast<const uint2*>(&s_vt[buf][16 * n + l16][kk + 16 + 4 * q4]);
+                    const typename M::vec vt =
+                        __builtin_bit_cast(typename M::vec, make_uint4(va.x, va.y, vb.x, vb.y));
+                    acc[n] = M::mma(vt, phi, acc[n]);
+                    acc[n] = M::mma(vt, plo, acc[n]);
                 }
             } else {
-                // exact float products for a group with Inf / NaN values
+                // exact float products for a group with Inf / NaN values: the row's 32 weights
+                // gathered from the four lanes holding them, keys outside its range skipped
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * q4 + r;
-                    for (int k = 0; k < kTile; ++k) {
-                        if (base + k >= lim[r] || base + k < lo[r]) continue;
-                        const float pk = s_p[wave][row][k];
+                for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-                        for (int n = 0; n < NT; ++n)
-                            acc[n][r] = fmaf(pk, code_to_float<BF16>(s_vt[buf][16 * n + l16][kk + k]),
-                                             acc[n][r]);
+                    for (int j = 0; j < 8; ++j) {
+                        const float pk = __shfl(p[j], l16 + 16 * qq);
+                        const int k = j < 4 ? 4 * qq + j : 16 + 4 * qq + (j - 4);
+                        const int key = base + k;
+                        if (key < lim_r && key >= lo_r) {
+#pragma unroll
+                            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    acc[n][r] = fmaf(
+                                        pk,
+                                        code_to_float<BF16>(s_vt[buf][16 * n + 4 * q4 + r][kk + k]),
+                                        acc[n][r]);
+                        }
                     }
-                }
             }
-            wave_lds_sync();
         };
 
         uint4 regs[PER];
@@ -705,10 +762,11 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
             const bool more = base + KT < c_hi;
             if (more) load_kv(base + KT, regs);
 #pragma unroll
-            for (int sg = 0; sg < NSUB; ++sg) {
-                const int gb = base + sg * kTile;
-                if (gb < L_w && gb + kTile > lo_w)
-                    compute_group(gb, sg * kTile, buf, s_vbad[buf][sg] == base);
+            for (int sg = 0; sg < KT / 32; ++sg) {
+                const int gb = base + sg * 32;
+                if (gb < L_w && gb + 32 > lo_w)
+                    compute_group(gb, sg * 32, buf,
+                                  s_vbad[buf][2 * sg] == base || s_vbad[buf][2 * sg + 1] == base);
             }
             if (more) store_kv(base + KT, regs, buf ^ 1);
             __syncthreads();
@@ -717,16 +775,17 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
     }
 
     // ---- this wave's rows: out = acc / l
+    lsum = swap16_sum(lsum);
+    lsum = swap32_sum(lsum);
+    {
+        const int t = l16 / G;
+        if (l16 < QT * G && t < ntok) {
+            float* o = a.out + ((int64_t)(c0 + tok0 + t) * Hq + g * G + l16 % G) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * q4 + r;
-        const int t = row / G;
-        if (row < QT * G && t < ntok) {
-            float* o = a.out + ((int64_t)(c0 + tok0 + t) * Hq + g * G + row % G) * D;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) o[16 * n + l16] = acc[n][r] / lsum[r];
+            for (int n = 0; n < NT; ++n)
+                *reinterpret_cast<float4*>(o + 16 * n + 4 * q4) =
+                    make_float4(acc[n][0] / lsum, acc[n][1] / lsum, acc[n][2] / lsum,
+                                acc[n][3] / lsum);
         }
     }
 }
