@@ -9,10 +9,12 @@
 //    page "makarna/pkg/kvcache/paged_cache.go", GetBlockForPosition / GetBlockOffset / Append).
 //
 // Schedule. The K/V rows of the batch form one list of 16-token tiles: segment (b, g) holds the
-// ceil(L_b / 16) tiles of KV head g of sequence b, segments in (b, g) order. The grid has one
-// workgroup per resident slot (normally two per compute unit) and workgroup w takes tiles
-// [w*T, (w+1)*T), T = ceil(total / grid): every workgroup streams the same number of bytes
-// whatever the mix of lengths, and all of them are resident from start to end. Inside a
+// ceil(L_b / 16) tiles of KV head g of sequence b, segments in (b, g) order, each preceded by
+// kUnitCost empty positions that stand for what starting a unit costs. The grid has one
+// workgroup per resident slot (normally two per compute unit) and workgroup w takes positions
+// [w*T, (w+1)*T), T = ceil(total / grid): every workgroup has the same work (tiles streamed
+// plus units started) whatever the mix of lengths, and all of them are resident from start to
+// end. Inside a
 // workgroup the 4 waves interleave the 16-token tiles of each unit (the part of one segment
 // that falls in the range); a tile is computed as decode_tile.h describes (QK^T and PV on the
 // matrix cores, online softmax in registers, an exact float path for tiles holding non-finite
@@ -64,6 +66,13 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
+// What starting a unit costs a workgroup (staging its block ids and query, the rotation, the
+// first tile's latency, the merge), in tiles: every segment is preceded by this many empty
+// positions in the tile list, so the ranges of workgroups that start more units hold fewer tiles.
+#ifndef PKV_UNIT_COST
+#define PKV_UNIT_COST 6
+#endif
+constexpr int kUnitCost = PKV_UNIT_COST;
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 constexpr int kGMax = 8;          // query heads per KV head
 constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;
@@ -203,6 +212,8 @@ void decode_balanced_kernel(BalancedArgs a) {
     const int W = VAR != kVarNone ? a.window : 0;
     // tiles of a sequence of L tokens: from the one holding its first visible key to the last
     auto ntiles = [=](int L) { return (L + kTile - 1) / kTile - window_lo(L, W) / kTile; };
+    // positions a segment of nt tiles takes in the list: its start cost, then its tiles
+    auto span = [=](int nt) { return nt > 0 ? nt + kUnitCost : 0; };
 
     // ---- 1. lengths and the tile prefix of every sequence (all heads) -> LDS
     const int64_t cap64 = (int64_t)a.max_blocks * a.bs;
@@ -220,7 +231,7 @@ void decode_balanced_kernel(BalancedArgs a) {
                 L = max(0, min(a.lens[b], cap));
             }
             s_len[b] = L;
-            cnt += ntiles(L);
+            cnt += span(ntiles(L));
         }
     }
     if constexpr (APPEND) {  // while the lengths arrive
@@ -252,7 +263,7 @@ void decode_balanced_kernel(BalancedArgs a) {
             const int b = tid * kPerThread + k;
             if (b < B) {
                 s_pre[b] = run;
-                run += Hkv * ntiles(s_len[b]);
+                run += Hkv * span(ntiles(s_len[b]));
             }
         }
         if (tid == kThreads - 1) s_pre[B] = (before + incl) * Hkv;
@@ -291,7 +302,7 @@ void decode_balanced_kernel(BalancedArgs a) {
         }
         b = lo;
     }
-    int g = (r0 - s_pre[b]) / ntiles(s_len[b]);
+    int g = (r0 - s_pre[b]) / span(ntiles(s_len[b]));
 
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
     const bool tile_in_block = a.bs % kTile == 0;   // a 16-token tile never crosses a block
@@ -308,8 +319,12 @@ void decode_balanced_kernel(BalancedArgs a) {
         const int vis_lo = window_lo(L, W);          // first key the query sees
         const int t0 = vis_lo / kTile * kTile;        // first token of the segment's first tile
         const int nb = ntiles(L);
-        const int seg_start = s_pre[b] + g * nb;
+        const int seg_start = s_pre[b] + g * span(nb) + kUnitCost;  // its first tile
         const int seg_end = seg_start + nb;
+        if (x < seg_start) {  // the range starts in the segment's start cost
+            x = seg_start;
+            if (x >= r1) break;  // ... and ends there: nothing of this segment is ours
+        }
         const int u_end = min(seg_end, r1);
         const int tok_lo = t0 + (x - seg_start) * kTile;
         const int tok_hi = min(t0 + (u_end - seg_start) * kTile, L);
