@@ -408,6 +408,10 @@ def run_timeline(args, torch, pkv, wl, step) -> int:
     per_x, rem_x = n // 8, n % 8
     rng_of = (ids % 8) * per_x + np.minimum(ids % 8, rem_x) + ids // 8
     by_range_mod8 = [round(float(np.median(mean_dur[rng_of % 8 == k])), 2) for k in range(8)]
+    # stream time by the number of units (segment pieces) a workgroup streams
+    units = per[0][:n, 7][work].astype(np.int64)
+    by_units = {int(u): [int((units == u).sum()), round(float(np.median(mean_dur[units == u])), 2)]
+                for u in np.unique(units)}
     half = [round(float(np.median(mean_dur[ids < n // 2])), 2),
             round(float(np.median(mean_dur[ids >= n // 2])), 2)]
     rot_corr = None
@@ -429,6 +433,7 @@ def run_timeline(args, torch, pkv, wl, step) -> int:
                       if corr else None,
                       "stream_us_by_xcd": by_xcd, "stream_us_first_second_half_of_ids": half,
                       "stream_us_by_range_mod8": by_range_mod8,
+                      "workgroups_and_stream_us_by_units": by_units,
                       "stream_us_mean_per_wg_p10_p50_p90": [
                           round(float(np.percentile(mean_dur, q)), 2) for q in (10, 50, 90)]}),
           flush=True)
