@@ -441,7 +441,8 @@ def run_timeline(args, torch, pkv, wl, step) -> int:
 
 
 def run_rope(args, torch, pkv, W) -> int:
-    """Decode step on the vector-ALU kernel of decode_rope.hip, append + decode: with RoPE
+    """Decode step over un-rotated or float32 pools (decode_rope_mfma.hip, the float32
+    matrix-core tile on the balanced schedule), append + decode: with RoPE
     applied at read (--workload rope: pkv_kv_append storing un-rotated keys, the decode rotating
     query and keys), or over float32 pools (--workload f32: the same lengths and shapes with
     float32 K/V, rotation by the append). HBM-bound like the plain decode."""
@@ -466,7 +467,9 @@ def run_rope(args, torch, pkv, W) -> int:
     k0, v0 = t(wl["k_pool"], pool_view), t(wl["v_pool"], pool_view)
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     B, Hq, Hkv, D, bs = wl["B"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"]
-    split = args.split_tokens or pkv.decode_split_tokens(B, Hq, Hkv, D, bs, wl["max_context_len"])
+    split = args.split_tokens or pkv.decode_schedule_split(
+        B, Hq, Hkv, D, bs, wl["max_context_len"], pkv.pool_dtype_code(None, wl["dtype"]),
+        rope_on_read=rope)
     ws = torch.zeros(max(pkv.decode_workspace_bytes(B, Hq, Hkv, D, bs, wl["max_context_len"],
                                                     split), 1), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(q)
@@ -546,7 +549,9 @@ def run_rope(args, torch, pkv, W) -> int:
                    "max_context_len": wl["max_context_len"], "rope_theta": wl["theta"],
                    "pool_copies": copies, "split_tokens": split,
                    "bytes_per_step": nbytes["step"]},
-        "roofline": {"bound": "hbm", "kernel": "decode_rope_kernel (pkv_paged_attn_decode)",
+        "roofline": {"bound": "hbm", "kernel": ("decode_rope_balanced_kernel" if split == 0 else
+                                                "decode_rope_mfma_kernel / decode_rope_kernel")
+                     + " (pkv_paged_attn_decode)",
                      "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": nbytes["decode"],

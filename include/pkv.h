@@ -69,8 +69,8 @@ typedef enum {
                      Append copies float32 rows as they are; page "makarna/pkg/model/arch/
                      hybrid_decoder.go" sends float32 KV to its plain paged kernel). Taken by
                      pkv_kv_append, pkv_prefill_append and pkv_paged_attn_decode (which then runs
-                     the partitioned vector-ALU kernel of the rotation-at-read path, rotating
-                     only with rope_on_read); pkv_decode_step and pkv_paged_attn_prefill return
+                     the kernels of the rotation-at-read path, rotating only with
+                     rope_on_read); pkv_decode_step and pkv_paged_attn_prefill return
                      UNSUPPORTED for it. */
 } pkv_dtype;
 
@@ -193,9 +193,13 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  *              different streams) need separate workspaces.
  * split_tokens 0 for the balanced schedule, or tokens per partition: a positive multiple of
  *              64 of at most 1022 * block_size (a partition stages its block ids in LDS).
- *              With rope_on_read (variant) or float32 pools the partitioned vector-ALU kernel
- *              always runs, split_tokens is at most 4096, and 0 means
+ *              With rope_on_read (variant) or float32 pools: head_dim 64 or 128 with the
+ *              rotated dims (rope_dim, when rotating at read) a multiple of 64 run a float32
+ *              matrix-core kernel on the same schedules and workspace as 16-bit pools; other
+ *              shapes always run the partitioned vector-ALU kernel, where 0 means
  *              pkv_decode_split_tokens(...)'s choice (size the workspace with that value).
+ *              Either way split_tokens is at most 4096 (the rotation is carried across a
+ *              partition in float steps).
  * variant      (host) NULL, or a window as described under pkv_variant: then only the keys
  *              max(0, L - window) .. L - 1 are attended (the partitions and tiles start at the
  *              16-token tile that holds the first of them; the rest of the context is not read)

@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import PKV_BF16, PKV_F16, PKV_F32, PkvError
 
 __all__ = ["PKV_F16", "PKV_BF16", "PKV_F32", "kv_append", "paged_attn_decode", "decode_step",
-           "decode_workspace_bytes",
+           "decode_workspace_bytes", "decode_schedule_split",
            "prefill_append", "paged_attn_prefill", "prefill_workspace_bytes", "prefill_step",
            "decode_step_workspace_bytes", "decode_step_noalloc", "decode_step_noalloc_scratch_bytes",
            "append_then_decode", "decode_split_tokens", "validate_tables", "version",
@@ -119,6 +119,20 @@ def decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_context_len,
                                                   split_tokens)
 
 
+def decode_schedule_split(B, Hq, Hkv, D, block_size, max_context_len, dtype_code: int,
+                          rope_on_read: bool = False, rope_dim: int = 0) -> int:
+    """split_tokens to size a decode workspace with when the call passes split_tokens = 0:
+    0 (the library picks the schedule pkv_decode_workspace_bytes sizes for), except for rotation
+    at read or float32 pools on shapes the matrix-core tile does not serve (head_dim other than
+    64 / 128, or rotated dims not a multiple of 64), which always run the partitioned
+    vector-ALU kernel with pkv_decode_split_tokens(...) tokens per partition."""
+    read_dim = (rope_dim or D) if rope_on_read else 0
+    special = rope_on_read or dtype_code == PKV_F32
+    if special and not (D in (64, 128) and read_dim % 64 == 0):
+        return decode_split_tokens(B, Hq, Hkv, D, block_size, max_context_len)
+    return 0
+
+
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
                       scale: float, *, out=None, workspace=None, split_tokens: int = 0,
                       dtype=None, window: int = 0, rope_on_read: bool = False,
@@ -136,11 +150,10 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, max_context
     NB, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if out is None:
         out = torch.empty_like(q)
-    # rotation at read and float32 pools always run the partitioned schedule: size the
-    # workspace for the partition length the library will pick
-    vector_alu = rope_on_read or pool_dtype_code(k_pool, dtype) == PKV_F32
-    if vector_alu and not split_tokens and B and max_context_len:
-        split_tokens = decode_split_tokens(B, Hq, Hkv, D, bs, max_context_len)
+    if not split_tokens and B and max_context_len:
+        split_tokens = decode_schedule_split(B, Hq, Hkv, D, bs, max_context_len,
+                                             pool_dtype_code(k_pool, dtype), rope_on_read,
+                                             rope_dim)
     need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, split_tokens) if B else 0
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)

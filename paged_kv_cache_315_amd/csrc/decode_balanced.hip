@@ -66,13 +66,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr int kTblCap = 1024;     // block ids staged in LDS per chunk of a unit
-// What starting a unit costs a workgroup (staging its block ids and query, the rotation, the
-// first tile's latency, the merge), in tiles: every segment is preceded by this many empty
-// positions in the tile list, so the ranges of workgroups that start more units hold fewer tiles.
-#ifndef PKV_UNIT_COST
-#define PKV_UNIT_COST 6
-#endif
-constexpr int kUnitCost = PKV_UNIT_COST;
+constexpr int kUnitCost = kBalancedUnitCost;
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 constexpr int kGMax = 8;          // query heads per KV head
 constexpr int kVarNone = 0, kVarWindow = 1, kVarFull = 2;

@@ -96,7 +96,9 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // The balanced schedule needs the per-sequence tile prefix in LDS and int32 tile counts.
 bool balanced_ok(int B, int Hkv, int64_t max_tokens) {
-    return B <= pkv::kMaxBalancedBatch && (int64_t)B * Hkv * ((max_tokens + 15) / 16) < (1LL << 31);
+    // the tile list (tiles plus each segment's start cost) is indexed with 32-bit ints
+    return B <= pkv::kMaxBalancedBatch &&
+           (int64_t)B * Hkv * ((max_tokens + 15) / 16 + pkv::kBalancedUnitCost) < (1LL << 31);
 }
 
 WorkspaceLayout layout_for(int B, int Hq, int Hkv, int D, int64_t max_tokens, int split_tokens,
@@ -456,7 +458,49 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
         return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer argument");
     if (var.rope_read || dtype == PKV_F32) {
-        // rotation at read or float32 pools: the partitioned schedule of decode_rope.hip
+        const int read_dim = var.rope_read ? var.rope_dim : 0;
+        if (split_tokens == 0 && balanced_ok(B, num_kv_heads, max_context_len) &&
+            pkv::decode_rope_mfma_ok(head_dim, num_q_heads / num_kv_heads, read_dim)) {
+            // the float32 matrix-core tile on the balanced schedule (the workspace of the
+            // 16-bit decode: pkv_decode_workspace_bytes with split_tokens = 0)
+            const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len, 0, block_size, true);
+            if (workspace == nullptr || workspace_bytes < wl.total)
+                return fail(PKV_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu",
+                            workspace_bytes, wl.total);
+            char* ws = static_cast<char*>(workspace);
+            pkv::BalancedArgs a{};
+            a.q = q;
+            a.k_pool = static_cast<uint16_t*>(const_cast<void*>(k_pool));
+            a.v_pool = static_cast<uint16_t*>(const_cast<void*>(v_pool));
+            a.tables = block_tables;
+            a.lens = context_lens;
+            a.out = out;
+            a.part_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+            a.part_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+            a.counters = reinterpret_cast<int*>(ws + wl.cnt_off);
+            a.max_blocks = max_blocks_per_seq;
+            a.max_context_len = max_context_len;
+            a.scale = scale;
+            a.theta = var.read_theta;
+            a.B = B;
+            a.Hq = num_q_heads;
+            a.Hkv = num_kv_heads;
+            a.D = head_dim;
+            a.bs = block_size;
+            a.num_blocks = num_blocks;
+            a.num_cus = device_cus();
+            a.rope_dim = read_dim;
+            a.window = var.window;
+            a.bf16 = dtype == PKV_BF16;
+            a.f32 = dtype == PKV_F32;
+            const hipError_t e = pkv::launch_decode_rope_balanced(a, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess)
+                return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString(e));
+            return PKV_OK;
+        }
+        // otherwise the partitioned schedule of decode_rope.hip (the matrix-core tile where it
+        // serves the shape, else the vector-ALU kernel)
         if (split_tokens > 4096)
             return fail(PKV_ERR_INVALID_ARG,
                         "decode: split_tokens=%d above 4096 for rope_on_read / float32 pools (the "

@@ -95,9 +95,21 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 // partitions, workspace layout and merge as launch_paged_decode.
 hipError_t launch_decode_rope(const DecodeArgs& a, hipStream_t stream);
 
+// Shapes the float32 matrix-core tile of decode_rope_mfma.hip serves: head_dim 64 / 128, rotated
+// dims at read a multiple of 64 (0: no rotation).
+bool decode_rope_mfma_ok(int D, int G, int rope_dim);
+
 // Balanced schedule (decode_balanced.hip): one resident workgroup per slot, equal tile ranges.
 constexpr int kMaxBalancedBatch = 2048;  // sequences whose tile prefix fits in LDS
 constexpr int kMaxBalancedGrid = 2048;   // workgroups; each owns two partial-piece slots
+// What starting a unit costs a workgroup (staging its block ids and query, the rotation, the
+// first tile's latency, the merge), in 16-token tiles: in the balanced tile list every segment
+// is preceded by this many empty positions, so the ranges of workgroups that start more units
+// hold fewer tiles.
+#ifndef PKV_UNIT_COST
+#define PKV_UNIT_COST 6
+#endif
+constexpr int kBalancedUnitCost = PKV_UNIT_COST;
 
 struct BalancedArgs {
     const float* q;         // append: q_in (rotated in-kernel); decode: rotated q
@@ -130,9 +142,15 @@ struct BalancedArgs {
     bool v_norm;            // append only: V rows normalised per KV head
     bool bf16;
     bool append;
+    bool f32;               // decode_rope_mfma.hip: float32 pools
 };
 
 hipError_t launch_decode_balanced(const BalancedArgs& a, hipStream_t stream);
+
+// The balanced schedule over the float32 matrix-core tile of decode_rope_mfma.hip (decode only:
+// rotation at read with base `theta` over `rope_dim` dims, 0 = none; float32 or 16-bit pools),
+// for the shapes decode_rope_mfma_ok accepts.
+hipError_t launch_decode_rope_balanced(const BalancedArgs& a, hipStream_t stream);
 
 // Profiling builds (-DPKV_TIMELINE): per workgroup of the balanced kernel, real-time counter
 // stamps (100 MHz) at entry, lengths loaded, tile range known, first unit's query ready, wave

@@ -31,6 +31,13 @@ CASES = {
                    64),
     "g5-d64-window": (lambda: W.make_workload(206, [17, 64, 65, 400], 10, 2, 64, 16, "f16", 1e4),
                       0, 50, 0),
+    # one sequence of 2.2 M tokens: a workgroup's share of the balanced schedule is longer than
+    # 4096 tokens, so its rotation is seeded afresh for each run of at most 4096
+    "long-bs16-runs": (lambda: W.make_workload(210, [2200000], 2, 1, 64, 16, "bf16", 1e4), 0, 0,
+                       0),
+    # block size 12: a 16-token tile spans two blocks (per-row block lookups)
+    "bs12-bf16": (lambda: W.make_workload(209, [100, 777, 1500, 12], 16, 4, 128, 12, "bf16", 5e5),
+                  0, 0, 0),
     # QK-norm with edge values in the new K/V (+-70000, 1e-7, NaN in 1 % of the elements): NaN
     # keys poison their group, +-Inf values (fp16 overflow of V) reach the outputs
     "qknorm-edges-f16": (lambda: W.make_workload(208, [300, 1000, 2000, 64], 32, 8, 128, 16,
