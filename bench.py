@@ -121,6 +121,10 @@ def main() -> int:
     ap.add_argument("--pool-offset", default="0,0",
                     help="K,V: bytes by which each pool copy starts past a 4 KiB-aligned "
                          "allocation (the caller's pool placement; decode workloads)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only time a plain streaming read (torch's float32 sum) of the step's "
+                         "K/V byte count and of 2 GiB, over rotating buffers: context for the "
+                         "decode's rate, not a figure of this library")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (a known-size kernel that the "
                          "HBM byte counters are scaled by)")
@@ -143,6 +147,27 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.read_ceiling:
+        res = {}
+        for name, nbytes_ in (("llama3-8b K/V (296 MB)", 296108032), ("2 GiB", 1 << 31)):
+            n = nbytes_ // 4
+            copies = max(2, int(np.ceil(1.2e9 / nbytes_)))
+            bufs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(copies)]
+            for i in range(5):
+                bufs[i % copies].sum()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 50
+            e0.record()
+            for i in range(reps):
+                bufs[i % copies].sum()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            res[name] = {"us": round(us, 2), "GB_per_s": round(nbytes_ / (us * 1e-6) / 1e9, 1)}
+            del bufs
+        print(json.dumps({"read_ceiling": "torch float32 sum over rotating buffers", **res}))
+        return 0
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
