@@ -26,6 +26,10 @@ CASES = {
                                                   5e5, pool_std=0.5), 0, 0, 64),
     "partial-64of128-window": (lambda: W.make_workload(203, [5, 700, 2100], 16, 4, 128, 16,
                                                        "f16", 1e6, qk_norm=True), 64, 300, 256),
+    # the same layer on the balanced schedule (one rotated chunk pair per lane, window masks)
+    "partial-64of128-window-balanced": (lambda: W.make_workload(211, [5, 700, 2100, 64], 16, 4,
+                                                                128, 16, "f16", 1e6,
+                                                                qk_norm=True), 64, 300, 0),
     "d256-g2": (lambda: W.make_workload(204, [0, 33, 511], 4, 2, 256, 8, "bf16", 1e4), 0, 0, 0),
     "d32-g1-bs1": (lambda: W.make_workload(205, [0, 1, 63, 200], 3, 3, 32, 1, "f16", 1e4), 16, 0,
                    64),
