@@ -433,6 +433,14 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
 
     __shared__ __align__(16) uint16_t s_k[2][KT][KS];
     __shared__ __align__(16) uint16_t s_vt[2][D][VS];
+    // Position of key `key` in row `row` of the transposed V stage: groups of 4 keys are
+    // permuted by row bits 4-6 (XOR of the group index with 0 .. 7). LDS serves 8-byte accesses
+    // 16 lanes at a time over 32 banks: a store pass writes rows 8 dims apart (at 34 words per
+    // row, two bank offsets without the permutation), a read pass reads 16 consecutive rows that
+    // share bits 4-6; with it both fall on distinct banks.
+    auto vt_key = [](int row, int key) -> int {
+        return (((key >> 2) ^ ((row >> 4) & 7)) << 2) | (key & 3);
+    };
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ int s_vbad[2][NSUB];     // stage base whose group holds a non-finite V code
 
@@ -631,7 +639,7 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
             // transposed V: dim 8 kcol + d of keys vkey0 .. vkey0 + NV - 1, two keys per word
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                uint16_t* dst = &s_vt[buf][8 * kcol + d][vkey0];
+                const int row = 8 * kcol + d;
                 const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
                 auto word = [&](int j) -> uint32_t {
                     const uint4 v = r[NKC + j];
@@ -641,13 +649,15 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
                 if constexpr (NV >= 4) {
 #pragma unroll
                     for (int j = 0; j < NV; j += 4)
-                        *reinterpret_cast<uint2*>(dst + j) =
+                        *reinterpret_cast<uint2*>(&s_vt[buf][row][vt_key(row, vkey0 + j)]) =
                             make_uint2(__builtin_amdgcn_perm(word(j + 1), word(j), sel),
                                        __builtin_amdgcn_perm(word(j + 3), word(j + 2), sel));
                 } else if constexpr (NV == 2) {
-                    *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(word(1), word(0), sel);
+                    *reinterpret_cast<uint32_t*>(&s_vt[buf][row][vt_key(row, vkey0)]) =
+                        __builtin_amdgcn_perm(word(1), word(0), sel);
                 } else {
-                    dst[0] = (uint16_t)((d & 1) ? word(0) >> 16 : word(0) & 0xFFFFu);
+                    s_vt[buf][row][vt_key(row, vkey0)] =
+                        (uint16_t)((d & 1) ? word(0) >> 16 : word(0) & 0xFFFFu);
                 }
             }
         };
@@ -720,10 +730,11 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
                 }
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
+                    const int row = 16 * n + l16;
                     const uint2 va =
-                        *reinterpret_cast<const uint2*>(&s_vt[buf][16 * n + l16][kk + 4 * q4]);
-                    const uint2 vb =
-                        *reinterpret_cast<const uint2*>(&s_vt[buf][16 * n + l16][kk + 16 + 4 * q4]);
+                        *reinterpret_cast<const uint2*>(&s_vt[buf][row][vt_key(row, kk + 4 * q4)]);
+                    const uint2 vb = *reinterpret_cast<const uint2*>(
+                        &s_vt[buf][row][vt_key(row, kk + 16 + 4 * q4)]);
                     const typename M::vec vt =
                         __builtin_bit_cast(typename M::vec, make_uint4(va.x, va.y, vb.x, vb.y));
                     acc[n] = M::mma(vt, phi, acc[n]);
@@ -746,7 +757,8 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
                                 for (int r = 0; r < 4; ++r)
                                     acc[n][r] = fmaf(
                                         pk,
-                                        code_to_float<BF16>(s_vt[buf][16 * n + 4 * q4 + r][kk + k]),
+                                        code_to_float<BF16>(s_vt[buf][16 * n + 4 * q4 + r]
+                                                                [vt_key(16 * n + 4 * q4 + r, kk + k)]),
                                         acc[n][r]);
                         }
                     }
