@@ -744,7 +744,7 @@ def run_prefill(args, torch, pkv, W) -> int:
         value, unit = achieved, "TFLOP/s"
     else:
         achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "prefill_attn_kernel (pkv_paged_attn_prefill)",
+        roof = {"bound": "hbm", "kernel": "prefill_balanced_kernel (pkv_paged_attn_prefill)",
                 "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "bytes_per_launch": attn_bytes, "avg_launch_us": round(attn_ms * 1e3, 3)}

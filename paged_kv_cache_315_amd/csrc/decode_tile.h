@@ -112,7 +112,10 @@ struct TileSource {
 constexpr int kDecodeWaves = 4;     // waves per workgroup of the decode kernels
 constexpr int kDecodeDefCap = 8;    // exact-path tiles a wave lists before it runs them
 
-template <int D, bool BF16>
+// ROWS: the 16 rows are (token, head) pairs of several query tokens, each row with its own key
+// range [State::rlo, State::rhi) inside the tile-uniform one (chunked prefill); without it every
+// row sees the same keys (decode).
+template <int D, bool BF16, bool ROWS = false>
 struct DecodeTile {
     static constexpr int NK = D / 32;              // K loads (and MFMA k-steps) per lane
     static constexpr int NC = D / 8;               // 8-dim chunks of a row
@@ -133,6 +136,8 @@ struct DecodeTile {
         float m;            // exponent base of head l16 (log2 units)
         float l;            // this lane's part of the sum of weights of head l16
         f32x4 acc[NH][8];   // O^T rows 4*q4 + r (chunk), MFMA e (dim in chunk), head l16
+        int rlo, rhi;       // ROWS: keys row l16 sees
+        int alo, ahi;       // ROWS: keys every row sees (the same in every lane)
     };
     struct Regs {
         uint4 k[NK];        // token l16, dims 8*q4 + 32 i .. + 7
@@ -273,7 +278,8 @@ struct DecodeTile {
             s = M32::mma(kv, q.hi[i], s);
             s = M32::mma(kv, q.lo[i], s);
         }
-        const bool full = base >= lo && base + 16 <= hi;   // the same in every lane
+        bool full = base >= lo && base + 16 <= hi;   // the same in every lane
+        if constexpr (ROWS) full = full && base >= st.alo && base + 16 <= st.ahi;
         if (!full) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -302,7 +308,7 @@ struct DecodeTile {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int t = base + 4 * q4 + j;
-            const bool ok = full || (t >= lo && t < hi);
+            const bool ok = full || (t >= lo && t < hi && (!ROWS || (t >= st.rlo && t < st.rhi)));
             const float x = s[j] * q.fix;
             bad |= ok && !__builtin_isfinite(x);
             sc[j] = ok ? x : -INFINITY;
@@ -349,7 +355,8 @@ struct DecodeTile {
                                                  State& st, int G, float qs, QF&& qf, Scratch& scr) {
         const int lane = threadIdx.x & 63;
         const int l16 = lane & 15, q4 = lane >> 4;
-        const bool full = base >= lo && base + 16 <= hi;
+        bool full = base >= lo && base + 16 <= hi;
+        if constexpr (ROWS) full = full && base >= st.alo && base + 16 <= st.ahi;
 #pragma unroll
         for (int i = 0; i < NK; ++i) scr.k[l16][4 * i + q4] = r.k[i];
 #pragma unroll
@@ -376,7 +383,8 @@ struct DecodeTile {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int t = base + 4 * q4 + j;
-            sc[j] = ((full || (t >= lo && t < hi)) && l16 < G) ? x[j] : -INFINITY;
+            const bool ok = full || (t >= lo && t < hi && (!ROWS || (t >= st.rlo && t < st.rhi)));
+            sc[j] = (ok && l16 < G) ? x[j] : -INFINITY;
         }
         float p[4];
         softmax(sc, st, p);
@@ -387,6 +395,8 @@ struct DecodeTile {
         for (int t = 0; t < 16; ++t) {
             const int tt = base + t;
             if (!(full || (tt >= lo && tt < hi))) continue;
+            // a row that does not see this key has weight 0, which must not meet its values
+            if (ROWS && !full && !(tt >= st.rlo && tt < st.rhi)) continue;
             const float pt = scr.s[l16][t];
 #pragma unroll
             for (int w = 0; w < NH; ++w)

@@ -194,6 +194,8 @@ pkv_status check_decode_shape(const char* who, int B, int Hq, int Hkv, int D) {
 struct PrefillPlan {
     int QTmax, P, S;
     bool shared;   // 4 query tiles per workgroup sharing each K/V tile (no key split)
+    bool balanced; // one query tile per sequence: the balanced schedule
+    int max_grid;  // balanced: workgroups the pieces are sized for
     size_t cnt_off, acc_off, ml_off, total;
 };
 
@@ -209,6 +211,21 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int D, int bs, int max_chunk, i
         p.shared = true;
         p.S = 1;
         p.P = 0;
+        return p;
+    }
+    // at most one query tile per sequence (draft verification, short chunks): the balanced
+    // schedule, pieces for two workgroups per compute unit
+    if (p.QTmax == 1 && B <= pkv::kMaxBalancedBatch &&
+        (int64_t)B * Hkv * ((max_ctx + 15) / 16 + pkv::kBalancedUnitCost) < (1LL << 31)) {
+        p.balanced = true;
+        p.S = 1;
+        p.P = 0;
+        p.max_grid = std::min(pkv::kMaxBalancedGrid, 2 * cus);
+        const size_t parts = (size_t)p.max_grid * 2 * 16;
+        p.cnt_off = 0;
+        p.acc_off = align256((size_t)B * Hkv * sizeof(int));
+        p.ml_off = p.acc_off + align256(parts * D * sizeof(float));
+        p.total = p.ml_off + align256(parts * 2 * sizeof(float));
         return p;
     }
     // split the keys only as far as needed to give every compute unit a few workgroups
@@ -913,6 +930,9 @@ pkv_status pkv_paged_attn_prefill(const float* q, const void* k_pool, const void
     a.window = var.window;
     a.bf16 = dtype == PKV_BF16;
     a.shared_tiles = plan.shared;
+    a.balanced = plan.balanced;
+    a.max_grid = plan.max_grid;
+    a.num_cus = device_cus();
     const hipError_t e = pkv::launch_prefill_attn(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(PKV_ERR_HIP, "prefill: launch failed: %s", hipGetErrorString(e));

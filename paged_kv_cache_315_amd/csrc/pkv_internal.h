@@ -57,6 +57,10 @@ struct PrefillArgs {
     int window;                 // sliding window (0: every token)
     bool bf16;
     bool shared_tiles;          // 4 query tiles per workgroup sharing each K/V tile (S == 1)
+    bool balanced;              // one query tile per sequence on the balanced schedule: pieces
+                                // [max_grid * 2, 16, D] / [max_grid * 2, 16, 2], counters [B, Hkv]
+    int max_grid;               // balanced: workgroups (two piece slots each)
+    int num_cus;                // balanced: compute units of the device
 };
 
 // Query tokens per tile (16 MFMA rows of G heads each).

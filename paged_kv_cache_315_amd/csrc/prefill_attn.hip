@@ -14,15 +14,13 @@
 // keys [s*P, min((s+1)*P, L_tile)), L_tile = one past the last token's position. The 4 waves
 // take interleaved 16-key tiles with the next tile's K/V loads in flight, as in the decode.
 //
-// Per 16-key tile and wave:
-//   S = Q K^T on the matrix cores (v_mfma_f32_16x16x32, Q split into a 16-bit head and a 16-bit
-//     remainder, scaled by scale*log2(e)), then the causal mask per row (key <= the row's
-//     position) and the online softmax per row (DPP row max, exp2).
-//   O += P V on the matrix cores (v_mfma_f32_16x16x16): P goes through LDS to the A layout and
-//     is split into a 16-bit head and remainder (two MFMAs), V goes through LDS to the B layout
-//     (keys along k). A tile holding a non-finite V code takes an exact vector-ALU product
-//     instead (the split's zero remainder, or a masked key's zero weight, times Inf would
-//     give NaN where float arithmetic gives Inf or nothing).
+// Per 16-key tile and wave: the decode tile of decode_tile.h with its 16 rows taken as the
+// (token, head) rows of the query tile and a key range per row (State::rlo / rhi: key <= the
+// row's position, and the row's window start): scores as K Q^T on the matrix cores, so each lane
+// holds four keys of one row, which is the B operand of O^T += V^T P^T — the weights stay in
+// registers; the online softmax per row with a lazily moved exponent base; a tile holding a
+// non-finite code (or a row-masked key meeting a non-finite value) is computed afterwards in
+// float arithmetic, row ranges included.
 //   The waves merge through LDS; a tile with one partition writes out, otherwise the last of
 //   its partitions merges the pieces (agent-scope atomics, as the decode does).
 #include "decode_tile.h"
@@ -64,40 +62,27 @@ __device__ __forceinline__ bool any_nonfinite(const uint4 w) {
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void prefill_attn_kernel(PrefillArgs a) {
-    using M = Mma<BF16>;
-    using M16 = Mma16<BF16>;
-    constexpr int NK = D / 32;          // QK^T k-steps (and K loads) per tile
-    constexpr int NT = D / 16;          // PV output tiles of 16 dims
-    constexpr int R = D / 8;            // lanes per V row (8 codes per lane)
-    constexpr int TPL = 64 / R;         // V rows per load instruction
-    constexpr int U = kTile / TPL;      // V loads per tile
+    using Tile = DecodeTile<D, BF16, true>;
     constexpr int QT = 16 / G;          // query tokens per tile
-    constexpr int VS = D + 8;           // LDS row stride of a V tile, in codes (bank spread)
-    constexpr int PS = 20;              // LDS row stride of a P tile, in floats
-    static_assert(D % 32 == 0 && U * TPL == kTile, "tile shape");
     static_assert(G >= 1 && G <= 8, "GQA group");
-
-    constexpr int kVBytes = kWaves * kTile * VS * 2;
-    constexpr int kAccBytes = kWaves * 16 * D * 4;
-    __shared__ __align__(16) char s_big[kVBytes > kAccBytes ? kVBytes : kAccBytes];
-    __shared__ __align__(16) float s_p[kWaves][16][PS];
+    union WaveLds {
+        typename Tile::Scratch scr;     // the exact path's tile while streaming
+        float acc[16][D];               // the wave's partial result after it
+    };
+    __shared__ __align__(16) WaveLds s_w[kWaves];
     __shared__ int32_t s_tbl[kTblCap];
+    __shared__ __align__(16) float s_q[16][D];
     __shared__ float s_m[kWaves][16];
     __shared__ float s_l[kWaves][16];
+    __shared__ int s_def[kWaves][kDecodeDefCap];
     __shared__ int s_last;
-    uint16_t (*s_v)[kTile][VS] = reinterpret_cast<uint16_t (*)[kTile][VS]>(s_big);
-    float (*s_acc)[16][D] = reinterpret_cast<float (*)[16][D]>(s_big);
 
     const int g = blockIdx.x;
     const int s = blockIdx.y;
     const int b = blockIdx.z / a.QTmax;
     const int qt = blockIdx.z - b * a.QTmax;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15;          // key of the score layout / row of the A operands
-    const int q4 = lane >> 4;           // lane group: k-slice of the operands, row quad of S / O
-    const int vrow = lane / R;          // V load layout: key row within a load
-    const int vcol = lane % R;          //                8-dim column
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int l16 = threadIdx.x & 15;
     const int Hq = a.Hkv * G;
 
     const int c0 = a.cu_seqlens[b];
@@ -105,6 +90,7 @@ void prefill_attn_kernel(PrefillArgs a) {
     const int tok0 = qt * QT;
     if (tok0 >= T) return;              // whole workgroup exits together
     const int ntok = min(QT, T - tok0);
+    const int R = ntok * G;             // valid rows: (token r / G, head r % G)
     const int st = a.start_pos[b];
     const int64_t cap = min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
     // keys a row may see: positions 0 .. st + token (capped so every index stays in range)
@@ -114,14 +100,15 @@ void prefill_attn_kernel(PrefillArgs a) {
     // ... and the first of them (a sliding window hides the keys before it)
     auto row_lo = [&](int t) -> int { return window_lo(row_limit(t), a.window); };
     const int L_tile = row_limit(ntok - 1);
-    const int t_first = row_lo(0) / kTile * kTile;   // partitions start at the tile holding it
+    const int vis_lo = row_lo(0);                     // first key any row sees
+    const int t_first = vis_lo / kTile * kTile;       // partitions start at the tile holding it
     const int P = a.split_tokens;
     const int t_begin = t_first + s * P;
     if (t_begin >= L_tile) return;
     const int t_end = min(L_tile, t_begin + P);
     const int nsplit = (L_tile - t_first + P - 1) / P;
 
-    // ---- block ids of this partition -> LDS
+    // ---- block ids of this partition and the tile's query rows -> LDS
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
     const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
     const int first_blk = (int)bdiv.div((uint32_t)t_begin);
@@ -131,207 +118,56 @@ void prefill_attn_kernel(PrefillArgs a) {
         const int64_t id = trow[first_blk + i];
         s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
     }
-
-    // ---- Q operand: row l16 = (token l16 / G, head l16 % G), zero where no valid token
-    typename M::vec qhi[NK], qlo[NK];
-    float score_fix = 1.f;
-    {
-        const int tq = l16 / G;
-        const bool qok = l16 < QT * G && tq < ntok;
-        const float* qrow = a.q + ((int64_t)(c0 + tok0 + min(tq, ntok - 1)) * Hq + g * G +
-                                   l16 % G) * D + 8 * q4;
-        const float qs = a.scale * kLog2e;
-        float qv[NK][8];
-        float qmax = 0.f;
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * i);
-            const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * i + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                qv[i][j] = qok ? xs[j] * qs : 0.f;
-                qmax = fmaxf(qmax, fabsf(qv[i][j]));
-            }
-        }
-        float qscale = 1.f;
-        if constexpr (!BF16) {
-            // fp16 operand: bring max |q| below 2^14 with an exact power-of-two scale
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
-            if (qmax >= 16384.f && qmax <= 3.0e38f) {
-                const int e = ilogbf(qmax) - 13;
-                qscale = ldexpf(1.f, -e);
-                score_fix = ldexpf(1.f, e);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NK; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = qv[i][j] * qscale;
-                const typename M::elem hi = (typename M::elem)x;
-                qhi[i][j] = hi;
-                qlo[i][j] = (typename M::elem)(x - (float)hi);
-            }
+    for (int i = threadIdx.x; i < R * D; i += kThreads) {
+        const int row = i / D;
+        s_q[row][i % D] =
+            a.q[((int64_t)(c0 + tok0 + row / G) * Hq + g * G + row % G) * D + i % D];
     }
-    // the rows of the score / output layout this lane holds: 4 * q4 + r
-    int lim[4], lo[4];   // the row sees keys lo .. lim-1
-    bool rvalid[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * q4 + r;
-        const int t = row / G;
-        rvalid[r] = row < QT * G && t < ntok;
-        lim[r] = rvalid[r] ? min(row_limit(t), t_end) : 0;
-        lo[r] = rvalid[r] ? row_lo(t) : 0;
-    }
-    __syncthreads();  // s_tbl ready
+    __syncthreads();
 
-    const int64_t tok_stride = (int64_t)a.Hkv * D;   // codes between consecutive slots
-    const int64_t head_off = (int64_t)g * D;
-    auto row_off = [&](int t) -> int64_t {
-        const int j = (int)bdiv.div((uint32_t)t);
-        const int64_t blk = s_tbl[min(j - first_blk, kTblCap - 1)];
-        return (blk * a.bs + (t - j * a.bs)) * tok_stride + head_off;
+    auto qf = [&](int h, int d0, float (&o)[8]) {
+        const float4* src = reinterpret_cast<const float4*>(&s_q[h][d0]);
+        const float4 x0 = src[0], x1 = src[1];
+        o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+        o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
     };
-    // loads are unconditional (keys past the partition clamp to its last key, masked at use)
-    auto load_tile = [&](int base, uint4 (&kr)[NK], uint4 (&vr)[U]) {
-        const uint16_t* kp = a.k_pool + row_off(min(base + l16, t_end - 1)) + 8 * q4;
-#pragma unroll
-        for (int i = 0; i < NK; ++i) kr[i] = load_stream(kp + 32 * i);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int tv = min(base + u * TPL + vrow, t_end - 1);
-            vr[u] = load_stream(a.v_pool + row_off(tv) + 8 * vcol);
-        }
-    };
+    TileSource src;
+    src.k_pool = a.k_pool;
+    src.v_pool = a.v_pool;
+    src.tbl = s_tbl;
+    src.first_blk = first_blk;
+    src.tbl_cap = kTblCap;
+    src.bdiv = bdiv;
+    src.bs = a.bs;
+    src.tile_in_block = a.bs % kTile == 0;
+    src.tok_stride = (int64_t)a.Hkv * D;
+    src.head_off = (int64_t)g * D;
+    // this wave's first tile is requested before the query operands are built
+    const int first_base = t_begin + wave * kTile;
+    typename Tile::Regs first;
+    Tile::load_tile(src, first_base, t_begin, t_end, first);
+    const float qs = a.scale * kLog2e;
+    typename Tile::Query qop;
+    Tile::setup_query(qf, R, qs, qop);
+    typename Tile::State stt;
+    Tile::init(stt);
+    // row l16's keys (limits and window starts grow with the token), and the keys all rows see
+    stt.rlo = l16 < R ? row_lo(l16 / G) : 0;
+    stt.rhi = l16 < R ? min(row_limit(l16 / G), t_end) : 0;
+    stt.alo = row_lo(ntok - 1);
+    stt.ahi = min(row_limit(0), t_end);
+    Tile::stream(src, t_begin, t_end, vis_lo, qop, stt, R, qs, qf, s_w[wave].scr, s_def[wave],
+                 []() {}, first, first_base < t_end);
 
-    float m[4], lsum[4];
-    f32x4 acc[NT];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m[r] = -INFINITY;
-        lsum[r] = 0.f;
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute_tile = [&](int base, const uint4 (&kc)[NK], const uint4 (&vc)[U]) {
-        // scores
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const typename M::vec kv = __builtin_bit_cast(typename M::vec, kc[i]);
-            sacc = M::mma(qhi[i], kv, sacc);
-            sacc = M::mma(qlo[i], kv, sacc);
-        }
-        const int key = base + l16;
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float sc = key < lim[r] && key >= lo[r] ? sacc[r] * score_fix : -INFINITY;
-            const float tmax = row16_max(sc);
-            const float m_new = fmaxf(m[r], tmax);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m[r] - m_use);   // 1 unless the row's max grew
-            p[r] = exp2f(sc - m_use);
-            lsum[r] = fmaf(lsum[r], alpha, p[r]);
-#pragma unroll
-            for (int n = 0; n < NT; ++n) acc[n][r] *= alpha;
-            m[r] = m_new;
-        }
-        // P -> LDS [row][key]; V -> LDS [key][dim] (keys past the partition as zero codes)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s_p[wave][4 * q4 + r][l16] = p[r];
-        bool vbad = false;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kr = u * TPL + vrow;
-            const uint4 raw = base + kr < t_end ? vc[u] : make_uint4(0, 0, 0, 0);
-            vbad |= any_nonfinite<BF16>(raw);
-            *reinterpret_cast<uint4*>(&s_v[wave][kr][8 * vcol]) = raw;
-        }
-        wave_lds_sync();
-        if (!__any(vbad)) {
-            // A = P rows l16, keys 4*q4 .. 4*q4+3, split into head and remainder
-            const float4 pr = *reinterpret_cast<const float4*>(&s_p[wave][l16][4 * q4]);
-            const float pf[4] = {pr.x, pr.y, pr.z, pr.w};
-            typename M16::vec phi, plo;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const typename M16::elem h = (typename M16::elem)pf[j];
-                phi[j] = h;
-                plo[j] = (typename M16::elem)(pf[j] - (float)h);
-            }
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                // B = V keys 4*q4 .. 4*q4+3, dim 16*n + l16
-                typename M16::vec vb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    vb[j] = __builtin_bit_cast(typename M16::elem, s_v[wave][4 * q4 + j][16 * n + l16]);
-                acc[n] = M16::mma(phi, vb, acc[n]);
-                acc[n] = M16::mma(plo, vb, acc[n]);
-            }
-        } else {
-            // exact float products for a tile with Inf / NaN values
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * q4 + r;
-                for (int k = 0; k < kTile; ++k) {
-                    if (base + k >= lim[r] || base + k < lo[r]) continue;
-                    const float pk = s_p[wave][row][k];
-#pragma unroll
-                    for (int n = 0; n < NT; ++n)
-                        acc[n][r] = fmaf(pk, code_to_float<BF16>(s_v[wave][k][16 * n + l16]),
-                                         acc[n][r]);
-                }
-            }
-        }
-        wave_lds_sync();
-    };
-
-    // ---- stream the partition: two register buffers, the next tile in flight
-    constexpr int kStride = kWaves * kTile;
-    int base = t_begin + wave * kTile;
-    {
-        uint4 ka[NK], va[U], kb[NK], vb[U];
-        load_tile(base, ka, va);
-        while (base < t_end) {
-            load_tile(base + kStride, kb, vb);
-            compute_tile(base, ka, va);
-            base += kStride;
-            if (base >= t_end) break;
-            load_tile(base + kStride, ka, va);
-            compute_tile(base, kb, vb);
-            base += kStride;
-        }
-    }
-
-    // ---- combine the waves through LDS (s_acc reuses the V staging space)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
-    __syncthreads();  // every wave is done with its V tiles
-    if (l16 == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s_m[wave][4 * q4 + r] = m[r];
-            s_l[wave][4 * q4 + r] = lsum[r];
-        }
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s_acc[wave][4 * q4 + r][16 * n + l16] = acc[n][r];
+    // ---- combine the waves through LDS
+    Tile::flush(stt, R, s_m[wave], s_l[wave], &s_w[wave].acc[0][0]);
     __syncthreads();
 
     const int64_t item = ((int64_t)b * a.QTmax + qt) * a.Hkv + g;
-    for (int i = threadIdx.x; i < 16 * D; i += kThreads) {
+    for (int i = threadIdx.x; i < R * D; i += kThreads) {
         const int row = i / D;
         const int d = i % D;
         const int t = row / G;
-        if (row >= QT * G || t >= ntok) continue;
         float Mx = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][row]);
@@ -340,7 +176,7 @@ void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float e = exp2f(s_m[w][row] - M_use);
-            num = fmaf(e, s_acc[w][row][d], num);
+            num = fmaf(e, s_w[w].acc[row][d], num);
             den = fmaf(e, s_l[w][row], den);
         }
         if (nsplit == 1) {
@@ -363,11 +199,10 @@ void prefill_attn_kernel(PrefillArgs a) {
     if (threadIdx.x == 0) s_last = arrive(counter) == nsplit - 1;
     __syncthreads();
     if (!s_last) return;
-    for (int i = threadIdx.x; i < 16 * D; i += kThreads) {
+    for (int i = threadIdx.x; i < R * D; i += kThreads) {
         const int row = i / D;
         const int d = i % D;
         const int t = row / G;
-        if (row >= QT * G || t >= ntok) continue;
         const int64_t p0 = item * a.S;
         float Mx = -INFINITY;
         for (int k0 = 0; k0 < nsplit; k0 += 8) {
@@ -802,9 +637,269 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
     }
 }
 
+// Chunks of at most one query tile per sequence (draft verification, short chunks): the
+// balanced schedule of decode_balanced.hip over the same tile. Segment (b, g) = the keys the
+// chunk of sequence b sees through KV head g, as 16-key tiles from the one holding its first
+// token's first key to its last token's last, preceded by kBalancedUnitCost empty positions;
+// workgroup w takes positions [r T, (r + 1) T) (r its range under the XCD-aware deal), with the
+// chunk's (token, head) rows and their key ranges; a segment cut by ranges leaves one piece of
+// 16 rows per workgroup (slots 2r, 2r + 1) and the last workgroup to finish merges them.
+constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
+
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void prefill_balanced_kernel(PrefillArgs a) {
+    using Tile = DecodeTile<D, BF16, true>;
+    union WaveLds {
+        typename Tile::Scratch scr;     // the exact path's tile while streaming
+        float acc[16][D];               // the wave's partial result after it
+    };
+    __shared__ __align__(16) WaveLds s_w[kWaves];
+    __shared__ int s_nt[kMaxBalancedBatch];      // tiles of each sequence's segment (one head)
+    __shared__ int s_pre[kMaxBalancedBatch + 1];
+    __shared__ int s_scan[kWaves];
+    __shared__ int32_t s_tbl[kTblCap];
+    __shared__ __align__(16) float s_q[16][D];
+    __shared__ float s_m[kWaves][16];
+    __shared__ float s_l[kWaves][16];
+    __shared__ int s_def[kWaves][kDecodeDefCap];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int B = a.B;
+    const int Hkv = a.Hkv;
+    const int Hq = a.Hq;
+    const int W = a.window;
+    const int64_t cap = min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
+    // keys token t of a chunk starting at position st may see: 0 .. st + t (capped)
+    auto limit = [&](int st, int t) -> int {
+        return (int)max((int64_t)0, min((int64_t)st + t + 1, cap));
+    };
+    auto span = [=](int nt) { return nt > 0 ? nt + kBalancedUnitCost : 0; };
+
+    // ---- each sequence's tile count and the tile prefix of every sequence (all heads) -> LDS
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int b = tid * kPerThread + k;
+        if (b < B) {
+            // tokens of the chunk (the plan guarantees at most one query tile: QT)
+            const int Tb = min(16 / G, max(0, a.cu_seqlens[b + 1] - a.cu_seqlens[b]));
+            int nt = 0;
+            if (Tb > 0) {
+                const int st = a.start_pos[b];
+                const int L = limit(st, Tb - 1);
+                const int vis = window_lo(limit(st, 0), W);
+                nt = L > vis ? (L + kTile - 1) / kTile - vis / kTile : 0;
+            }
+            s_nt[b] = nt;
+            cnt += span(nt);
+        }
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_scan[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_scan[w];
+    {
+        int run = (before + incl - cnt) * Hkv;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int b = tid * kPerThread + k;
+            if (b < B) {
+                s_pre[b] = run;
+                run += Hkv * span(s_nt[b]);
+            }
+        }
+        if (tid == kThreads - 1) s_pre[B] = (before + incl) * Hkv;
+    }
+    __syncthreads();
+
+    // ---- this workgroup's range of the list
+    const int total = s_pre[B];
+    const int T = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int wr = xcd_range((int)blockIdx.x, (int)gridDim.x);
+    const int r0 = (int)min((int64_t)wr * T, (int64_t)total);
+    const int r1 = min(total, r0 + T);
+    if (r0 >= r1) return;  // whole workgroup together
+
+    int b;
+    {  // last sequence whose prefix is <= r0 (its segment list contains position r0)
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= r0) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    }
+    int g = (r0 - s_pre[b]) / span(s_nt[b]);
+
+    const BlockDiv bdiv = make_div((uint32_t)a.bs);
+    const int64_t nb_max = a.num_blocks - 1;
+    const int chunk_tokens = ((kTblCap - 2) * a.bs) / 64 * 64;
+    const float qs = a.scale * kLog2e;
+    auto qf = [&](int h, int d0, float (&o)[8]) {
+        const float4* src = reinterpret_cast<const float4*>(&s_q[h][d0]);
+        const float4 x0 = src[0], x1 = src[1];
+        o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+        o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+    };
+
+    for (int x = r0; x < r1;) {
+        // ---- one unit: tiles [x, u_end) of segment (b, g)
+        const int nb = s_nt[b];
+        const int c0 = a.cu_seqlens[b];
+        const int Tb = min(16 / G, max(0, a.cu_seqlens[b + 1] - c0));
+        const int stp = a.start_pos[b];
+        const int L = limit(stp, Tb - 1);
+        const int vis = window_lo(limit(stp, 0), W);   // first key any row sees
+        const int t0 = vis / kTile * kTile;
+        const int seg_start = s_pre[b] + g * span(nb) + kBalancedUnitCost;  // its first tile
+        const int seg_end = seg_start + nb;
+        if (x < seg_start) {  // the range starts in the segment's start cost
+            x = seg_start;
+            if (x >= r1) break;  // ... and ends there: nothing of this segment is ours
+        }
+        const int u_end = min(seg_end, r1);
+        const int tok_lo = t0 + (x - seg_start) * kTile;
+        const int tok_hi = min(t0 + (u_end - seg_start) * kTile, L);
+        const bool seg_first = x == seg_start;
+        const int R = Tb * G;                          // rows (token r / G, head r % G)
+        const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+
+        for (int i = tid; i < R * D; i += kThreads) {
+            const int row = i / D;
+            s_q[row][i % D] = a.q[((int64_t)(c0 + row / G) * Hq + g * G + row % G) * D + i % D];
+        }
+        typename Tile::State stt;
+        Tile::init(stt);
+        // row l16's keys (limits and window starts grow with the token), and the keys all rows see
+        stt.rlo = l16 < R ? window_lo(limit(stp, l16 / G), W) : 0;
+        stt.rhi = l16 < R ? limit(stp, l16 / G) : 0;
+        stt.alo = window_lo(limit(stp, Tb - 1), W);
+        stt.ahi = limit(stp, 0);
+        typename Tile::Query qop;
+        for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
+            const int c_hi = min(tok_hi, c_lo + chunk_tokens);
+            if (c_lo != tok_lo) __syncthreads();  // readers of s_tbl are done
+            const int first_blk = (int)bdiv.div((uint32_t)c_lo);
+            const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
+            for (int i = tid; i < n_blk; i += kThreads) {
+                const int64_t id = trow[first_blk + i];
+                s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+            }
+            __syncthreads();  // s_tbl (and, for the first run, s_q)
+            if (c_lo == tok_lo) Tile::setup_query(qf, R, qs, qop);
+            TileSource src;
+            src.k_pool = a.k_pool;
+            src.v_pool = a.v_pool;
+            src.tbl = s_tbl;
+            src.first_blk = first_blk;
+            src.tbl_cap = kTblCap;
+            src.bdiv = bdiv;
+            src.bs = a.bs;
+            src.tile_in_block = a.bs % kTile == 0;
+            src.tok_stride = (int64_t)Hkv * D;
+            src.head_off = (int64_t)g * D;
+            typename Tile::Regs ra;
+            Tile::stream(src, c_lo, c_hi, vis, qop, stt, R, qs, qf, s_w[wave].scr, s_def[wave],
+                         []() {}, ra, false);
+        }
+
+        // ---- combine the waves; the outputs, or this workgroup's piece of the segment
+        Tile::flush(stt, R, s_m[wave], s_l[wave], &s_w[wave].acc[0][0]);
+        __syncthreads();
+        const bool full = seg_first && u_end == seg_end;
+        const int slot = wr * 2 + (seg_start > r0 ? 1 : 0);
+        for (int i = tid; i < R * D; i += kThreads) {
+            const int row = i / D;
+            const int d = i % D;
+            float Mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][row]);
+            const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float e = exp2f(s_m[w][row] - M_use);
+                num = fmaf(e, s_w[w].acc[row][d], num);
+                den = fmaf(e, s_l[w][row], den);
+            }
+            if (full) {
+                a.out[((int64_t)(c0 + row / G) * Hq + g * G + row % G) * D + d] = num / den;
+            } else {
+                const int64_t pi = (int64_t)slot * 16 + row;
+                store_shared(a.part_acc + pi * D + d, num);
+                if (d == 0) {
+                    store_shared(a.part_ml + pi * 2, Mx);
+                    store_shared(a.part_ml + pi * 2 + 1, den);
+                }
+            }
+        }
+        if (!full) {
+            // the workgroups holding pieces of this segment: w_a .. w_b (ranges)
+            const int w_a = seg_start / T;
+            const int w_b = (seg_end - 1) / T;
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores are complete
+            __syncthreads();                // ... and so are every other thread's
+            int* counter = a.counters + (int64_t)b * Hkv + g;
+            if (tid == 0) s_last = arrive(counter) == w_b - w_a;
+            __syncthreads();
+            if (s_last) {
+                for (int i = tid; i < R * D; i += kThreads) {
+                    const int row = i / D;
+                    const int d = i % D;
+                    float Mx = -INFINITY;
+                    for (int w = w_a; w <= w_b; ++w) {
+                        const int sl = w * 2 + (w == w_a && seg_start != w_a * T ? 1 : 0);
+                        Mx = fmaxf(Mx, load_shared(a.part_ml + ((int64_t)sl * 16 + row) * 2));
+                    }
+                    const float M_use = (Mx == -INFINITY) ? 0.f : Mx;
+                    float num = 0.f, den = 0.f;
+                    for (int w = w_a; w <= w_b; ++w) {
+                        const int sl = w * 2 + (w == w_a && seg_start != w_a * T ? 1 : 0);
+                        const int64_t pk = (int64_t)sl * 16 + row;
+                        const float e = exp2f(load_shared(a.part_ml + pk * 2) - M_use);
+                        den = fmaf(e, load_shared(a.part_ml + pk * 2 + 1), den);
+                        num = fmaf(e, load_shared(a.part_acc + pk * D + d), num);
+                    }
+                    a.out[((int64_t)(c0 + row / G) * Hq + g * G + row % G) * D + d] = num / den;
+                }
+                if (tid == 0) store_shared(counter, 0);  // ready for the next call
+            }
+        }
+        __syncthreads();  // LDS (s_q, s_tbl, s_w, s_m, s_l) is reused by the next unit
+
+        x = u_end;
+        if (x < r1) {
+            if (++g == Hkv) {
+                g = 0;
+                do { ++b; } while (b < B - 1 && s_nt[b] == 0);
+            }
+        }
+    }
+}
+
 template <int D, int G, bool BF16>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-    if (a.shared_tiles) {
+    if (a.balanced) {
+        auto kern = prefill_balanced_kernel<D, G, BF16>;
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        const int grid = (int)std::min<int64_t>(
+            std::min<int64_t>((int64_t)per_cu * a.num_cus, a.max_grid), kMaxBalancedGrid);
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    } else if (a.shared_tiles) {
         dim3 grid((unsigned)a.Hkv, (unsigned)((a.QTmax + kWaves - 1) / kWaves), (unsigned)a.B);
         hipLaunchKernelGGL((prefill_attn_shared_kernel<D, G, BF16>), grid, dim3(kThreads), 0,
                            stream, a);

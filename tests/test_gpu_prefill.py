@@ -114,6 +114,22 @@ def test_prefill_nonfinite_values():
         assert np.isfinite(out[40:]).all()
 
 
+def test_prefill_balanced_short_chunks():
+    """At most one query tile per sequence: the balanced kernel. Non-finite K/V in the drafts
+    (a row that does not see a key must not meet its Inf value), and one sequence of 300000
+    cached tokens in 1-token blocks, whose workgroup shares span several staged block-id runs
+    and whose pieces hundreds of workgroups merge."""
+    wl = W.make_prefill_workload(225, [20, 0, 57, 200, 3, 31, 16, 90], [4, 3, 4, 2, 4, 1, 4, 4],
+                                 8, 2, 64, 16, "f16", 1e4, spare_blocks=1)
+    wl["v_new"][2, 1, 3] = np.inf      # sequence 0, token 2: tokens 0, 1 do not see it
+    wl["v_new"][12, 0, 7] = -np.inf
+    wl["k_new"][21, 1, 0] = np.nan
+    dev, out = _check(wl, "balanced, non-finite drafts", finite=False)
+    assert np.isfinite(out[:2]).all()
+    wl = W.make_prefill_workload(226, [300000], [3], 8, 2, 64, 1, "f16", 1e4, spare_blocks=1)
+    _check(wl, "balanced, 300000 tokens in 1-token blocks")
+
+
 def test_prefill_one_token_matches_decode():
     """One token per sequence: the prefill kernel and the decode kernel agree (float tolerance:
     different kernels, different summation order)."""

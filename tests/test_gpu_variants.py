@@ -147,6 +147,8 @@ PREFILL_VARIANTS = [
     ([0, 700, 1500, 5] * 4, [400, 300, 77, 200] * 4, 8, 2, 64, 4, "bf16", False, 0, False,
      100, 5),                                                              # shared-tile kernel
     ([900, 100] * 4, [512, 512] * 4, 32, 8, 128, 16, "bf16", True, 64, True, 256, 9),
+    # one query tile per sequence (the balanced kernel), block size 12, a window
+    ([300, 40, 2000, 0], [4, 3, 2, 1], 32, 8, 128, 12, "bf16", False, 0, False, 100, 1),
 ]
 
 
