@@ -140,15 +140,11 @@ struct RTile {
     }
 
     // The query operand in LDS (all threads of the workgroup; the caller meets at a barrier
-    // before it is read): the G heads at q_rows (head h at q_rows + h D) scaled by
-    // qs = scale * log2 e, rows G .. 15 zero. Rows are D + 4 floats apart, so the 16 lanes of a
-    // lane group (16 rows, 16 bytes each) hit distinct banks.
-    static __device__ __forceinline__ void stage_query(const float* q_rows, int G, float qs,
-                                                       float (*sq)[D + 4]) {
-        for (int i = threadIdx.x; i < 16 * D; i += kThreads) {
-            const int h = i / D;
-            sq[h][i % D] = h < G ? q_rows[i] * qs : 0.f;
-        }
+    // before it is read): rows 0 .. G - 1 the G heads scaled by qs = scale * log2 e, rows
+    // G .. 15 zero (written once per workgroup by zero_query_rows). Rows are D + 4 floats apart,
+    // so the 16 lanes of a lane group (16 rows, 16 bytes each) hit distinct banks.
+    static __device__ __forceinline__ void zero_query_rows(int G, float (*sq)[D + 4]) {
+        for (int i = threadIdx.x + G * D; i < 16 * D; i += kThreads) sq[i / D][i % D] = 0.f;
     }
 
     // Rotation seeds of a run of tiles starting at token c_lo (all threads of the workgroup;
@@ -397,12 +393,16 @@ void decode_rope_balanced_kernel(BalancedArgs a) {
 
     // ---- lengths and the tile prefix of every sequence (all heads) -> LDS
     const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
+    // all of a thread's loads first (one round trip), then the counts
+    int lv[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) lv[k] = a.lens[min(tid * kPerThread + k, B - 1)];
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int b = tid * kPerThread + k;
         if (b < B) {
-            const int L = max(0, min(a.lens[b], cap));
+            const int L = max(0, min(lv[k], cap));
             s_len[b] = L;
             cnt += span(ntiles(L));
         }
@@ -465,6 +465,7 @@ void decode_rope_balanced_kernel(BalancedArgs a) {
     float* part_acc = a.part_acc;
     float* part_ml = a.part_ml;
 
+    Tile::zero_query_rows(G, s_q);  // read after the first unit's barrier
     for (int x = r0; x < r1;) {
         // ---- one unit: tiles [x, u_end) of segment (b, g)
         const int L = s_len[b];
@@ -484,18 +485,27 @@ void decode_rope_balanced_kernel(BalancedArgs a) {
         const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
         const int64_t head_off = (int64_t)g * D;
 
-        Tile::stage_query(a.q + ((int64_t)b * Hq + g * G) * D, G, qs, s_q);
+        const float* qsrc = a.q + ((int64_t)b * Hq + g * G) * D;
         typename Tile::State st;
         Tile::init(st);
         for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
             const int c_hi = min(tok_hi, c_lo + chunk_tokens);
             if (c_lo != tok_lo) __syncthreads();  // readers of s_tbl / s_rot are done
-            // block ids of the chunk -> LDS (at most kTblCap - 1 of them)
+            // block ids of the run -> LDS (at most kTblCap - 1 of them)
             const int first_blk = (int)bdiv.div((uint32_t)c_lo);
             const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
-            for (int i = tid; i < n_blk; i += kThreads) {
-                const int64_t id = trow[first_blk + i];
-                s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+            // (with the query rows for the first run: one round trip for both)
+            {
+                float qv[8 * D / kThreads];
+                batched_load<kThreads>(c_lo == tok_lo ? G * D : 0,
+                                       [&](int i) { return qsrc[i]; }, qv);
+                int32_t tv[kTblCap / kThreads];
+                batched_load<kThreads>(n_blk, [&](int i) { return trow[first_blk + i]; }, tv);
+                batched_store<kThreads>(c_lo == tok_lo ? G * D : 0, qv,
+                                        [&](int i, float v) { s_q[i / D][i % D] = v * qs; });
+                batched_store<kThreads>(n_blk, tv, [&](int i, int32_t id) {
+                    s_tbl[i] = id < 0 ? 0 : (int32_t)min((int64_t)id, nb_max);
+                });
             }
             Tile::seeds(s_rot, a.theta, L - 1, c_lo);
             __syncthreads();

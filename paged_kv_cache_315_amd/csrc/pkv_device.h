@@ -215,6 +215,28 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // (0: no window).
 __device__ __forceinline__ int window_lo(int L, int W) { return (W > 0 && L > W) ? L - W : 0; }
 
+// Copy of n elements (n <= PER NT), element i -> st(i, ld(i)), by the NT threads of a
+// workgroup, thread t taking i = t + k NT, in two halves: batched_load issues every load of a
+// thread into registers, batched_store stores them. Copies whose loads are all issued before
+// the first store wait for one memory round trip together, where a loop that stores each
+// element as it arrives waits for one per element it takes. Lanes past n load element n - 1
+// (in bounds) and store nothing. Every register of v is written (zero where nothing is
+// loaded), so no value of an earlier copy stays live in it across the code between copies.
+template <int NT, int PER, typename T, typename Ld>
+__device__ __forceinline__ void batched_load(int n, Ld&& ld, T (&v)[PER]) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        v[k] = k * NT < n ? ld(min((int)threadIdx.x + k * NT, n - 1)) : T{};
+}
+template <int NT, int PER, typename T, typename St>
+__device__ __forceinline__ void batched_store(int n, const T (&v)[PER], St&& st) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = (int)threadIdx.x + k * NT;
+        if (i < n) st(i, v[k]);
+    }
+}
+
 // ---- K/V codes ----------------------------------------------------------------------------
 template <bool BF16>
 __device__ __forceinline__ void decode8(const uint4 raw, float (&f)[8]) {

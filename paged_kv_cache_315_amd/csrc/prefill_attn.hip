@@ -655,8 +655,9 @@ void prefill_balanced_kernel(PrefillArgs a) {
         float acc[16][D];               // the wave's partial result after it
     };
     __shared__ __align__(16) WaveLds s_w[kWaves];
-    __shared__ int s_nt[kMaxBalancedBatch];      // tiles of each sequence's segment (one head)
-    __shared__ int s_pre[kMaxBalancedBatch + 1];
+    __shared__ int s_pre[kMaxBalancedBatch + 1];  // list position of each sequence's segments
+    __shared__ int s_c0[kMaxBalancedBatch + 1];   // cu_seqlens
+    __shared__ int s_st[kMaxBalancedBatch];       // start positions
     __shared__ int s_scan[kWaves];
     __shared__ int32_t s_tbl[kTblCap];
     __shared__ __align__(16) float s_q[16][D];
@@ -680,22 +681,31 @@ void prefill_balanced_kernel(PrefillArgs a) {
     };
     auto span = [=](int nt) { return nt > 0 ? nt + kBalancedUnitCost : 0; };
 
-    // ---- each sequence's tile count and the tile prefix of every sequence (all heads) -> LDS
+    // ---- each sequence's tile count and the tile prefix of every sequence (all heads) -> LDS;
+    // all of a thread's loads first (one round trip)
+    int cu[kPerThread + 1], sp[kPerThread], sn[kPerThread];
+#pragma unroll
+    for (int k = 0; k <= kPerThread; ++k) cu[k] = a.cu_seqlens[min(tid * kPerThread + k, B)];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) sp[k] = a.start_pos[min(tid * kPerThread + k, B - 1)];
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int b = tid * kPerThread + k;
+        sn[k] = 0;
         if (b < B) {
             // tokens of the chunk (the plan guarantees at most one query tile: QT)
-            const int Tb = min(16 / G, max(0, a.cu_seqlens[b + 1] - a.cu_seqlens[b]));
+            const int Tb = min(16 / G, max(0, cu[k + 1] - cu[k]));
             int nt = 0;
             if (Tb > 0) {
-                const int st = a.start_pos[b];
-                const int L = limit(st, Tb - 1);
-                const int vis = window_lo(limit(st, 0), W);
+                const int L = limit(sp[k], Tb - 1);
+                const int vis = window_lo(limit(sp[k], 0), W);
                 nt = L > vis ? (L + kTile - 1) / kTile - vis / kTile : 0;
             }
-            s_nt[b] = nt;
+            s_c0[b] = cu[k];
+            s_st[b] = sp[k];
+            if (b == B - 1) s_c0[B] = cu[k + 1];
+            sn[k] = nt;
             cnt += span(nt);
         }
     }
@@ -716,7 +726,7 @@ void prefill_balanced_kernel(PrefillArgs a) {
             const int b = tid * kPerThread + k;
             if (b < B) {
                 s_pre[b] = run;
-                run += Hkv * span(s_nt[b]);
+                run += Hkv * span(sn[k]);
             }
         }
         if (tid == kThreads - 1) s_pre[B] = (before + incl) * Hkv;
@@ -740,7 +750,12 @@ void prefill_balanced_kernel(PrefillArgs a) {
         }
         b = lo;
     }
-    int g = (r0 - s_pre[b]) / span(s_nt[b]);
+    // tiles of sequence b's segment (one head), from its positions in the list
+    auto seg_tiles = [&](int bb) {
+        const int sp1 = (s_pre[bb + 1] - s_pre[bb]) / Hkv;
+        return sp1 > 0 ? sp1 - kBalancedUnitCost : 0;
+    };
+    int g = (r0 - s_pre[b]) / span(seg_tiles(b));
 
     const BlockDiv bdiv = make_div((uint32_t)a.bs);
     const int64_t nb_max = a.num_blocks - 1;
@@ -755,10 +770,10 @@ void prefill_balanced_kernel(PrefillArgs a) {
 
     for (int x = r0; x < r1;) {
         // ---- one unit: tiles [x, u_end) of segment (b, g)
-        const int nb = s_nt[b];
-        const int c0 = a.cu_seqlens[b];
-        const int Tb = min(16 / G, max(0, a.cu_seqlens[b + 1] - c0));
-        const int stp = a.start_pos[b];
+        const int nb = seg_tiles(b);
+        const int c0 = s_c0[b];
+        const int Tb = min(16 / G, max(0, s_c0[b + 1] - c0));
+        const int stp = s_st[b];
         const int L = limit(stp, Tb - 1);
         const int vis = window_lo(limit(stp, 0), W);   // first key any row sees
         const int t0 = vis / kTile * kTile;
@@ -775,10 +790,27 @@ void prefill_balanced_kernel(PrefillArgs a) {
         const int R = Tb * G;                          // rows (token r / G, head r % G)
         const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
 
-        for (int i = tid; i < R * D; i += kThreads) {
+        // the query rows and the first chunk of block ids, requested together
+        float qv[16 * D / kThreads];
+        batched_load<kThreads>(R * D, [&](int i) {
             const int row = i / D;
-            s_q[row][i % D] = a.q[((int64_t)(c0 + row / G) * Hq + g * G + row % G) * D + i % D];
-        }
+            return a.q[((int64_t)(c0 + row / G) * Hq + g * G + row % G) * D + i % D];
+        }, qv);
+        int32_t tv[kTblCap / kThreads];
+        int n_blk = 0, first_blk = 0;
+        auto load_table = [&](int c_lo, int c_hi) {
+            first_blk = (int)bdiv.div((uint32_t)c_lo);
+            n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
+            batched_load<kThreads>(n_blk, [&](int i) { return trow[first_blk + i]; }, tv);
+        };
+        auto store_table = [&]() {
+            batched_store<kThreads>(n_blk, tv, [&](int i, int32_t id) {
+                s_tbl[i] = id < 0 ? 0 : (int32_t)min((int64_t)id, nb_max);
+            });
+        };
+        load_table(tok_lo, min(tok_hi, tok_lo + chunk_tokens));
+        batched_store<kThreads>(R * D, qv, [&](int i, float v) { s_q[i / D][i % D] = v; });
+        store_table();
         typename Tile::State stt;
         Tile::init(stt);
         // row l16's keys (limits and window starts grow with the token), and the keys all rows see
@@ -787,17 +819,15 @@ void prefill_balanced_kernel(PrefillArgs a) {
         stt.alo = window_lo(limit(stp, Tb - 1), W);
         stt.ahi = limit(stp, 0);
         typename Tile::Query qop;
+        typename Tile::Regs ra;   // each wave's first tile, requested before the query work
         for (int c_lo = tok_lo; c_lo < tok_hi; c_lo += chunk_tokens) {
             const int c_hi = min(tok_hi, c_lo + chunk_tokens);
-            if (c_lo != tok_lo) __syncthreads();  // readers of s_tbl are done
-            const int first_blk = (int)bdiv.div((uint32_t)c_lo);
-            const int n_blk = min((int)bdiv.div((uint32_t)(c_hi - 1)) - first_blk + 1, kTblCap);
-            for (int i = tid; i < n_blk; i += kThreads) {
-                const int64_t id = trow[first_blk + i];
-                s_tbl[i] = (int32_t)(id < 0 ? 0 : (id > nb_max ? nb_max : id));
+            if (c_lo != tok_lo) {
+                __syncthreads();  // readers of s_tbl are done
+                load_table(c_lo, c_hi);
+                store_table();
             }
             __syncthreads();  // s_tbl (and, for the first run, s_q)
-            if (c_lo == tok_lo) Tile::setup_query(qf, R, qs, qop);
             TileSource src;
             src.k_pool = a.k_pool;
             src.v_pool = a.v_pool;
@@ -809,9 +839,13 @@ void prefill_balanced_kernel(PrefillArgs a) {
             src.tile_in_block = a.bs % kTile == 0;
             src.tok_stride = (int64_t)Hkv * D;
             src.head_off = (int64_t)g * D;
-            typename Tile::Regs ra;
+            const bool first = c_lo == tok_lo;
+            if (first) {
+                Tile::load_tile(src, c_lo + wave * kTile, c_lo, c_hi, ra);
+                Tile::setup_query(qf, R, qs, qop);
+            }
             Tile::stream(src, c_lo, c_hi, vis, qop, stt, R, qs, qf, s_w[wave].scr, s_def[wave],
-                         []() {}, ra, false);
+                         []() {}, ra, first && c_lo + wave * kTile < c_hi);
         }
 
         // ---- combine the waves; the outputs, or this workgroup's piece of the segment
@@ -882,7 +916,7 @@ void prefill_balanced_kernel(PrefillArgs a) {
         if (x < r1) {
             if (++g == Hkv) {
                 g = 0;
-                do { ++b; } while (b < B - 1 && s_nt[b] == 0);
+                do { ++b; } while (b < B - 1 && s_pre[b + 1] == s_pre[b]);
             }
         }
     }
