@@ -99,6 +99,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="pool copies (0: enough for >= 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="--workload rope|f32: KV heads of the workload (query heads kept; "
+                         "0: the workload's own), to compare group sizes")
     ap.add_argument("--window", type=int, default=0,
                     help="decode step with a sliding window of this many tokens (layer variant)")
     ap.add_argument("--rope-dim", type=int, default=0,
@@ -473,9 +476,15 @@ def run_rope(args, torch, pkv, W) -> int:
     float32 K/V, rotation by the append). HBM-bound like the plain decode."""
     rope = args.workload == "rope"
     wl = W.config(args.config)
-    if not rope:
-        wl = W.make_workload(wl["wid"], wl["positions"], wl["Hq"], wl["Hkv"], wl["D"], wl["bs"],
-                             "f32", wl["theta"], name=wl["name"] + "-f32")
+    hkv = args.kv_heads or wl["Hkv"]
+    if wl["Hq"] % hkv:
+        print(f"--kv-heads {hkv} does not divide {wl['Hq']} query heads", file=sys.stderr)
+        return 2
+    if not rope or hkv != wl["Hkv"]:
+        wl = W.make_workload(wl["wid"], wl["positions"], wl["Hq"], hkv, wl["D"], wl["bs"],
+                             wl["dtype"] if rope else "f32", wl["theta"],
+                             name=wl["name"] + ("" if rope else "-f32") +
+                             ("" if hkv == W.config(args.config)["Hkv"] else f"-kv{hkv}"))
     nbytes = algorithmic_bytes(wl)
     dev = torch.device("cuda:0")
 
@@ -575,7 +584,7 @@ def run_rope(args, torch, pkv, W) -> int:
                    "pool_copies": copies, "split_tokens": split,
                    "bytes_per_step": nbytes["step"]},
         "roofline": {"bound": "hbm", "kernel": ("decode_rope_balanced_kernel" if split == 0 else
-                                                "decode_rope_mfma_kernel / decode_rope_kernel")
+                                                "decode_rope_kernel")
                      + " (pkv_paged_attn_decode)",
                      "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,

@@ -194,10 +194,13 @@ pkv_status pkv_kv_append(const float* q_in, const float* k_in, const float* v_in
  * split_tokens 0 for the balanced schedule, or tokens per partition: a positive multiple of
  *              64 of at most 1022 * block_size (a partition stages its block ids in LDS).
  *              With rope_on_read (variant) or float32 pools: head_dim 64 or 128 with the
- *              rotated dims (rope_dim, when rotating at read) a multiple of 64 run a float32
- *              matrix-core kernel on the same schedules and workspace as 16-bit pools; other
- *              shapes always run the partitioned vector-ALU kernel, where 0 means
- *              pkv_decode_split_tokens(...)'s choice (size the workspace with that value).
+ *              rotated dims (rope_dim, when rotating at read) a multiple of 64 and at least 3
+ *              query heads per KV head (2 for float32 pools without rotation) run a float32
+ *              matrix-core kernel on the same schedules and workspace as 16-bit pools when
+ *              split_tokens is 0; other shapes, and every positive split_tokens, run the
+ *              partitioned vector-ALU kernel, where 0 means the smaller of
+ *              pkv_decode_split_tokens(...)'s choice and 576 (size the workspace with that
+ *              value).
  *              Either way split_tokens is at most 4096 (the rotation is carried across a
  *              partition in float steps).
  * variant      (host) NULL, or a window as described under pkv_variant: then only the keys

@@ -123,13 +123,19 @@ def decode_schedule_split(B, Hq, Hkv, D, block_size, max_context_len, dtype_code
                           rope_on_read: bool = False, rope_dim: int = 0) -> int:
     """split_tokens to size a decode workspace with when the call passes split_tokens = 0:
     0 (the library picks the schedule pkv_decode_workspace_bytes sizes for), except for rotation
-    at read or float32 pools on shapes the matrix-core tile does not serve (head_dim other than
-    64 / 128, or rotated dims not a multiple of 64), which always run the partitioned
-    vector-ALU kernel with pkv_decode_split_tokens(...) tokens per partition."""
+    at read or float32 pools where the library runs the partitioned vector-ALU kernel with
+    min(pkv_decode_split_tokens(...), 576) tokens per partition: shapes the matrix-core tile does not
+    serve (head_dim other than 64 / 128, or rotated dims not a multiple of 64), and small query
+    groups, where the vector ALU is faster (G = Hq / Hkv below 3, or G = 1 for float32 pools
+    without rotation)."""
     read_dim = (rope_dim or D) if rope_on_read else 0
     special = rope_on_read or dtype_code == PKV_F32
-    if special and not (D in (64, 128) and read_dim % 64 == 0):
-        return decode_split_tokens(B, Hq, Hkv, D, block_size, max_context_len)
+    G = Hq // Hkv if Hkv else 0
+    tile_ok = D in (64, 128) and read_dim % 64 == 0
+    pays = G >= 3 or (dtype_code == PKV_F32 and read_dim == 0 and G == 2)
+    if special and not (tile_ok and pays):
+        # the library's partition length for that kernel (kValuSplitMax in pkv_api.hip)
+        return min(decode_split_tokens(B, Hq, Hkv, D, block_size, max_context_len), 576)
     return 0
 
 

@@ -94,6 +94,26 @@ struct WorkspaceLayout {
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
+// Whether rotation at read / float32 pools take the float32 matrix-core tile (when the caller
+// leaves the schedule to the library) rather than the vector-ALU kernel: the tile pads the G
+// query heads of a KV head to 16 columns. Measured on the llama3-8b lengths with 32 query heads
+// (decode us, matrix-core tile / vector-ALU kernel): rotating at read, G = 4 92.0 / 125.1,
+// G = 2 154.7 / 147.4, G = 1 283.7 / 212.0; float32 pools without rotation, G = 4 124.8 /
+// 161.1, G = 2 224.9 / 245.8, G = 1 420.3 / 400.3.
+bool rope_mfma_pays(int D, int G, int read_dim, bool f32) {
+    if (!pkv::decode_rope_mfma_ok(D, G, read_dim)) return false;
+    return G >= 3 || (f32 && read_dim == 0 && G == 2);
+}
+
+// Partition length of the vector-ALU rotation-at-read / float32 kernel when the caller leaves
+// it to the library: choose_split's, at most 576 tokens (its many short partitions keep more
+// rows in flight per compute unit; on the shapes above, 576 against choose_split's 4032:
+// G = 1 rotating 212.0 / 237.5 us, float32 400.3 / 463.5 us).
+constexpr int kValuSplitMax = 576;
+int valu_split(int B, int Hkv, int max_context_len, int block_size, int cus) {
+    return std::min(kValuSplitMax, choose_split(B, Hkv, max_context_len, block_size, cus));
+}
+
 // The balanced schedule needs the per-sequence tile prefix in LDS and int32 tile counts.
 bool balanced_ok(int B, int Hkv, int64_t max_tokens) {
     // the tile list (tiles plus each segment's start cost) is indexed with 32-bit ints
@@ -477,7 +497,7 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
     if (var.rope_read || dtype == PKV_F32) {
         const int read_dim = var.rope_read ? var.rope_dim : 0;
         if (split_tokens == 0 && balanced_ok(B, num_kv_heads, max_context_len) &&
-            pkv::decode_rope_mfma_ok(head_dim, num_q_heads / num_kv_heads, read_dim)) {
+            rope_mfma_pays(head_dim, num_q_heads / num_kv_heads, read_dim, dtype == PKV_F32)) {
             // the float32 matrix-core tile on the balanced schedule (the workspace of the
             // 16-bit decode: pkv_decode_workspace_bytes with split_tokens = 0)
             const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim,
@@ -523,8 +543,8 @@ pkv_status pkv_paged_attn_decode(const float* q, const void* k_pool, const void*
                         "decode: split_tokens=%d above 4096 for rope_on_read / float32 pools (the "
                         "rotation is carried across a partition in float steps)", split_tokens);
         const int P = split_tokens > 0 ? split_tokens
-                                       : choose_split(B, num_kv_heads, max_context_len,
-                                                      block_size, device_cus());
+                                       : valu_split(B, num_kv_heads, max_context_len,
+                                                    block_size, device_cus());
         if (((int64_t)max_context_len + P - 1) / P > 0x7FFFFFFF)
             return fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions");
         const WorkspaceLayout wl = layout_for(B, num_q_heads, num_kv_heads, head_dim,

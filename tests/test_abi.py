@@ -182,11 +182,12 @@ def test_library_missing_fails_loudly(tmp_path):
 def test_decode_schedule_split_routes_by_shape(lib):
     """With split_tokens = 0, rotation at read and float32 pools follow the 16-bit pools'
     schedule (workspace from pkv_decode_workspace_bytes(..., 0)) where the matrix-core tile
-    serves the shape (head_dim 64 / 128, rotated dims a multiple of 64), else the partition
-    length pkv_decode_split_tokens picks for the vector-ALU kernel."""
+    serves the shape (head_dim 64 / 128, rotated dims a multiple of 64) and the query group is
+    large enough to pay for it, else the vector-ALU kernel's partition length (the smaller of
+    pkv_decode_split_tokens' choice and 576)."""
     import paged_kv_cache_315_amd as pkv
     args = (32, 32, 8, 128, 16, 4096)
-    part = pkv.decode_split_tokens(*args)
+    part = min(pkv.decode_split_tokens(*args), 576)    # the vector-ALU kernel's partitions
     assert part > 0 and part % 64 == 0
     assert pkv.decode_schedule_split(*args, pkv.PKV_BF16) == 0                  # plain pool
     assert pkv.decode_schedule_split(*args, pkv.PKV_F32) == 0                   # float32, no rotation
@@ -195,7 +196,17 @@ def test_decode_schedule_split_routes_by_shape(lib):
     assert pkv.decode_schedule_split(*args, pkv.PKV_F32, True, 128) == 0
     assert pkv.decode_schedule_split(*args, pkv.PKV_BF16, True, 32) == part     # in-lane pairs need 64
     assert pkv.decode_schedule_split(*args, pkv.PKV_BF16, True, 96) == part
+    # small query groups: the vector-ALU kernel (rotation at read below G = 3, float32 pools
+    # without rotation at G = 1)
+    g1, g2 = (32, 32, 32, 128, 16, 4096), (32, 32, 16, 128, 16, 4096)
+    valu = lambda a: min(pkv.decode_split_tokens(*a), 576)
+    assert pkv.decode_schedule_split(*g1, pkv.PKV_BF16, True, 0) == valu(g1)
+    assert pkv.decode_schedule_split(*g2, pkv.PKV_BF16, True, 0) == valu(g2)
+    assert pkv.decode_schedule_split(*g2, pkv.PKV_F32, True, 0) == valu(g2)
+    assert pkv.decode_schedule_split(*g2, pkv.PKV_F32) == 0
+    assert pkv.decode_schedule_split(*g1, pkv.PKV_F32) == valu(g1)
+    assert pkv.decode_schedule_split(*g1, pkv.PKV_BF16) == 0                    # 16-bit pools
     a256 = (32, 32, 8, 256, 16, 4096)
-    assert pkv.decode_schedule_split(*a256, pkv.PKV_F32) == pkv.decode_split_tokens(*a256)
+    assert pkv.decode_schedule_split(*a256, pkv.PKV_F32) == valu(a256)
     a32 = (32, 32, 8, 32, 16, 4096)
-    assert pkv.decode_schedule_split(*a32, pkv.PKV_BF16, True, 0) == pkv.decode_split_tokens(*a32)
+    assert pkv.decode_schedule_split(*a32, pkv.PKV_BF16, True, 0) == valu(a32)

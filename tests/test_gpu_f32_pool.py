@@ -34,7 +34,7 @@ CASES = {
     # one sequence of 1.3 M tokens in 1-token blocks, rotated at read: a workgroup's share of
     # the balanced schedule is longer than the block ids it stages at once (several chunks,
     # the rotation seeded again at each), and hundreds of pieces are merged
-    "long-bs1-rope-chunked": (lambda: W.make_workload(309, [1300000], 1, 1, 64, 1, "f32", 1e4),
+    "long-bs1-rope-chunked": (lambda: W.make_workload(309, [1300000], 4, 1, 64, 1, "f32", 1e4),
                               True, 0, 0, False, 0),
     # edge values in the new K/V (1 %: +-70000, 1e-7, NaN) after QK-norm: float32 rows keep them
     "qknorm-edges": (lambda: W.make_workload(307, [100, 700, 33], 32, 8, 128, 16, "f32", 1e6,

@@ -37,7 +37,7 @@ CASES = {
                       0, 50, 0),
     # one sequence of 2.2 M tokens: a workgroup's share of the balanced schedule is longer than
     # 4096 tokens, so its rotation is seeded afresh for each run of at most 4096
-    "long-bs16-runs": (lambda: W.make_workload(210, [2200000], 2, 1, 64, 16, "bf16", 1e4), 0, 0,
+    "long-bs16-runs": (lambda: W.make_workload(210, [2200000], 4, 1, 64, 16, "bf16", 1e4), 0, 0,
                        0),
     # block size 12: a 16-token tile spans two blocks (per-row block lookups)
     "bs12-bf16": (lambda: W.make_workload(209, [100, 777, 1500, 12], 16, 4, 128, 12, "bf16", 5e5),
