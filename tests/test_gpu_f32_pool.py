@@ -36,6 +36,12 @@ CASES = {
     # the rotation seeded again at each), and hundreds of pieces are merged
     "long-bs1-rope-chunked": (lambda: W.make_workload(309, [1300000], 4, 1, 64, 1, "f32", 1e4),
                               True, 0, 0, False, 0),
+    # one query head per KV head with the schedule left to the library: the vector-ALU kernel
+    # on partitions of at most 576 tokens (several per sequence, merged)
+    "mha-d128-library-split": (lambda: W.make_workload(310, [1, 600, 1700, 2500], 8, 8, 128, 16,
+                                                       "f32", 5e5), False, 0, 0, False, 0),
+    "mha-d128-rope-library-split": (lambda: W.make_workload(311, [1300, 64, 2047], 8, 8, 128, 16,
+                                                            "f32", 5e5), True, 0, 0, False, 0),
     # edge values in the new K/V (1 %: +-70000, 1e-7, NaN) after QK-norm: float32 rows keep them
     "qknorm-edges": (lambda: W.make_workload(307, [100, 700, 33], 32, 8, 128, 16, "f32", 1e6,
                                              qk_norm=True, edge_fraction=0.01), False, 0, 0,

@@ -39,6 +39,12 @@ CASES = {
     # 4096 tokens, so its rotation is seeded afresh for each run of at most 4096
     "long-bs16-runs": (lambda: W.make_workload(210, [2200000], 4, 1, 64, 16, "bf16", 1e4), 0, 0,
                        0),
+    # one and two query heads per KV head, schedule left to the library: the vector-ALU kernel
+    # on partitions of at most 576 tokens
+    "mha-bf16-library-split": (lambda: W.make_workload(212, [3000, 1, 577, 1200], 16, 16, 128,
+                                                       16, "bf16", 5e5), 0, 0, 0),
+    "g2-f16-library-split": (lambda: W.make_workload(213, [2000, 700], 8, 4, 128, 16, "f16",
+                                                     1e6, qk_norm=True), 0, 0, 0),
     # block size 12: a 16-token tile spans two blocks (per-row block lookups)
     "bs12-bf16": (lambda: W.make_workload(209, [100, 777, 1500, 12], 16, 4, 128, 12, "bf16", 5e5),
                   0, 0, 0),
