@@ -640,11 +640,15 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
 // Chunks of at most one query tile per sequence (draft verification, short chunks): the
 // balanced schedule of decode_balanced.hip over the same tile. Segment (b, g) = the keys the
 // chunk of sequence b sees through KV head g, as 16-key tiles from the one holding its first
-// token's first key to its last token's last, preceded by kBalancedUnitCost empty positions;
+// token's first key to its last token's last, preceded by kPrefillUnitCost empty positions;
 // workgroup w takes positions [r T, (r + 1) T) (r its range under the XCD-aware deal), with the
 // chunk's (token, head) rows and their key ranges; a segment cut by ranges leaves one piece of
 // 16 rows per workgroup (slots 2r, 2r + 1) and the last workgroup to finish merges them.
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
+// Empty positions before each segment in the list (the decode step's 15 tiles measured 89.2 us
+// on 32 x 4 draft tokens over U{512..4096} cached, 6 tiles 84.2 us, 30 tiles 85.8 us; at most
+// kBalancedUnitCost, which the host's size checks assume).
+constexpr int kPrefillUnitCost = kBalancedUnitCost < 6 ? kBalancedUnitCost : 6;
 
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
@@ -679,7 +683,7 @@ void prefill_balanced_kernel(PrefillArgs a) {
     auto limit = [&](int st, int t) -> int {
         return (int)max((int64_t)0, min((int64_t)st + t + 1, cap));
     };
-    auto span = [=](int nt) { return nt > 0 ? nt + kBalancedUnitCost : 0; };
+    auto span = [=](int nt) { return nt > 0 ? nt + kPrefillUnitCost : 0; };
 
     // ---- each sequence's tile count and the tile prefix of every sequence (all heads) -> LDS;
     // all of a thread's loads first (one round trip)
@@ -753,7 +757,7 @@ void prefill_balanced_kernel(PrefillArgs a) {
     // tiles of sequence b's segment (one head), from its positions in the list
     auto seg_tiles = [&](int bb) {
         const int sp1 = (s_pre[bb + 1] - s_pre[bb]) / Hkv;
-        return sp1 > 0 ? sp1 - kBalancedUnitCost : 0;
+        return sp1 > 0 ? sp1 - kPrefillUnitCost : 0;
     };
     int g = (r0 - s_pre[b]) / span(seg_tiles(b));
 
@@ -777,7 +781,7 @@ void prefill_balanced_kernel(PrefillArgs a) {
         const int L = limit(stp, Tb - 1);
         const int vis = window_lo(limit(stp, 0), W);   // first key any row sees
         const int t0 = vis / kTile * kTile;
-        const int seg_start = s_pre[b] + g * span(nb) + kBalancedUnitCost;  // its first tile
+        const int seg_start = s_pre[b] + g * span(nb) + kPrefillUnitCost;  // its first tile
         const int seg_end = seg_start + nb;
         if (x < seg_start) {  // the range starts in the segment's start cost
             x = seg_start;
