@@ -359,7 +359,7 @@ struct RTile {
 
 // ---- balanced schedule (the decode_balanced.hip deal, decode only)
 // The K/V rows of the batch form one list of 16-token tiles, segment (b, g) = KV head g of
-// sequence b preceded by kBalancedUnitCost empty positions; workgroup w takes positions
+// sequence b preceded by a start cost of empty positions; workgroup w takes positions
 // [r T, (r + 1) T), r its range under the XCD-aware deal. A segment inside one range is finished
 // there; a cut one leaves one piece per workgroup it touches (a workgroup holds at most two:
 // slots 2r and 2r + 1), and the last workgroup to finish it merges the pieces.
@@ -389,7 +389,12 @@ void decode_rope_balanced_kernel(BalancedArgs a) {
     const int Hq = a.Hq;
     const int W = a.window;
     auto ntiles = [=](int L) { return (L + 15) / 16 - window_lo(L, W) / 16; };
-    auto span = [=](int nt) { return nt > 0 ? nt + kBalancedUnitCost : 0; };
+    // empty positions before each segment: the 16-bit decode's start cost, or 6 tiles over
+    // float32 pools (on the llama3-8b lengths: 6 tiles 122.8 us, 15 tiles 125.0 us, 30 tiles
+    // 132.9 us; rotating at read 15 tiles is best: 92.2 against 95.2 and 95.9 us); never more
+    // than kBalancedUnitCost, which the host's size checks assume
+    constexpr int kCost = EK == kF32 && NJR == 0 && kBalancedUnitCost > 6 ? 6 : kBalancedUnitCost;
+    auto span = [=](int nt) { return nt > 0 ? nt + kCost : 0; };
 
     // ---- lengths and the tile prefix of every sequence (all heads) -> LDS
     const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks * a.bs);
@@ -472,7 +477,7 @@ void decode_rope_balanced_kernel(BalancedArgs a) {
         const int vis_lo = window_lo(L, W);
         const int t0 = vis_lo / 16 * 16;
         const int nb = ntiles(L);
-        const int seg_start = s_pre[b] + g * span(nb) + kBalancedUnitCost;  // its first tile
+        const int seg_start = s_pre[b] + g * span(nb) + kCost;  // its first tile
         const int seg_end = seg_start + nb;
         if (x < seg_start) {  // the range starts in the segment's start cost
             x = seg_start;
