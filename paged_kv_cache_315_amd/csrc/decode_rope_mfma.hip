@@ -357,6 +357,10 @@ struct RTile {
 // in flight and 32 cos / sin pairs per lane need more than 256 registers).
 #define PKV_RTILE_WAVES(EK, NJR) (EK == kF32 && NJR == 2 ? 1 : 2)
 
+#ifndef PKV_F32_UNIT_COST
+#define PKV_F32_UNIT_COST 6
+#endif
+
 // ---- balanced schedule (the decode_balanced.hip deal, decode only)
 // The K/V rows of the batch form one list of 16-token tiles, segment (b, g) = KV head g of
 // sequence b preceded by a start cost of empty positions; workgroup w takes positions
@@ -392,8 +396,11 @@ void decode_rope_balanced_kernel(BalancedArgs a) {
     // empty positions before each segment: the 16-bit decode's start cost, or 6 tiles over
     // float32 pools (on the llama3-8b lengths: 6 tiles 122.8 us, 15 tiles 125.0 us, 30 tiles
     // 132.9 us; rotating at read 15 tiles is best: 92.2 against 95.2 and 95.9 us); never more
-    // than kBalancedUnitCost, which the host's size checks assume
-    constexpr int kCost = EK == kF32 && NJR == 0 && kBalancedUnitCost > 6 ? 6 : kBalancedUnitCost;
+    // than kBalancedUnitCost, which the host's size checks assume (PKV_F32_UNIT_COST overrides
+    // the 6 in builds that sweep it)
+    constexpr int kCost = EK == kF32 && NJR == 0 && kBalancedUnitCost > PKV_F32_UNIT_COST
+                              ? PKV_F32_UNIT_COST
+                              : kBalancedUnitCost;
     auto span = [=](int nt) { return nt > 0 ? nt + kCost : 0; };
 
     // ---- lengths and the tile prefix of every sequence (all heads) -> LDS

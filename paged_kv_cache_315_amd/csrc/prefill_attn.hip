@@ -647,8 +647,13 @@ void prefill_attn_shared_kernel(PrefillArgs a) {
 constexpr int kPerThread = (kMaxBalancedBatch + kThreads - 1) / kThreads;
 // Empty positions before each segment in the list (the decode step's 15 tiles measured 89.2 us
 // on 32 x 4 draft tokens over U{512..4096} cached, 6 tiles 84.2 us, 30 tiles 85.8 us; at most
-// kBalancedUnitCost, which the host's size checks assume).
-constexpr int kPrefillUnitCost = kBalancedUnitCost < 6 ? kBalancedUnitCost : 6;
+// kBalancedUnitCost, which the host's size checks assume; PKV_PREFILL_UNIT_COST overrides it in
+// builds that sweep it).
+#ifndef PKV_PREFILL_UNIT_COST
+#define PKV_PREFILL_UNIT_COST 6
+#endif
+constexpr int kPrefillUnitCost =
+    kBalancedUnitCost < PKV_PREFILL_UNIT_COST ? kBalancedUnitCost : PKV_PREFILL_UNIT_COST;
 
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
